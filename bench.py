@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN verify step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: for each of the 48
+layers a conv1d span and a GDN verify span with checkpoints, then greedy
+acceptance, rollback of every layer to the accepted checkpoint, the
+feature-ring set/get, and the step's single host sync (accepted lengths and
+bonus tokens back to the host). Inputs are seeded synthetic data already
+resident in HBM when the timed region starts.
+
+Prints ONE JSON line on stdout. Progress goes to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME|INDEX] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = 3   # 16 requests x 48 layers, chain K=16, with the feature ring
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=str(DEFAULT_WORKLOAD))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    whole (layer, request) units (conv span, GDN span, acceptance of the
+    request, replay rollback along the accepted path), single-threaded."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from oracle import accept as oacc, conv as oconv, gdn as ogdn, rollback as orb
+    from synth import gen_accept, gen_conv_weight, gen_unit
+    units = [(l, r) for r in range(w.n_req) for l in range(w.n_layers)]
+    done = 0
+    t_work = 0.0
+    with threadpool_limits(limits=1):
+        for (l, r) in units:
+            u = gen_unit(w, l, r)
+            wt = gen_conv_weight(w, l)
+            ai = gen_accept(w, r, with_logits=w.vocab > 0)
+            t0 = time.perf_counter()
+            par = ai.parent if w.tree else None
+            oconv.conv_span(u.x, wt, u.conv_state, par)
+            ogdn.gdn_span(u.state, u.q, u.k, u.v, u.a, u.b, par)
+            if w.vocab and l == 0:
+                am = oacc.argmax_rows(ai.logits)
+                res = oacc.accept(am, ai.tokens, par)
+                path = res.path
+            else:
+                res = oacc.accept(ai.planted_argmax, ai.tokens, par)
+                path = res.path
+            orb.replay_state(u.state, u.q, u.k, u.v, u.a, u.b, path)
+            orb.replay_conv_state(u.conv_state, u.x, path)
+            t_work += time.perf_counter() - t0
+            done += 1
+            if t_work >= seconds:
+                break
+    tokens = done * w.n_pos
+    return {"value": tokens / t_work, "unit": "verify tokens/s per layer", "cores": 1, "kind": "oracle",
+            "sample": f"{done} (layer, request) units of {w.name}: conv span, GDN span, acceptance "
+                      f"(argmax once per request), replay rollback; {t_work:.1f} s of CPU work, 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
+              "(requests, layers and heads shard with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from synth import WORKLOADS, WORKLOAD_ORDER
+    from synth.device import fill_step, step_shape
+    import hybrid_recurrent_state_amd as hrs
+    from hybrid_recurrent_state_amd.step import StepBuffers, VerifyStep
+
+    name = WORKLOAD_ORDER[int(args.workload)] if args.workload.isdigit() else args.workload
+    w = WORKLOADS[name]
+    shape = step_shape(w)
+    log(f"workload {name}: R={w.n_req} L={w.n_layers} T={w.n_pos} Hk={w.n_kheads} Hv={w.n_vheads} "
+        f"d={w.d_k} C={w.conv_channels} V={w.vocab} ring={w.ring_slots}x{w.ring_width}")
+    torch.cuda.set_device(0)
+    bufs = StepBuffers(shape)
+    loaded = fill_step(bufs, w, log=log)
+    step = VerifyStep(bufs, parent=loaded.parent, runs=loaded.runs)
+    stream = torch.cuda.current_stream()
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step.run(stream)
+    torch.cuda.synchronize()
+
+    L, K = w.n_layers, args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+          for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step.launch(stream, gdn_events=ev[i])
+        step.finish()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    gdn_ms = np.array([[s.elapsed_time(e) for (s, e) in row] for row in ev])
+    gdn_avg_s = float(gdn_ms.mean()) / 1e3
+
+    # Phase split (separate, untimed pass with events between phases).
+    ph = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    h = stream.cuda_stream
+    ph[0].record()
+    for l in range(L):
+        step.launch_layer(l, h)
+    ph[1].record()
+    step.launch_accept(h)
+    ph[2].record()
+    step.launch_rollback(h)
+    ph[3].record()
+    step.launch_ring(h)
+    ph[4].record()
+    torch.cuda.synchronize()
+    phases = {"conv+gdn": ph[0].elapsed_time(ph[1]), "accept": ph[1].elapsed_time(ph[2]),
+              "rollback": ph[2].elapsed_time(ph[3]), "ring": ph[3].elapsed_time(ph[4])}
+
+    R, T = w.n_req, w.n_pos
+    value = R * T * L / (ms_per_step / 1e3)
+    gdn_bytes = shape.gdn_bytes_per_layer
+    achieved = gdn_bytes / gdn_avg_s / 1e9
+    log(f"step {ms_per_step:.3f} ms; gdn launch avg {gdn_avg_s * 1e6:.1f} us = {achieved:.0f} GB/s; phases {phases}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    line = {
+        "metric": "GDN verify tokens/s per layer + achieved HBM GB/s (fraction of peak), K=16",
+        "value": value,
+        "unit": "verify tokens/s per layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; Qwen3.6-27B-shaped GDN layers, no weights)",
+        "config": {"workload": name, "n_req": R, "n_layers": L, "n_pos": T, "draft_tokens": T - 1,
+                   "topology": "tree" if w.tree else "chain", "n_kheads": w.n_kheads, "n_vheads": w.n_vheads,
+                   "d_k": w.d_k, "d_v": w.d_v, "inputs": w.dtype, "state": "f32",
+                   "conv_channels": w.conv_channels, "conv_width": w.conv_width, "vocab": w.vocab,
+                   "ring": [w.n_req, w.ring_slots, w.ring_width] if w.ring_slots else None},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gdn_verify_span", "bytes_per_launch": gdn_bytes,
+                     "avg_launch_us": gdn_avg_s * 1e6},
+        "gdn_tokens_per_s_per_layer": R * T / gdn_avg_s,
+        "phases_ms": phases,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

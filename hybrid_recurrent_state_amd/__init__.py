@@ -1,0 +1,262 @@
+"""Python binding of libhrs: verify-span checkpoints, greedy acceptance and
+on-device rollback for Gated DeltaNet layers on MI355X (gfx950).
+
+Argument marshalling only. Every function here takes torch tensors that
+live on the GPU, checks that they are contiguous and of the expected dtype,
+and passes raw pointers, sizes and the current HIP stream to the C ABI in
+include/hrs.h; all computation happens in the HIP kernels of libhrs.so. A
+negative status from the library raises ``HrsError``.
+
+The library must be built first (``python -m hybrid_recurrent_state_amd.build``
+or ``__graft_entry__.build()``); importing this package without it raises
+ImportError, so nothing silently falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhrs.so")
+
+HRS_OK, HRS_EINVAL, HRS_EGEOMETRY, HRS_EALIGN, HRS_EDEVICE, HRS_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+HRS_F32, HRS_BF16 = 0, 1
+HRS_CHAIN, HRS_TREE = 0, 1
+HRS_MAX_POS = 64
+GEOMETRY_CLASSES = {0: "OK", 1: "NULL", 2: "TRUNCATED", 3: "ROOT", 4: "RANGE", 5: "FORWARD", 6: "NOT_CHAIN"}
+
+
+class HrsError(RuntimeError):
+    def __init__(self, status: int, func: str):
+        self.status = status
+        super().__init__(f"{func}: {strerror(status)} (status {status})")
+
+
+# --- C structs (mirror include/hrs.h) -------------------------------------
+_i32 = ctypes.c_int32
+_p = ctypes.c_void_p
+
+
+class GdnDesc(ctypes.Structure):
+    _fields_ = [("n_req", _i32), ("n_pos", _i32), ("n_kheads", _i32), ("n_vheads", _i32),
+                ("d_k", _i32), ("d_v", _i32), ("in_dtype", _i32), ("q_scale", ctypes.c_float),
+                ("topo", _i32), ("parent", ctypes.POINTER(_i32))]
+
+
+class ConvDesc(ctypes.Structure):
+    _fields_ = [("n_req", _i32), ("n_pos", _i32), ("channels", _i32), ("width", _i32),
+                ("dtype", _i32), ("silu", _i32), ("topo", _i32), ("parent", ctypes.POINTER(_i32))]
+
+
+class AcceptDesc(ctypes.Structure):
+    _fields_ = [("n_req", _i32), ("n_pos", _i32), ("vocab", _i32), ("logit_dtype", _i32),
+                ("topo", _i32), ("parent", ctypes.POINTER(_i32))]
+
+
+class RollbackDesc(ctypes.Structure):
+    _fields_ = [("n_layers", _i32), ("n_req", _i32), ("n_pos", _i32), ("n_vheads", _i32),
+                ("d_k", _i32), ("d_v", _i32), ("conv_channels", _i32), ("conv_width", _i32),
+                ("conv_dtype", _i32)]
+
+
+class RingRun(ctypes.Structure):
+    _fields_ = [("ring_id", _i32), ("start_pos", _i32), ("n_rows", _i32), ("packed_row", _i32)]
+
+
+class RingDesc(ctypes.Structure):
+    _fields_ = [("n_rings", _i32), ("n_slots", _i32), ("width", _i32), ("dtype", _i32),
+                ("n_packed_rows", _i32), ("n_runs", _i32), ("runs", ctypes.POINTER(RingRun))]
+
+
+# Exported symbols and their signatures (every function of include/hrs.h).
+_SIGNATURES = {
+    "hrs_validate_tree": (_i32, [ctypes.POINTER(_i32), _i32, _i32, ctypes.POINTER(_i32)]),
+    "gdn_verify_span": (_i32, [ctypes.POINTER(GdnDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "conv1d_verify_span": (_i32, [ctypes.POINTER(ConvDesc), _p, _p, _p, _p, _p, _p]),
+    "accept_greedy_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AcceptDesc)]),
+    "accept_greedy": (_i32, [ctypes.POINTER(AcceptDesc), _p, _p, _p, _p, _p, _p, _p, _p,
+                             ctypes.c_size_t, _p]),
+    "rollback_restore": (_i32, [ctypes.POINTER(RollbackDesc), _p, _p, _p, _p, _p, _p, _p]),
+    "ring_set_2d": (_i32, [ctypes.POINTER(RingDesc), _p, _p, _p]),
+    "ring_get_2d": (_i32, [ctypes.POINTER(RingDesc), _p, _p, _p]),
+    "hrs_strerror": (ctypes.c_char_p, [_i32]),
+    "hrs_abi_version": (_i32, []),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m hybrid_recurrent_state_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.hrs_strerror(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib.hrs_abi_version())
+
+
+def _check(status: int, func: str) -> None:
+    if status != HRS_OK:
+        raise HrsError(status, func)
+
+
+# --- marshalling helpers --------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return HRS_F32
+    if t.dtype == torch.bfloat16:
+        return HRS_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _parent_array(parent, n_req: int, n_pos: int):
+    """Host int32 [n_req * n_pos] array (a single [n_pos] row is repeated)."""
+    if parent is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
+    if arr.ndim == 1 and n_req > 1 and arr.size == n_pos:
+        arr = np.ascontiguousarray(np.tile(arr, n_req))
+    arr = arr.reshape(-1)
+    return arr, arr.ctypes.data_as(ctypes.POINTER(_i32))
+
+
+# --- entry points (same names as the C ABI) -------------------------------
+
+def validate_tree(parent, n_pos: Optional[int] = None, require_chain: bool = False):
+    """Run the host geometry guard. Returns (status, class name)."""
+    cls = _i32(-1)
+    if parent is None:
+        st = lib.hrs_validate_tree(None, int(n_pos or 0), int(require_chain), ctypes.byref(cls))
+    else:
+        arr = np.ascontiguousarray(np.asarray(parent, dtype=np.int32)).reshape(-1)
+        n = arr.size if n_pos is None else int(n_pos)
+        st = lib.hrs_validate_tree(arr.ctypes.data_as(ctypes.POINTER(_i32)), n, int(require_chain),
+                                   ctypes.byref(cls))
+    return int(st), GEOMETRY_CLASSES.get(cls.value, "?")
+
+
+hrs_validate_tree = validate_tree
+
+
+def gdn_verify_span(q, k, v, a, b, state, ckpt, out, parent=None, q_scale: float = 1.0, stream=None):
+    """q, k [R,T,Hk,dk]; v [R,T,Hv,dv]; a, b [R,T,Hv] (f32 or bf16);
+    state [R,Hv,dv,dk] f32; ckpt [R,T,Hv,dv,dk] f32 or None; out [R,T,Hv,dv] f32.
+    parent: None (chain) or host ints [R,T] / [T] (tree)."""
+    R, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    par, par_p = _parent_array(parent, R, T)
+    d = GdnDesc(R, T, Hk, Hv, dk, dv, _dtype_code(q), float(q_scale),
+                HRS_TREE if parent is not None else HRS_CHAIN, par_p)
+    st = lib.gdn_verify_span(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(state),
+                             _ptr(ckpt), _ptr(out), _stream(stream))
+    _check(st, "gdn_verify_span")
+
+
+def conv1d_verify_span(x, w, conv_state, conv_ckpt, y, parent=None, silu: bool = False, stream=None):
+    """x [R,T,C]; w [C,W]; conv_state [R,W-1,C]; conv_ckpt [R,T,W-1,C] or None
+    (same dtype as x); y [R,T,C] f32. parent: None (chain) or host [R,T]/[T]."""
+    R, T, C = x.shape
+    W = w.shape[1]
+    par, par_p = _parent_array(parent, R, T)
+    d = ConvDesc(R, T, C, W, _dtype_code(x), int(bool(silu)),
+                 HRS_TREE if parent is not None else HRS_CHAIN, par_p)
+    st = lib.conv1d_verify_span(ctypes.byref(d), _ptr(x), _ptr(w), _ptr(conv_state), _ptr(conv_ckpt),
+                                _ptr(y), _stream(stream))
+    _check(st, "conv1d_verify_span")
+
+
+def accept_desc(n_req: int, n_pos: int, vocab: int, logit_dtype: int, parent=None):
+    par, par_p = _parent_array(parent, n_req, n_pos)
+    d = AcceptDesc(n_req, n_pos, vocab, logit_dtype, HRS_TREE if parent is not None else HRS_CHAIN, par_p)
+    return d, par
+
+
+def accept_greedy_workspace_bytes(n_req: int, n_pos: int, vocab: int, logit_dtype: int = HRS_BF16,
+                                  parent=None) -> int:
+    d, _keep = accept_desc(n_req, n_pos, vocab, logit_dtype, parent)
+    return int(lib.accept_greedy_workspace_bytes(ctypes.byref(d)))
+
+
+def accept_greedy(logits, tokens, argmax, accept_node, accept_len, path, bonus, workspace,
+                  parent=None, stream=None):
+    """logits [R,T,V]; tokens [R,T] int32; outputs int32 device tensors
+    argmax [R,T], accept_node [R], accept_len [R], path [R,T], bonus [R];
+    workspace: device tensor of at least accept_greedy_workspace_bytes."""
+    R, T, V = logits.shape
+    d, _keep = accept_desc(R, T, V, _dtype_code(logits), parent)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib.accept_greedy(ctypes.byref(d), _ptr(logits), _ptr(tokens), _ptr(argmax), _ptr(accept_node),
+                           _ptr(accept_len), _ptr(path), _ptr(bonus), _ptr(workspace), nbytes,
+                           _stream(stream))
+    _check(st, "accept_greedy")
+
+
+def rollback_restore(ckpt, state, conv_ckpt, conv_state, accept_node, status, stream=None):
+    """ckpt [L,R,T,Hv,dv,dk] f32 -> state [L,R,Hv,dv,dk]; conv_ckpt
+    [L,R,T,W-1,C] -> conv_state [L,R,W-1,C] (both None to skip);
+    accept_node [R] int32 device; status [>=1] int32 device."""
+    L, R, T, Hv, dv, dk = ckpt.shape
+    if conv_ckpt is not None:
+        C, W1 = conv_ckpt.shape[4], conv_ckpt.shape[3]
+        cdt = _dtype_code(conv_ckpt)
+    else:
+        C, W1, cdt = 0, 0, HRS_F32
+    d = RollbackDesc(L, R, T, Hv, dk, dv, C, W1 + 1 if conv_ckpt is not None else 0, cdt)
+    st = lib.rollback_restore(ctypes.byref(d), _ptr(ckpt), _ptr(state), _ptr(conv_ckpt), _ptr(conv_state),
+                              _ptr(accept_node), _ptr(status), _stream(stream))
+    _check(st, "rollback_restore")
+
+
+def _ring_desc(ring, n_packed_rows: int, runs: Sequence[tuple]):
+    n_rings, S, D = ring.shape
+    arr = (RingRun * max(1, len(runs)))(*[RingRun(*map(int, r)) for r in runs])
+    d = RingDesc(n_rings, S, D, _dtype_code(ring), n_packed_rows, len(runs), arr)
+    return d, arr
+
+
+def ring_set_2d(ring, packed, runs, stream=None):
+    """ring [n_rings,S,D]; packed [N,D]; runs: (ring_id, start_pos, n_rows, packed_row)."""
+    d, _keep = _ring_desc(ring, packed.shape[0], runs)
+    _check(lib.ring_set_2d(ctypes.byref(d), _ptr(ring), _ptr(packed), _stream(stream)), "ring_set_2d")
+
+
+def ring_get_2d(ring, packed, runs, stream=None):
+    d, _keep = _ring_desc(ring, packed.shape[0], runs)
+    _check(lib.ring_get_2d(ctypes.byref(d), _ptr(ring), _ptr(packed), _stream(stream)), "ring_get_2d")

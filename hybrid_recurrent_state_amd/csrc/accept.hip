@@ -1,0 +1,208 @@
+// accept_greedy: target argmax per verified position and greedy acceptance of
+// the longest matching prefix (chain) or root path (draft tree).
+//
+// Greedy verification of one draft block (openinfer PR #626, "feat(qwen35):
+// add opt-in DFlash speculative decoding", Summary: the output must match
+// plain greedy decoding); chain and DDTree verification (lucebox PR #533,
+// "feat: DFlash support for tensor-parallel Qwen3.6 targets", Verification).
+//
+// MI355X design: the argmax rows are long (151,936 entries) and few (T per
+// request), so pass 1 splits every row into 8192-entry chunks, one block
+// each, streaming 16-byte loads; each block reduces a 64-bit key (ordered
+// value bits above the complemented index) and writes it to the caller's
+// workspace. Taking the maximum key realises "largest value, lowest index on
+// ties, NaN never wins" with plain integer compares, in any reduction order,
+// so the result is deterministic. Pass 2 is one wave per request: lane t
+// reduces row t's chunk keys, then the acceptance walk runs over the T <= 64
+// positions in LDS.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "device.h"
+#include "internal.h"
+
+namespace hrs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 8192;  // logits per pass-1 block
+
+struct AcceptArgs {
+  const int32_t* tokens;
+  const uint64_t* keys;   // workspace [rows][n_chunks]
+  int32_t* argmax;
+  int32_t* accept_node;
+  int32_t* accept_len;
+  int32_t* path;
+  int32_t* bonus;
+  int32_t n_pos;
+  int32_t n_chunks;
+  int32_t req0;
+  int32_t tree;
+  int8_t parent[kGeomBytes];  // tree: [requests of this launch][n_pos]
+};
+
+// Order-preserving map of a float to u32: NaN -> 0 (below everything),
+// -0 -> +0, otherwise larger floats map to larger integers.
+__device__ __forceinline__ uint32_t ordered_bits(float x) {
+  if (x != x) return 0u;
+  if (x == 0.0f) x = 0.0f;
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t make_key(float x, uint32_t idx) {
+  return (static_cast<uint64_t>(ordered_bits(x)) << 32) | static_cast<uint64_t>(~idx);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const T* logits, uint64_t* keys, int32_t vocab,
+                                                                  int32_t n_chunks) {
+  const int row = blockIdx.x / n_chunks;
+  const int chunk = blockIdx.x % n_chunks;
+  const T* base = logits + static_cast<size_t>(row) * vocab;
+  const int begin = chunk * kChunk;
+  const int end = min(vocab, begin + kChunk);
+  uint64_t best = 0;
+  for (int e = begin + threadIdx.x * 8; e < end; e += kThreads * 8) {
+    float v[8];
+    load8<T>(base + e, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint64_t key = make_key(v[i], static_cast<uint32_t>(e + i));
+      best = key > best ? key : best;
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint64_t o = shfl_xor_u64(best, m);
+    best = o > best ? o : best;
+  }
+  __shared__ uint64_t wave_best[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wave_best[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t b = wave_best[0];
+    for (int i = 1; i < kThreads / 64; ++i) b = wave_best[i] > b ? wave_best[i] : b;
+    keys[blockIdx.x] = b;
+  }
+}
+
+__global__ __launch_bounds__(64) void accept_walk_kernel(const AcceptArgs args) {
+  const int T_ = args.n_pos;
+  const int rl = blockIdx.x;
+  const int r = args.req0 + rl;
+  const int lane = threadIdx.x;
+  __shared__ int32_t am[HRS_MAX_POS];
+  __shared__ int32_t path_s[HRS_MAX_POS];
+  __shared__ int32_t depth[HRS_MAX_POS];
+  __shared__ int32_t matched[HRS_MAX_POS];
+  __shared__ int32_t len_s;
+  if (lane < T_) {
+    const uint64_t* k = args.keys + (static_cast<size_t>(r) * T_ + lane) * args.n_chunks;
+    uint64_t b = 0;
+    for (int c = 0; c < args.n_chunks; ++c) b = k[c] > b ? k[c] : b;
+    const int32_t idx = static_cast<int32_t>(~static_cast<uint32_t>(b));
+    am[lane] = idx;
+    args.argmax[static_cast<size_t>(r) * T_ + lane] = idx;
+  }
+  __syncthreads();
+  if (lane == 0) {
+    const int32_t* tok = args.tokens + static_cast<size_t>(r) * T_;
+    const int8_t* par = args.parent + rl * T_;
+    matched[0] = 1;
+    depth[0] = 0;
+    int32_t best = 0;
+    for (int t = 1; t < T_; ++t) {
+      const int p = args.tree ? par[t] : t - 1;
+      depth[t] = depth[p] + 1;
+      matched[t] = (matched[p] && tok[t] == am[p]) ? 1 : 0;
+      if (matched[t] && depth[t] > depth[best]) best = t;
+    }
+    const int len = depth[best];
+    int node = best;
+    for (int d = len; d >= 0; --d) {
+      path_s[d] = node;
+      node = args.tree ? par[node] : node - 1;
+    }
+    len_s = len;
+    args.accept_node[r] = best;
+    args.accept_len[r] = len;
+    args.bonus[r] = am[best];
+  }
+  __syncthreads();
+  if (lane < T_) args.path[static_cast<size_t>(r) * T_ + lane] = lane <= len_s ? path_s[lane] : -1;
+}
+
+}  // namespace
+}  // namespace hrs
+
+using namespace hrs;
+
+static bool accept_desc_ok(const hrs_accept_desc* d) {
+  return d && d->n_req >= 1 && d->vocab >= 8 && d->vocab % 8 == 0 && dtype_ok(d->logit_dtype) &&
+         (d->topo == HRS_CHAIN || d->topo == HRS_TREE) && d->n_pos >= 1 && d->n_pos <= HRS_MAX_POS &&
+         static_cast<int64_t>(d->n_req) * d->n_pos <= 65535 * 64;
+}
+
+static int accept_chunks(const hrs_accept_desc* d) { return (d->vocab + kChunk - 1) / kChunk; }
+
+extern "C" size_t accept_greedy_workspace_bytes(const hrs_accept_desc* d) {
+  if (!accept_desc_ok(d)) return 0;
+  return static_cast<size_t>(d->n_req) * d->n_pos * accept_chunks(d) * sizeof(uint64_t);
+}
+
+extern "C" int accept_greedy(const hrs_accept_desc* d, const void* logits, const int32_t* tokens, int32_t* argmax,
+                             int32_t* accept_node, int32_t* accept_len, int32_t* path, int32_t* bonus,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (d == nullptr) return HRS_EINVAL;
+  if (d->topo == HRS_TREE || d->topo == HRS_CHAIN) {
+    const int geo = check_topology(d->topo, d->parent, d->n_req < 1 ? 0 : d->n_req, d->n_pos);
+    if (geo != HRS_OK) return geo;
+  }
+  if (!accept_desc_ok(d)) return HRS_EINVAL;
+  if (!logits || !tokens || !argmax || !accept_node || !accept_len || !path || !bonus || !workspace)
+    return HRS_EINVAL;
+  if (workspace_bytes < accept_greedy_workspace_bytes(d)) return HRS_EINVAL;
+  if (!aligned16(logits) || !aligned16(tokens) || !aligned16(argmax) || !aligned16(accept_node) ||
+      !aligned16(accept_len) || !aligned16(path) || !aligned16(bonus) || !aligned16(workspace))
+    return HRS_EALIGN;
+
+  const int n_chunks = accept_chunks(d);
+  const int rows = d->n_req * d->n_pos;
+  uint64_t* keys = static_cast<uint64_t*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const dim3 grid1(rows * n_chunks);
+  if (d->logit_dtype == HRS_BF16)
+    hipLaunchKernelGGL(argmax_partial_kernel<uint16_t>, grid1, dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(logits), keys, d->vocab, n_chunks);
+  else
+    hipLaunchKernelGGL(argmax_partial_kernel<float>, grid1, dim3(kThreads), 0, s,
+                       static_cast<const float*>(logits), keys, d->vocab, n_chunks);
+  if (hipGetLastError() != hipSuccess) return HRS_EDEVICE;
+
+  AcceptArgs args;
+  args.tokens = tokens; args.keys = keys; args.argmax = argmax; args.accept_node = accept_node;
+  args.accept_len = accept_len; args.path = path; args.bonus = bonus;
+  args.n_pos = d->n_pos; args.n_chunks = n_chunks;
+  args.tree = d->topo == HRS_TREE;
+  const int per_launch = args.tree ? std::max(1, kGeomBytes / d->n_pos) : 65535;
+  for (int r0 = 0; r0 < d->n_req; r0 += per_launch) {
+    const int n = std::min(per_launch, d->n_req - r0);
+    args.req0 = r0;
+    if (args.tree)
+      for (int i = 0; i < n * d->n_pos; ++i)
+        args.parent[i] = static_cast<int8_t>(d->parent[static_cast<size_t>(r0) * d->n_pos + i]);
+    hipLaunchKernelGGL(accept_walk_kernel, dim3(n), dim3(64), 0, s, args);
+    if (hipGetLastError() != hipSuccess) return HRS_EDEVICE;
+  }
+  return HRS_OK;
+}

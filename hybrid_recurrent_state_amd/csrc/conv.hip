@@ -1,0 +1,220 @@
+// conv1d_verify_span: causal depthwise conv over the verify span with the
+// conv state (last W-1 inputs) captured after every position.
+//
+// The hybrid layer's state is the recurrent state plus a short conv state
+// (openinfer PR #626, "feat(qwen35): add opt-in DFlash speculative
+// decoding", What Changed); restoring it after rollback is on-device
+// (lucebox PR #533, "feat: DFlash support for tensor-parallel Qwen3.6
+// targets", Changes).
+//
+// MI355X design: in capture mode every (position, 8-channel group) is an
+// independent thread. The host turns the parent array into a table that
+// names, for each position and window slot, the x row or conv-state row to
+// read, so chain and tree run the same code and all T positions proceed in
+// parallel (x rows are re-read from L2 by up to W threads). Loads and stores
+// are 16 bytes per lane, coalesced along channels. Captured states are raw
+// copies of input bits, so they are exact in any dtype. Without capture
+// (decode, chain only) one thread walks its channels through the positions
+// in order and writes the advanced state at the end, so no thread reads a
+// state row another thread has already overwritten.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "device.h"
+#include "internal.h"
+
+namespace hrs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWidth = 4;
+constexpr int kBack = kWidth - 1;
+
+struct ConvArgs {
+  const void* x;
+  const void* w;
+  void* conv_state;
+  void* conv_ckpt;
+  float* y;
+  int32_t n_pos;
+  int32_t channels;
+  int32_t req0;
+  int32_t per_request_table;  // 0: one table shared by all requests (chain)
+  int32_t silu;
+  int8_t src[kGeomBytes];     // [requests of this launch or 1][n_pos][W-1]
+};
+
+// Eight consecutive elements of a row, kept as raw bits and as f32.
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void store(uint16_t* p) const { *reinterpret_cast<u32x4*>(p) = v; }
+  __device__ __forceinline__ float f(int i) const {
+    const uint32_t w = v[i >> 1];
+    return (i & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+};
+template <> struct Raw8<float> {
+  f32x4 v0, v1;
+  __device__ __forceinline__ void load(const float* p) {
+    v0 = *reinterpret_cast<const f32x4*>(p);
+    v1 = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void store(float* p) const {
+    *reinterpret_cast<f32x4*>(p) = v0;
+    *reinterpret_cast<f32x4*>(p + 4) = v1;
+  }
+  __device__ __forceinline__ float f(int i) const { return i < 4 ? v0[i] : v1[i - 4]; }
+};
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Weights of 8 channels: w[c][m], c in [c0, c0+8), m in [0, W).
+template <typename T>
+__device__ __forceinline__ void load_weights(const T* w, int c0, float (&wt)[8][kWidth]) {
+  float buf[8 * kWidth];
+#pragma unroll
+  for (int i = 0; i < kWidth; ++i) load8<T>(w + static_cast<size_t>(c0) * kWidth + 8 * i, buf + 8 * i);
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int m = 0; m < kWidth; ++m) wt[c][m] = buf[c * kWidth + m];
+}
+
+template <typename T>
+__device__ __forceinline__ void conv_out(const float (&wt)[8][kWidth], const Raw8<T> (&win)[kWidth], int silu_on,
+                                         float* y) {
+  float o[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float acc = wt[c][0] * win[0].f(c);
+#pragma unroll
+    for (int m = 1; m < kWidth; ++m) acc = __builtin_fmaf(wt[c][m], win[m].f(c), acc);
+    o[c] = silu_on ? silu(acc) : acc;
+  }
+  *reinterpret_cast<f32x4*>(y) = f32x4{o[0], o[1], o[2], o[3]};
+  *reinterpret_cast<f32x4*>(y + 4) = f32x4{o[4], o[5], o[6], o[7]};
+}
+
+// Capture mode: one thread per (position, 8-channel group).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void conv_capture_kernel(const ConvArgs args) {
+  const int C = args.channels;
+  const int c0 = (blockIdx.x * kThreads + threadIdx.x) * 8;
+  if (c0 >= C) return;
+  const int T_ = args.n_pos;
+  const int t = blockIdx.y;
+  const int rl = blockIdx.z;
+  const int r = args.req0 + rl;
+  const T* x = static_cast<const T*>(args.x);
+  const T* cs = static_cast<const T*>(args.conv_state);
+  T* ck = static_cast<T*>(args.conv_ckpt);
+  const int8_t* src = args.src + (args.per_request_table ? rl * T_ * kBack : 0) + t * kBack;
+
+  Raw8<T> win[kWidth];
+#pragma unroll
+  for (int m = 0; m < kBack; ++m) {
+    const int s = src[m];
+    if (s >= 0)
+      win[m].load(x + (static_cast<size_t>(r) * T_ + s) * C + c0);
+    else
+      win[m].load(cs + (static_cast<size_t>(r) * kBack + (-1 - s)) * C + c0);
+  }
+  win[kBack].load(x + (static_cast<size_t>(r) * T_ + t) * C + c0);
+  float wt[8][kWidth];
+  load_weights<T>(static_cast<const T*>(args.w), c0, wt);
+
+  conv_out<T>(wt, win, args.silu, args.y + (static_cast<size_t>(r) * T_ + t) * C + c0);
+  T* dst = ck + (static_cast<size_t>(r) * T_ + t) * kBack * C + c0;
+#pragma unroll
+  for (int m = 0; m < kBack; ++m) win[m + 1].store(dst + static_cast<size_t>(m) * C);
+}
+
+// No capture (chain): one thread per 8-channel group walks the positions.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void conv_inplace_kernel(const ConvArgs args) {
+  const int C = args.channels;
+  const int c0 = (blockIdx.x * kThreads + threadIdx.x) * 8;
+  if (c0 >= C) return;
+  const int T_ = args.n_pos;
+  const int r = args.req0 + blockIdx.z;
+  const T* x = static_cast<const T*>(args.x);
+  T* cs = static_cast<T*>(args.conv_state);
+  Raw8<T> win[kWidth];
+#pragma unroll
+  for (int m = 0; m < kBack; ++m) win[m].load(cs + (static_cast<size_t>(r) * kBack + m) * C + c0);
+  float wt[8][kWidth];
+  load_weights<T>(static_cast<const T*>(args.w), c0, wt);
+  for (int t = 0; t < T_; ++t) {
+    win[kBack].load(x + (static_cast<size_t>(r) * T_ + t) * C + c0);
+    conv_out<T>(wt, win, args.silu, args.y + (static_cast<size_t>(r) * T_ + t) * C + c0);
+#pragma unroll
+    for (int m = 0; m < kBack; ++m) win[m] = win[m + 1];
+  }
+#pragma unroll
+  for (int m = 0; m < kBack; ++m) win[m].store(cs + (static_cast<size_t>(r) * kBack + m) * C + c0);
+}
+
+template <typename T>
+hipError_t launch(ConvArgs& args, bool capture, int n, hipStream_t s) {
+  const int groups = args.channels / 8;
+  dim3 block(kThreads);
+  if (capture) {
+    dim3 grid((groups + kThreads - 1) / kThreads, args.n_pos, n);
+    hipLaunchKernelGGL(conv_capture_kernel<T>, grid, block, 0, s, args);
+  } else {
+    dim3 grid((groups + kThreads - 1) / kThreads, 1, n);
+    hipLaunchKernelGGL(conv_inplace_kernel<T>, grid, block, 0, s, args);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace hrs
+
+using namespace hrs;
+
+extern "C" int conv1d_verify_span(const hrs_conv_desc* d, const void* x, const void* w, void* conv_state,
+                                  void* conv_ckpt, float* y, void* stream) {
+  if (d == nullptr) return HRS_EINVAL;
+  if (d->n_req < 1 || d->channels < 8 || d->channels % 8 != 0 || d->width < 2) return HRS_EINVAL;
+  if (!dtype_ok(d->dtype)) return HRS_EINVAL;
+  if (d->topo != HRS_CHAIN && d->topo != HRS_TREE) return HRS_EINVAL;
+  if (!x || !w || !conv_state || !y) return HRS_EINVAL;
+  if (d->topo == HRS_TREE && conv_ckpt == nullptr) return HRS_EINVAL;
+  if (d->n_req > 65535 * 64) return HRS_EINVAL;
+  const int geo = check_topology(d->topo, d->parent, d->n_req, d->n_pos);
+  if (geo != HRS_OK) return geo;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(conv_state) || !aligned16(y) ||
+      (conv_ckpt && !aligned16(conv_ckpt)))
+    return HRS_EALIGN;
+  if (d->width != kWidth) return HRS_EUNSUPPORTED;
+
+  ConvArgs args;
+  args.x = x; args.w = w; args.conv_state = conv_state; args.conv_ckpt = conv_ckpt; args.y = y;
+  args.n_pos = d->n_pos; args.channels = d->channels; args.silu = d->silu != 0;
+  const bool tree = d->topo == HRS_TREE;
+  const bool capture = conv_ckpt != nullptr;
+  const int T_ = d->n_pos;
+  const int table = T_ * kBack;
+  int per_launch = 65535;
+  args.per_request_table = tree ? 1 : 0;
+  if (tree) per_launch = std::max(1, kGeomBytes / table);
+  else conv_window_sources(nullptr, T_, kWidth, args.src);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  for (int r0 = 0; r0 < d->n_req; r0 += per_launch) {
+    const int n = std::min(per_launch, d->n_req - r0);
+    args.req0 = r0;
+    if (tree)
+      for (int i = 0; i < n; ++i)
+        conv_window_sources(d->parent + static_cast<size_t>(r0 + i) * T_, T_, kWidth, args.src + i * table);
+    const hipError_t e = d->dtype == HRS_BF16 ? launch<uint16_t>(args, capture, n, s)
+                                              : launch<float>(args, capture, n, s);
+    if (e != hipSuccess) return HRS_EDEVICE;
+  }
+  return HRS_OK;
+}

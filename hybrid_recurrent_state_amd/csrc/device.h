@@ -1,0 +1,61 @@
+// Device helpers shared by the HIP translation units (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hrs {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 -> f32 is exact: the bf16 pattern is the upper half of the f32.
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_one(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+
+// Load one element of a float or bf16 array as f32.
+template <typename T> __device__ __forceinline__ float load_elem(const T* p, size_t i);
+template <> __device__ __forceinline__ float load_elem<float>(const float* p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, size_t i) {
+  return bf16_one(p[i]);
+}
+
+// Eight consecutive elements as f32 (16 B of bf16 or 2 x 16 B of f32);
+// the source must be 16-byte aligned.
+template <typename T> __device__ __forceinline__ void load8(const T* p, float* o);
+template <> __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* o) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+  o[0] = bf16_lo(w.x); o[1] = bf16_hi(w.x);
+  o[2] = bf16_lo(w.y); o[3] = bf16_hi(w.y);
+  o[4] = bf16_lo(w.z); o[5] = bf16_hi(w.z);
+  o[6] = bf16_lo(w.w); o[7] = bf16_hi(w.w);
+}
+template <> __device__ __forceinline__ void load8<float>(const float* p, float* o) {
+  const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 y = *reinterpret_cast<const f32x4*>(p + 4);
+  o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+  o[4] = y.x; o[5] = y.y; o[6] = y.z; o[7] = y.w;
+}
+
+// Cross-lane move inside a 16-lane DPP row. CTRL is a DPP control code:
+// 0xB1 quad_perm[1,0,3,2], 0x4E quad_perm[2,3,0,1], 0x141 row_half_mirror,
+// 0x140 row_mirror. Every lane has a valid source for these patterns.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Butterfly sum over aligned groups of N lanes (N in {4, 8, 16}). Every lane
+// of a group ends with the same bits (IEEE addition is commutative), and the
+// association order is fixed, so results are reproducible.
+template <int N> __device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  if (N >= 8) x += dpp_mov<0x141>(x);
+  if (N >= 16) x += dpp_mov<0x140>(x);
+  return x;
+}
+
+}  // namespace hrs

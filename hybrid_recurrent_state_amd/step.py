@@ -1,0 +1,235 @@
+"""One verify step over a stack of GDN layers, on one stream, one host sync.
+
+Order of the step (all on the caller's stream):
+  for each layer: conv1d_verify_span, then gdn_verify_span (checkpoints on)
+  accept_greedy over the target logits
+  rollback_restore of every layer to the accepted position (index stays on
+  the device)
+  ring_set_2d, ring_get_2d of the step's hidden-feature rows
+then one device-to-host copy of the accepted lengths and bonus tokens,
+which is the step's only synchronisation (lucebox PR #533, "feat: DFlash
+support for tensor-parallel Qwen3.6 targets", Changes: restore SSM and conv
+state on device and synchronize once after rollback).
+
+Buffers are allocated once by ``StepBuffers`` (device memory through torch)
+and every descriptor and pointer of the step is computed once by
+``VerifyStep``, so launching a step is a fixed sequence of C calls.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+from . import (AcceptDesc, ConvDesc, GdnDesc, HRS_BF16, HRS_CHAIN, HRS_F32, HRS_TREE, HrsError, RingDesc,
+               RingRun, RollbackDesc, accept_greedy_workspace_bytes, lib)
+
+
+@dataclasses.dataclass(frozen=True)
+class StepShape:
+    n_layers: int
+    n_req: int
+    n_pos: int
+    n_kheads: int
+    n_vheads: int
+    d_k: int
+    d_v: int
+    bf16: bool                 # q/k/v/a/b and conv dtype (state is always f32)
+    conv_channels: int
+    conv_width: int = 4
+    vocab: int = 0             # 0: no logits; accept_node is provided directly
+    ring_slots: int = 0        # 0: no feature ring
+    ring_width: int = 0
+
+    @property
+    def gdn_bytes_per_layer(self) -> int:
+        """Algorithmic HBM bytes of one gdn_verify_span call with capture:
+        read q, k, v, a, b and the state once; write every checkpoint and
+        every output once."""
+        R, T, Hk, Hv, dk, dv = self.n_req, self.n_pos, self.n_kheads, self.n_vheads, self.d_k, self.d_v
+        e = 2 if self.bf16 else 4
+        reads = R * T * (2 * Hk * dk + Hv * dv + 2 * Hv) * e + R * Hv * dv * dk * 4
+        writes = R * T * Hv * dv * dk * 4 + R * T * Hv * dv * 4
+        return reads + writes
+
+    @property
+    def conv_bytes_per_layer(self) -> int:
+        R, T, C, W = self.n_req, self.n_pos, self.conv_channels, self.conv_width
+        e = 2 if self.bf16 else 4
+        return R * T * C * e + C * W * e + R * (W - 1) * C * e + R * T * (W - 1) * C * e + R * T * C * 4
+
+    @property
+    def accept_bytes(self) -> int:
+        e = 2 if self.bf16 else 4
+        return self.n_req * self.n_pos * self.vocab * e
+
+    @property
+    def rollback_bytes(self) -> int:
+        """Read + write of one checkpoint per (layer, request), state and conv."""
+        e = 2 if self.bf16 else 4
+        per = self.n_vheads * self.d_v * self.d_k * 4 + (self.conv_width - 1) * self.conv_channels * e
+        return 2 * self.n_layers * self.n_req * per
+
+    @property
+    def ring_bytes(self) -> int:
+        """set + get: each moves n_req * n_pos rows in and out."""
+        return 2 * 2 * self.n_req * self.n_pos * self.ring_width * 2
+
+
+class StepBuffers:
+    """Device buffers of one step, laid out [L, ...] per layer (torch owned)."""
+
+    def __init__(self, shape: StepShape, device="cuda"):
+        import torch
+        s = shape
+        dt = torch.bfloat16 if s.bf16 else torch.float32
+        L, R, T, Hk, Hv, dk, dv, C, W = (s.n_layers, s.n_req, s.n_pos, s.n_kheads, s.n_vheads, s.d_k, s.d_v,
+                                         s.conv_channels, s.conv_width)
+        e = lambda *shp, dtype=dt: torch.empty(shp, dtype=dtype, device=device)
+        self.shape = s
+        self.q = e(L, R, T, Hk, dk)
+        self.k = e(L, R, T, Hk, dk)
+        self.v = e(L, R, T, Hv, dv)
+        self.a = e(L, R, T, Hv)
+        self.b = e(L, R, T, Hv)
+        self.state = e(L, R, Hv, dv, dk, dtype=torch.float32)
+        self.ckpt = e(L, R, T, Hv, dv, dk, dtype=torch.float32)
+        self.out = e(L, R, T, Hv, dv, dtype=torch.float32)
+        self.x = e(L, R, T, C)
+        self.w = e(L, C, W)
+        self.conv_state = e(L, R, W - 1, C)
+        self.conv_ckpt = e(L, R, T, W - 1, C)
+        self.y = e(L, R, T, C, dtype=torch.float32)
+        self.tokens = e(R, T, dtype=torch.int32)
+        self.argmax = e(R, T, dtype=torch.int32)
+        self.accept_node = torch.zeros(R, dtype=torch.int32, device=device)
+        self.accept_len = e(R, dtype=torch.int32)
+        self.path = e(R, T, dtype=torch.int32)
+        self.bonus = e(R, dtype=torch.int32)
+        self.status = torch.zeros(4, dtype=torch.int32, device=device)
+        self.logits = e(R, T, s.vocab) if s.vocab else None
+        self.workspace = None
+        if s.vocab:
+            nbytes = accept_greedy_workspace_bytes(R, T, s.vocab, HRS_BF16 if s.bf16 else HRS_F32)
+            self.workspace = torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
+        self.ring = e(R, s.ring_slots, s.ring_width, dtype=torch.bfloat16) if s.ring_slots else None
+        self.packed_in = e(R * T, s.ring_width, dtype=torch.bfloat16) if s.ring_slots else None
+        self.packed_out = e(R * T, s.ring_width, dtype=torch.bfloat16) if s.ring_slots else None
+        # Host mirror of the step's only device-to-host transfer.
+        self.host_result = torch.empty(2 * R, dtype=torch.int32, pin_memory=True)
+        self.dev_result = torch.empty(2 * R, dtype=torch.int32, device=device)
+
+
+def _check(st: int, name: str) -> None:
+    if st != 0:
+        raise HrsError(st, name)
+
+
+class VerifyStep:
+    """Precomputed launch sequence of one verify step.
+
+    parent: None (chain) or host ints [R, T] (draft trees, one per request).
+    runs: ring runs (ring_id, start_pos, n_rows, packed_row) for set and get.
+    """
+
+    def __init__(self, bufs: StepBuffers, parent=None, runs: Optional[Sequence[tuple]] = None,
+                 silu: bool = False, q_scale: float = 1.0):
+        s = bufs.shape
+        self.bufs = bufs
+        L, R, T = s.n_layers, s.n_req, s.n_pos
+        self.topo = HRS_TREE if parent is not None else HRS_CHAIN
+        dt = HRS_BF16 if s.bf16 else HRS_F32
+        if parent is not None:
+            self._parent = np.ascontiguousarray(np.broadcast_to(np.asarray(parent, dtype=np.int32), (R, T)))
+            par_p = self._parent.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        else:
+            self._parent, par_p = None, None
+        self.gdn_desc = GdnDesc(R, T, s.n_kheads, s.n_vheads, s.d_k, s.d_v, dt, q_scale, self.topo, par_p)
+        self.conv_desc = ConvDesc(R, T, s.conv_channels, s.conv_width, dt, int(silu), self.topo, par_p)
+        self.accept_desc = AcceptDesc(R, T, s.vocab, dt, self.topo, par_p) if s.vocab else None
+        self.rb_desc = RollbackDesc(L, R, T, s.n_vheads, s.d_k, s.d_v, s.conv_channels, s.conv_width, dt)
+        self.runs = list(runs or [])
+        if s.ring_slots and self.runs:
+            self._runs_arr = (RingRun * len(self.runs))(*[RingRun(*map(int, r)) for r in self.runs])
+            self.ring_desc = RingDesc(R, s.ring_slots, s.ring_width, HRS_BF16, R * T, len(self.runs),
+                                      self._runs_arr)
+        else:
+            self.ring_desc = None
+
+        b = bufs
+        ptr = lambda t, l: t[l].data_ptr()
+        self.layer_args: List[tuple] = []
+        for l in range(L):
+            self.layer_args.append((
+                (ptr(b.x, l), ptr(b.w, l), ptr(b.conv_state, l), ptr(b.conv_ckpt, l), ptr(b.y, l)),
+                (ptr(b.q, l), ptr(b.k, l), ptr(b.v, l), ptr(b.a, l), ptr(b.b, l), ptr(b.state, l),
+                 ptr(b.ckpt, l), ptr(b.out, l)),
+            ))
+        if s.vocab:
+            self.accept_args = (b.logits.data_ptr(), b.tokens.data_ptr(), b.argmax.data_ptr(),
+                                b.accept_node.data_ptr(), b.accept_len.data_ptr(), b.path.data_ptr(),
+                                b.bonus.data_ptr(), b.workspace.data_ptr(),
+                                b.workspace.numel())
+        self.rb_args = (b.ckpt.data_ptr(), b.state.data_ptr(), b.conv_ckpt.data_ptr(), b.conv_state.data_ptr(),
+                        b.accept_node.data_ptr(), b.status.data_ptr())
+        self.gdn_p = ctypes.byref(self.gdn_desc)
+        self.conv_p = ctypes.byref(self.conv_desc)
+        self.rb_p = ctypes.byref(self.rb_desc)
+
+    # -- pieces -------------------------------------------------------------
+    def launch_layer(self, l: int, stream: int, events=None) -> None:
+        conv_a, gdn_a = self.layer_args[l]
+        _check(lib.conv1d_verify_span(self.conv_p, *conv_a, stream), "conv1d_verify_span")
+        if events is not None:
+            events[0].record()
+        _check(lib.gdn_verify_span(self.gdn_p, *gdn_a, stream), "gdn_verify_span")
+        if events is not None:
+            events[1].record()
+
+    def launch_accept(self, stream: int) -> None:
+        if self.accept_desc is not None:
+            _check(lib.accept_greedy(ctypes.byref(self.accept_desc), *self.accept_args, stream), "accept_greedy")
+
+    def launch_rollback(self, stream: int) -> None:
+        _check(lib.rollback_restore(self.rb_p, *self.rb_args, stream), "rollback_restore")
+
+    def launch_ring(self, stream: int) -> None:
+        if self.ring_desc is None:
+            return
+        b = self.bufs
+        _check(lib.ring_set_2d(ctypes.byref(self.ring_desc), b.ring.data_ptr(), b.packed_in.data_ptr(), stream),
+               "ring_set_2d")
+        _check(lib.ring_get_2d(ctypes.byref(self.ring_desc), b.ring.data_ptr(), b.packed_out.data_ptr(), stream),
+               "ring_get_2d")
+
+    # -- whole step -----------------------------------------------------------
+    def launch(self, stream=None, gdn_events=None) -> None:
+        """Issue the whole step on ``stream`` (torch stream or raw handle); no sync.
+
+        gdn_events: optional list of (start, end) torch events per layer,
+        recorded around each gdn_verify_span launch (same stream).
+        """
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        h = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        for l in range(self.bufs.shape.n_layers):
+            self.launch_layer(l, h, None if gdn_events is None else gdn_events[l])
+        self.launch_accept(h)
+        self.launch_rollback(h)
+        self.launch_ring(h)
+
+    def finish(self):
+        """The step's single host sync: accepted lengths and bonus tokens."""
+        b = self.bufs
+        R = self.bufs.shape.n_req
+        b.dev_result[:R].copy_(b.accept_len)
+        b.dev_result[R:].copy_(b.bonus)
+        b.host_result.copy_(b.dev_result)   # blocking copy into pinned memory
+        return b.host_result[:R].numpy().copy(), b.host_result[R:].numpy().copy()
+
+    def run(self, stream=None):
+        self.launch(stream)
+        return self.finish()

@@ -1,0 +1,246 @@
+"""The C-ABI boundary on the host: the library loads, exports every function
+include/hrs.h declares, and rejects malformed calls before any launch.
+
+No compute runs here. Device pointers are fake aligned addresses that the
+host code never dereferences; a call that got past its checks would try to
+launch and return HRS_EDEVICE (no GPU in this environment), so seeing the
+specific rejection code proves the check ran first.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from tests.conftest import ROOT
+
+
+def _ensure_built():
+    lib = os.path.join(ROOT, "hybrid_recurrent_state_amd", "libhrs.so")
+    if not os.path.exists(lib):
+        from hybrid_recurrent_state_amd.build import build
+        build()
+
+
+_ensure_built()
+import hybrid_recurrent_state_amd as hrs  # noqa: E402
+from oracle import geometry as ogeo  # noqa: E402
+from tests.test_oracle_geometry import load_cases  # noqa: E402
+
+FAKE = 0x7F0000000000      # 16-byte aligned, never dereferenced on the host
+MIS = FAKE + 4             # misaligned
+P = ctypes.c_void_p
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "hrs.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "return")))
+
+
+def test_every_declared_function_is_exported():
+    names = header_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(hrs.lib, n), n
+    assert sorted(hrs.EXPORTED) == names
+
+
+def test_abi_version_and_strerror():
+    assert hrs.abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5):
+        assert hrs.strerror(st) and hrs.strerror(st) != "unknown status"
+    assert hrs.strerror(-99) == "unknown status"
+
+
+def test_guard_matches_golden_and_oracle(golden_dir):
+    codes = {v: k for k, v in ogeo.NAMES.items()}
+    for name, parent, n, chain_v, tree_v in load_cases(golden_dir):
+        for req_chain, exp in ((True, chain_v), (False, tree_v)):
+            st, cls = hrs.validate_tree(parent, n, req_chain)
+            assert cls == exp, (name, req_chain, cls)
+            assert st == (0 if exp == "OK" else hrs.HRS_EGEOMETRY)
+            assert codes[cls] == ogeo.check_tree(parent, n, req_chain)
+
+
+def test_guard_random_arrays_agree_with_oracle():
+    rng = np.random.default_rng(11)
+    for _ in range(3000):
+        T = int(rng.integers(0, 10))
+        parent = rng.integers(-3, T + 2, T).astype(np.int32)
+        if rng.random() < 0.5 and T > 0:
+            parent = np.arange(-1, T - 1, dtype=np.int32)
+            i = int(rng.integers(0, T))
+            parent[i] = int(rng.integers(-2, T + 1))
+        for req_chain in (True, False):
+            st, cls = hrs.validate_tree(parent, T, req_chain)
+            assert cls == ogeo.NAMES[ogeo.check_tree(parent, T, req_chain)]
+
+
+# ---------------------------------------------------------------------------
+# Fail-closed entry points
+
+
+def gdn_call(**kw):
+    d = dict(n_req=1, n_pos=4, n_kheads=2, n_vheads=4, d_k=128, d_v=128, in_dtype=hrs.HRS_BF16,
+             q_scale=1.0, topo=hrs.HRS_CHAIN, parent=None)
+    ptrs = dict(q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, state=FAKE, ckpt=FAKE, out=FAKE)
+    for key in list(kw):
+        if key in ptrs:
+            ptrs[key] = kw.pop(key)
+    d.update(kw)
+    par = d.pop("parent")
+    keep = None
+    if par is not None:
+        keep = np.ascontiguousarray(np.asarray(par, dtype=np.int32))
+        par = keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    desc = hrs.GdnDesc(d["n_req"], d["n_pos"], d["n_kheads"], d["n_vheads"], d["d_k"], d["d_v"],
+                       d["in_dtype"], d["q_scale"], d["topo"], par)
+    return hrs.lib.gdn_verify_span(ctypes.byref(desc), ptrs["q"], ptrs["k"], ptrs["v"], ptrs["a"], ptrs["b"],
+                                   ptrs["state"], ptrs["ckpt"], ptrs["out"], None)
+
+
+def test_gdn_rejections():
+    E = hrs
+    assert hrs.lib.gdn_verify_span(None, *([FAKE] * 8), None) == E.HRS_EINVAL
+    assert gdn_call(n_req=0) == E.HRS_EINVAL
+    assert gdn_call(n_vheads=3) == E.HRS_EINVAL            # Hv % Hk
+    assert gdn_call(in_dtype=7) == E.HRS_EINVAL
+    assert gdn_call(topo=5) == E.HRS_EINVAL
+    assert gdn_call(q=None) == E.HRS_EINVAL
+    assert gdn_call(out=None) == E.HRS_EINVAL
+    assert gdn_call(n_pos=0) == E.HRS_EGEOMETRY            # truncated
+    assert gdn_call(n_pos=65) == E.HRS_EGEOMETRY
+    assert gdn_call(topo=E.HRS_TREE, parent=None) == E.HRS_EGEOMETRY   # null geometry
+    assert gdn_call(topo=E.HRS_TREE, parent=[-1, 0, 0, 1], ckpt=None) == E.HRS_EINVAL  # tree needs capture
+    assert gdn_call(topo=E.HRS_TREE, parent=[-1, 0, 3, 1]) == E.HRS_EGEOMETRY  # forward
+    assert gdn_call(topo=E.HRS_TREE, parent=[0, 0, 1, 1]) == E.HRS_EGEOMETRY   # root
+    # second request of a batch malformed
+    assert gdn_call(n_req=2, topo=E.HRS_TREE, parent=[-1, 0, 0, 1, -1, 0, -1, 2]) == E.HRS_EGEOMETRY
+    assert gdn_call(v=MIS) == E.HRS_EALIGN
+    assert gdn_call(ckpt=MIS) == E.HRS_EALIGN
+    assert gdn_call(d_k=96) == E.HRS_EUNSUPPORTED
+    assert gdn_call(d_v=24) == E.HRS_EUNSUPPORTED
+    # a well-formed call gets past every check; without a GPU the launch fails
+    assert gdn_call() in (E.HRS_EDEVICE, E.HRS_OK)
+
+
+def conv_call(**kw):
+    d = dict(n_req=1, n_pos=4, channels=64, width=4, dtype=hrs.HRS_BF16, silu=0, topo=hrs.HRS_CHAIN, parent=None)
+    ptrs = dict(x=FAKE, w=FAKE, cs=FAKE, ck=FAKE, y=FAKE)
+    for key in list(kw):
+        if key in ptrs:
+            ptrs[key] = kw.pop(key)
+    d.update(kw)
+    par = d.pop("parent")
+    keep = None
+    if par is not None:
+        keep = np.ascontiguousarray(np.asarray(par, dtype=np.int32))
+        par = keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    desc = hrs.ConvDesc(d["n_req"], d["n_pos"], d["channels"], d["width"], d["dtype"], d["silu"], d["topo"], par)
+    return hrs.lib.conv1d_verify_span(ctypes.byref(desc), ptrs["x"], ptrs["w"], ptrs["cs"], ptrs["ck"],
+                                      ptrs["y"], None)
+
+
+def test_conv_rejections():
+    E = hrs
+    assert conv_call(channels=12) == E.HRS_EINVAL
+    assert conv_call(width=1) == E.HRS_EINVAL
+    assert conv_call(x=None) == E.HRS_EINVAL
+    assert conv_call(topo=E.HRS_TREE, parent=[-1, 0, 0, 1], ck=None) == E.HRS_EINVAL
+    assert conv_call(topo=E.HRS_TREE, parent=[-1, 0, 4, 1]) == E.HRS_EGEOMETRY
+    assert conv_call(n_pos=70) == E.HRS_EGEOMETRY
+    assert conv_call(y=MIS) == E.HRS_EALIGN
+    assert conv_call(width=3) == E.HRS_EUNSUPPORTED
+    assert conv_call() in (E.HRS_EDEVICE, E.HRS_OK)
+
+
+def accept_call(ws_bytes=None, **kw):
+    d = dict(n_req=2, n_pos=5, vocab=1024, logit_dtype=hrs.HRS_BF16, topo=hrs.HRS_CHAIN, parent=None)
+    ptrs = dict(logits=FAKE, tokens=FAKE, argmax=FAKE, node=FAKE, ln=FAKE, path=FAKE, bonus=FAKE, ws=FAKE)
+    for key in list(kw):
+        if key in ptrs:
+            ptrs[key] = kw.pop(key)
+    d.update(kw)
+    par = d.pop("parent")
+    keep = None
+    if par is not None:
+        keep = np.ascontiguousarray(np.asarray(par, dtype=np.int32))
+        par = keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    desc = hrs.AcceptDesc(d["n_req"], d["n_pos"], d["vocab"], d["logit_dtype"], d["topo"], par)
+    need = hrs.lib.accept_greedy_workspace_bytes(ctypes.byref(desc))
+    ws = need if ws_bytes is None else ws_bytes
+    return hrs.lib.accept_greedy(ctypes.byref(desc), ptrs["logits"], ptrs["tokens"], ptrs["argmax"], ptrs["node"],
+                                 ptrs["ln"], ptrs["path"], ptrs["bonus"], ptrs["ws"], ws, None), need
+
+
+def test_accept_rejections_and_workspace_size():
+    E = hrs
+    st, need = accept_call()
+    assert need == 2 * 5 * 1 * 8          # one 8192-entry chunk per row, 8-byte keys
+    assert st in (E.HRS_EDEVICE, E.HRS_OK)
+    assert accept_call(vocab=151936)[1] == 2 * 5 * 19 * 8
+    assert accept_call(vocab=1001)[0] == E.HRS_EINVAL
+    assert accept_call(ws_bytes=need - 1)[0] == E.HRS_EINVAL
+    assert accept_call(tokens=None)[0] == E.HRS_EINVAL
+    assert accept_call(n_pos=0)[0] == E.HRS_EGEOMETRY
+    assert accept_call(topo=E.HRS_TREE, parent=[-1, 0, 0, 1, 1, -1, 0, 1, 1, 5])[0] == E.HRS_EGEOMETRY
+    assert accept_call(topo=E.HRS_TREE, parent=[-1, 0, 0, 1, 1, -1, 0, 1, 1, 2])[0] in (E.HRS_EDEVICE, E.HRS_OK)
+    assert accept_call(path=MIS)[0] == E.HRS_EALIGN
+    assert accept_call(vocab=0)[1] == 0
+
+
+def rollback_call(**kw):
+    d = dict(n_layers=2, n_req=3, n_pos=5, n_vheads=4, d_k=64, d_v=64, conv_channels=64, conv_width=4,
+             conv_dtype=hrs.HRS_BF16)
+    ptrs = dict(ckpt=FAKE, state=FAKE, cck=FAKE, cs=FAKE, node=FAKE, status=FAKE)
+    for key in list(kw):
+        if key in ptrs:
+            ptrs[key] = kw.pop(key)
+    d.update(kw)
+    desc = hrs.RollbackDesc(*[d[k] for k in ("n_layers", "n_req", "n_pos", "n_vheads", "d_k", "d_v",
+                                              "conv_channels", "conv_width", "conv_dtype")])
+    return hrs.lib.rollback_restore(ctypes.byref(desc), ptrs["ckpt"], ptrs["state"], ptrs["cck"], ptrs["cs"],
+                                    ptrs["node"], ptrs["status"], None)
+
+
+def test_rollback_rejections():
+    E = hrs
+    assert rollback_call(n_layers=0) == E.HRS_EINVAL
+    assert rollback_call(n_pos=65) == E.HRS_EINVAL
+    assert rollback_call(status=None) == E.HRS_EINVAL
+    assert rollback_call(cs=None) == E.HRS_EINVAL          # conv buffers come in pairs
+    assert rollback_call(state=MIS) == E.HRS_EALIGN
+    assert rollback_call(conv_channels=3, conv_dtype=hrs.HRS_BF16) == E.HRS_EINVAL  # 3 rows x 3 x 2 B not 16-B
+    assert rollback_call() in (E.HRS_EDEVICE, E.HRS_OK)
+    assert rollback_call(cck=None, cs=None, conv_channels=0) in (E.HRS_EDEVICE, E.HRS_OK)
+
+
+def ring_call(setter=True, runs=((0, 14, 5, 0),), n_rings=2, n_slots=16, width=64, dtype=None, n_packed=8,
+              ring=FAKE, packed=FAKE):
+    arr = (hrs.RingRun * max(1, len(runs)))(*[hrs.RingRun(*r) for r in runs])
+    desc = hrs.RingDesc(n_rings, n_slots, width, hrs.HRS_BF16 if dtype is None else dtype, n_packed, len(runs), arr)
+    fn = hrs.lib.ring_set_2d if setter else hrs.lib.ring_get_2d
+    return fn(ctypes.byref(desc), ring, packed, None)
+
+
+def test_ring_rejections():
+    E = hrs
+    for setter in (True, False):
+        assert ring_call(setter) in (E.HRS_EDEVICE, E.HRS_OK)
+        assert ring_call(setter, runs=((2, 0, 1, 0),)) == E.HRS_EINVAL      # ring id
+        assert ring_call(setter, runs=((0, 16, 1, 0),)) == E.HRS_EINVAL     # start
+        assert ring_call(setter, runs=((0, 0, 17, 0),)) == E.HRS_EINVAL     # longer than the ring
+        assert ring_call(setter, runs=((0, 0, 5, 4),)) == E.HRS_EINVAL      # past the packed rows
+        assert ring_call(setter, width=3) == E.HRS_EINVAL                   # row not 16-byte multiple
+        assert ring_call(setter, ring=MIS) == E.HRS_EALIGN
+        assert ring_call(setter, runs=()) == E.HRS_OK                       # nothing to copy
+    # set: two runs writing the same slots (wrap overlap) are rejected
+    assert ring_call(True, runs=((0, 14, 3, 0), (0, 0, 2, 3))) == E.HRS_EINVAL
+    assert ring_call(True, runs=((0, 14, 3, 0), (1, 0, 2, 3))) in (E.HRS_EDEVICE, E.HRS_OK)
+    # get: two runs writing the same packed rows are rejected, same slots are fine
+    assert ring_call(False, runs=((0, 14, 3, 0), (1, 0, 2, 2))) == E.HRS_EINVAL
+    assert ring_call(False, runs=((0, 14, 3, 0), (0, 14, 3, 3))) in (E.HRS_EDEVICE, E.HRS_OK)
