@@ -7,7 +7,7 @@ and passes raw pointers, sizes and the current HIP stream to the C ABI in
 include/hrs.h; all computation happens in the HIP kernels of libhrs.so. A
 negative status from the library raises ``HrsError``.
 
-The library must be built first (``python -m hybrid_recurrent_state_amd.build``
+The library must be built first (``python hybrid_recurrent_state_amd/csrc/build.py``
 or ``__graft_entry__.build()``); importing this package without it raises
 ImportError, so nothing silently falls back to another implementation.
 """
@@ -32,7 +32,10 @@ GEOMETRY_CLASSES = {0: "OK", 1: "NULL", 2: "TRUNCATED", 3: "ROOT", 4: "RANGE", 5
 class HrsError(RuntimeError):
     def __init__(self, status: int, func: str):
         self.status = status
-        super().__init__(f"{func}: {strerror(status)} (status {status})")
+        detail = ""
+        if status == HRS_EDEVICE:
+            detail = f"; HIP error {lib.hrs_last_hip_error()}: {lib.hrs_last_hip_error_string().decode()}"
+        super().__init__(f"{func}: {strerror(status)} (status {status}){detail}")
 
 
 # --- C structs (mirror include/hrs.h) -------------------------------------
@@ -84,14 +87,37 @@ _SIGNATURES = {
     "ring_get_2d": (_i32, [ctypes.POINTER(RingDesc), _p, _p, _p]),
     "hrs_strerror": (ctypes.c_char_p, [_i32]),
     "hrs_abi_version": (_i32, []),
+    "hrs_last_hip_error": (_i32, []),
+    "hrs_last_hip_error_string": (ctypes.c_char_p, []),
 }
 EXPORTED = tuple(_SIGNATURES)
 
 
+def _hip_runtimes_mapped():
+    """Distinct HIP runtime files mapped into this process."""
+    found = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    found.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return found
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m hybrid_recurrent_state_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python hybrid_recurrent_state_amd/csrc/build.py`")
+    # torch owns device memory and streams. Its HIP runtime must be the one
+    # this library binds to: load torch first, so that the library's
+    # libamdhip64.so.7 dependency resolves (by soname) to the runtime that is
+    # already in the process instead of a second copy from /opt/rocm.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError(f"two HIP runtimes are loaded ({sorted(runtimes)}); libhrs must share torch's")
     for name, (res, args) in _SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res

@@ -187,7 +187,7 @@ extern "C" int accept_greedy(const hrs_accept_desc* d, const void* logits, const
   else
     hipLaunchKernelGGL(argmax_partial_kernel<float>, grid1, dim3(kThreads), 0, s,
                        static_cast<const float*>(logits), keys, d->vocab, n_chunks);
-  if (hipGetLastError() != hipSuccess) return HRS_EDEVICE;
+  if (launch_error() != hipSuccess) return HRS_EDEVICE;
 
   AcceptArgs args;
   args.tokens = tokens; args.keys = keys; args.argmax = argmax; args.accept_node = accept_node;
@@ -202,7 +202,7 @@ extern "C" int accept_greedy(const hrs_accept_desc* d, const void* logits, const
       for (int i = 0; i < n * d->n_pos; ++i)
         args.parent[i] = static_cast<int8_t>(d->parent[static_cast<size_t>(r0) * d->n_pos + i]);
     hipLaunchKernelGGL(accept_walk_kernel, dim3(n), dim3(64), 0, s, args);
-    if (hipGetLastError() != hipSuccess) return HRS_EDEVICE;
+    if (launch_error() != hipSuccess) return HRS_EDEVICE;
   }
   return HRS_OK;
 }

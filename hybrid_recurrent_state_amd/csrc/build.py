@@ -1,6 +1,9 @@
 """Build libhrs.so in-tree with hipcc for gfx950.
 
-Usage: python -m hybrid_recurrent_state_amd.build [-v]
+Usage: python hybrid_recurrent_state_amd/csrc/build.py [-v]
+
+(Run as a script or loaded by path: importing the package itself loads the
+library, which must not be required to build it.)
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
 selection disabled and floating-point contraction off (the kernels spell out
@@ -16,8 +19,8 @@ import shutil
 import subprocess
 import sys
 
-PKG = os.path.dirname(os.path.abspath(__file__))
-CSRC = os.path.join(PKG, "csrc")
+CSRC = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.dirname(CSRC)
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhrs.so")
 
@@ -26,7 +29,7 @@ HOST_SOURCES = ["validate.cpp"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument"]
-HIP_FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-ffp-contract=off",
+HIP_FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-ffp-contract=off", "-mcode-object-version=5",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -168,7 +168,7 @@ hipError_t launch(ConvArgs& args, bool capture, int n, hipStream_t s) {
     dim3 grid((groups + kThreads - 1) / kThreads, 1, n);
     hipLaunchKernelGGL(conv_inplace_kernel<T>, grid, block, 0, s, args);
   }
-  return hipGetLastError();
+  return launch_error();
 }
 
 }  // namespace

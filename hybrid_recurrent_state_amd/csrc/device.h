@@ -4,7 +4,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.h"
+
 namespace hrs {
+
+// Error of the launch just issued on this thread; recorded for
+// hrs_last_hip_error().
+inline hipError_t launch_error() {
+  const hipError_t e = hipGetLastError();
+  set_last_hip_error(static_cast<int>(e));
+  return e;
+}
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -207,7 +207,7 @@ hipError_t launch_one(GdnArgs& args, int n_req_launch, hipStream_t stream) {
   dim3 grid(args.d_v / RPB, args.n_vheads, n_req_launch);
   hipLaunchKernelGGL((gdn_span_kernel<DK, LPR, TIn, TREE, CAPTURE>), grid, dim3(kWaves * 64), lds, stream,
                      args);
-  return hipGetLastError();
+  return launch_error();
 }
 
 template <int DK, typename TIn>
@@ -270,4 +270,8 @@ extern "C" int gdn_verify_span(const hrs_gdn_desc* d, const void* q, const void*
     if (e != hipSuccess) return HRS_EDEVICE;
   }
   return HRS_OK;
+}
+
+extern "C" const char* hrs_last_hip_error_string(void) {
+  return hipGetErrorString(static_cast<hipError_t>(hrs_last_hip_error()));
 }

@@ -26,6 +26,9 @@ inline bool dtype_ok(int d) { return d == HRS_F32 || d == HRS_BF16; }
 // (chain mode). Returns HRS_OK or HRS_EGEOMETRY.
 int check_topology(int topo, const int32_t* parent, int32_t n_req, int32_t n_pos);
 
+// Per-thread record of the last HIP error seen by an entry point (0 = none).
+void set_last_hip_error(int err);
+
 // Conv window sources of every position of one request: for window slot m
 // (0 = oldest, W-2 = the slot before the current input) the x row to read
 // (>= 0) or the conv-state row encoded as -1 - row. parent == nullptr means

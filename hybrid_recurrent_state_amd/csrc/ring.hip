@@ -131,7 +131,7 @@ int ring_copy(const hrs_ring_desc* d, bool set, void* ring_w, const void* ring_r
     args.seg_first[n] = rows;
     args.n_seg = n;
     hipLaunchKernelGGL(ring_copy_kernel, dim3(gx, rows), block, 0, s, args);
-    if (hipGetLastError() != hipSuccess) return HRS_EDEVICE;
+    if (launch_error() != hipSuccess) return HRS_EDEVICE;
   }
   return HRS_OK;
 }

@@ -123,5 +123,5 @@ extern "C" int rollback_restore(const hrs_rollback_desc* d, const float* ckpt, f
   const dim3 grid(args.state_chunks + conv_chunks, d->n_layers * d->n_req);
   (void)hipGetLastError();
   hipLaunchKernelGGL(rollback_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), args);
-  return hipGetLastError() == hipSuccess ? HRS_OK : HRS_EDEVICE;
+  return launch_error() == hipSuccess ? HRS_OK : HRS_EDEVICE;
 }

@@ -52,7 +52,15 @@ extern "C" const char* hrs_strerror(int status) {
 
 extern "C" int hrs_abi_version(void) { return HRS_ABI_VERSION; }
 
+namespace {
+thread_local int g_last_hip_error = 0;
+}
+
+extern "C" int hrs_last_hip_error(void) { return g_last_hip_error; }
+
 namespace hrs {
+
+void set_last_hip_error(int err) { g_last_hip_error = err; }
 
 int check_topology(int topo, const int32_t* parent, int32_t n_req, int32_t n_pos) {
   if (topo == HRS_CHAIN) {

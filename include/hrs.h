@@ -32,7 +32,8 @@
  *    except HRS_EDEVICE, which reports that the launch itself failed.
  *    Every argument check runs on the host before any HIP call, so the
  *    checks also work on a machine without a GPU.
- *  - Thread safety: the library holds no mutable global state.
+ *  - Thread safety: the library holds no mutable global state (only a
+ *    per-thread record of the last HIP error, see hrs_last_hip_error).
  *  - Determinism: results are bit-identical from run to run, and the
  *    arithmetic of one position does not depend on the span length or on the
  *    tree topology.
@@ -327,6 +328,14 @@ const char* hrs_strerror(int status);
 
 /* HRS_ABI_VERSION of the built library. */
 int hrs_abi_version(void);
+
+/* hipError_t of the last launch an entry point made on the calling thread
+ * (0 = success): the detail behind HRS_EDEVICE. Per-thread; this record is
+ * the library's only mutable state. */
+int hrs_last_hip_error(void);
+
+/* hipGetErrorString() of hrs_last_hip_error(); never NULL. */
+const char* hrs_last_hip_error_string(void);
 
 #ifdef __cplusplus
 }

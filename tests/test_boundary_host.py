@@ -19,8 +19,8 @@ from tests.conftest import ROOT
 def _ensure_built():
     lib = os.path.join(ROOT, "hybrid_recurrent_state_amd", "libhrs.so")
     if not os.path.exists(lib):
-        from hybrid_recurrent_state_amd.build import build
-        build()
+        import __graft_entry__
+        __graft_entry__.build()
 
 
 _ensure_built()
@@ -47,6 +47,7 @@ def test_every_declared_function_is_exported():
     for n in names:
         assert hasattr(hrs.lib, n), n
     assert sorted(hrs.EXPORTED) == names
+    assert len(hrs._hip_runtimes_mapped()) <= 1, "one HIP runtime per process"
 
 
 def test_abi_version_and_strerror():
