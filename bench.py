@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--workload", default=str(DEFAULT_WORKLOAD))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="before warmup, run a plain device copy of this many MiB three times "
+                         "(reference kernel for scaling the FETCH_SIZE/WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -106,19 +109,33 @@ def main():
     step = VerifyStep(bufs, parent=loaded.parent, runs=loaded.runs)
     stream = torch.cuda.current_stream()
 
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calibrate_copy_mib} MiB read + {args.calibrate_copy_mib} MiB written, x3")
+        del src, dst
+
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step.run(stream)
     torch.cuda.synchronize()
 
     L, K = w.n_layers, args.steps
+    # One event pair per GDN launch of the timed region, recorded by the
+    # dispatch itself (gdn_verify_span_timed): no commands between kernels.
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
           for _ in range(K)]
+    ev_h = [[(hrs.event_handle(s), hrs.event_handle(e)) for (s, e) in row] for row in ev]
+    torch.cuda.synchronize()
     log(f"timing {K} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step.launch(stream, gdn_events=ev[i])
+        step.launch(stream, gdn_events=ev_h[i])
         step.finish()
     torch.cuda.synchronize()
     t1 = time.perf_counter()

@@ -78,6 +78,7 @@ class RingDesc(ctypes.Structure):
 _SIGNATURES = {
     "hrs_validate_tree": (_i32, [ctypes.POINTER(_i32), _i32, _i32, ctypes.POINTER(_i32)]),
     "gdn_verify_span": (_i32, [ctypes.POINTER(GdnDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "gdn_verify_span_timed": (_i32, [ctypes.POINTER(GdnDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "conv1d_verify_span": (_i32, [ctypes.POINTER(ConvDesc), _p, _p, _p, _p, _p, _p]),
     "accept_greedy_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AcceptDesc)]),
     "accept_greedy": (_i32, [ctypes.POINTER(AcceptDesc), _p, _p, _p, _p, _p, _p, _p, _p,
@@ -201,17 +202,31 @@ def validate_tree(parent, n_pos: Optional[int] = None, require_chain: bool = Fal
 hrs_validate_tree = validate_tree
 
 
-def gdn_verify_span(q, k, v, a, b, state, ckpt, out, parent=None, q_scale: float = 1.0, stream=None):
+def event_handle(ev) -> int:
+    """Raw hipEvent_t of a torch.cuda.Event (created by recording it once)."""
+    if not ev.cuda_event:
+        ev.record()
+    return ev.cuda_event
+
+
+def gdn_verify_span(q, k, v, a, b, state, ckpt, out, parent=None, q_scale: float = 1.0, stream=None,
+                    events=None):
     """q, k [R,T,Hk,dk]; v [R,T,Hv,dv]; a, b [R,T,Hv] (f32 or bf16);
     state [R,Hv,dv,dk] f32; ckpt [R,T,Hv,dv,dk] f32 or None; out [R,T,Hv,dv] f32.
-    parent: None (chain) or host ints [R,T] / [T] (tree)."""
+    parent: None (chain) or host ints [R,T] / [T] (tree).
+    events: optional (start, stop) torch.cuda.Event pair recorded by the
+    kernel dispatch itself (gdn_verify_span_timed)."""
     R, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     par, par_p = _parent_array(parent, R, T)
     d = GdnDesc(R, T, Hk, Hv, dk, dv, _dtype_code(q), float(q_scale),
                 HRS_TREE if parent is not None else HRS_CHAIN, par_p)
-    st = lib.gdn_verify_span(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(state),
-                             _ptr(ckpt), _ptr(out), _stream(stream))
+    args = (ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(state), _ptr(ckpt), _ptr(out),
+            _stream(stream))
+    if events is None:
+        st = lib.gdn_verify_span(*args)
+    else:
+        st = lib.gdn_verify_span_timed(*args, event_handle(events[0]), event_handle(events[1]))
     _check(st, "gdn_verify_span")
 
 

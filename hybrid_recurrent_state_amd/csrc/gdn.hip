@@ -27,6 +27,7 @@
 //  * Tree mode: a node whose parent is not the previous position reloads the
 //    parent's checkpoint rows (this lane's own earlier writes) before its
 //    update; the root starts from `state`.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -199,23 +200,25 @@ __global__ __launch_bounds__(kWaves * 64) void gdn_span_kernel(const GdnArgs arg
   }
 }
 
+// Launch through hipExtLaunchKernelGGL so that optional timing events are
+// recorded by the dispatch itself (no extra stream commands between kernels).
 template <int DK, int LPR, typename TIn, bool TREE, bool CAPTURE>
-hipError_t launch_one(GdnArgs& args, int n_req_launch, hipStream_t stream) {
+hipError_t launch_one(GdnArgs& args, int n_req_launch, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   constexpr int RPB = (64 / LPR) * kWaves;
   const int window = std::min(kWindow, static_cast<int>(args.n_pos));
   const size_t lds = static_cast<size_t>(window) * (2 * DK + RPB + 2) * sizeof(float);
   dim3 grid(args.d_v / RPB, args.n_vheads, n_req_launch);
-  hipLaunchKernelGGL((gdn_span_kernel<DK, LPR, TIn, TREE, CAPTURE>), grid, dim3(kWaves * 64), lds, stream,
-                     args);
+  hipExtLaunchKernelGGL((gdn_span_kernel<DK, LPR, TIn, TREE, CAPTURE>), grid, dim3(kWaves * 64), lds, stream,
+                        start, stop, 0, args);
   return launch_error();
 }
 
 template <int DK, typename TIn>
-hipError_t launch_dk(GdnArgs& args, bool tree, bool capture, int n, hipStream_t s) {
+hipError_t launch_dk(GdnArgs& args, bool tree, bool capture, int n, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr int LPR = 16;
-  if (tree) return launch_one<DK, LPR, TIn, true, true>(args, n, s);
-  if (capture) return launch_one<DK, LPR, TIn, false, true>(args, n, s);
-  return launch_one<DK, LPR, TIn, false, false>(args, n, s);
+  if (tree) return launch_one<DK, LPR, TIn, true, true>(args, n, s, e0, e1);
+  if (capture) return launch_one<DK, LPR, TIn, false, true>(args, n, s, e0, e1);
+  return launch_one<DK, LPR, TIn, false, false>(args, n, s, e0, e1);
 }
 
 }  // namespace
@@ -223,9 +226,9 @@ hipError_t launch_dk(GdnArgs& args, bool tree, bool capture, int n, hipStream_t 
 
 using namespace hrs;
 
-extern "C" int gdn_verify_span(const hrs_gdn_desc* d, const void* q, const void* k, const void* v,
-                               const void* a, const void* b, float* state, float* ckpt, float* out,
-                               void* stream) {
+static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, const void* v, const void* a,
+                         const void* b, float* state, float* ckpt, float* out, void* stream, void* start_event,
+                         void* stop_event) {
   if (d == nullptr) return HRS_EINVAL;
   if (d->n_req < 1 || d->n_kheads < 1 || d->n_vheads < 1 || d->d_k < 1 || d->d_v < 1) return HRS_EINVAL;
   if (d->n_vheads % d->n_kheads != 0) return HRS_EINVAL;
@@ -256,20 +259,35 @@ extern "C" int gdn_verify_span(const hrs_gdn_desc* d, const void* q, const void*
   for (int r0 = 0; r0 < d->n_req; r0 += per_launch) {
     const int n = std::min(per_launch, d->n_req - r0);
     args.req0 = r0;
+    // The first launch records the start event, the last one the stop event.
+    hipEvent_t e0 = r0 == 0 ? static_cast<hipEvent_t>(start_event) : nullptr;
+    hipEvent_t e1 = r0 + n >= d->n_req ? static_cast<hipEvent_t>(stop_event) : nullptr;
     if (tree) {
       for (int i = 0; i < n * d->n_pos; ++i)
         args.parent[i] = static_cast<int8_t>(d->parent[static_cast<size_t>(r0) * d->n_pos + i]);
     }
     hipError_t e;
     if (d->d_k == 128)
-      e = d->in_dtype == HRS_BF16 ? launch_dk<128, uint16_t>(args, tree, capture, n, s)
-                                  : launch_dk<128, float>(args, tree, capture, n, s);
+      e = d->in_dtype == HRS_BF16 ? launch_dk<128, uint16_t>(args, tree, capture, n, s, e0, e1)
+                                  : launch_dk<128, float>(args, tree, capture, n, s, e0, e1);
     else
-      e = d->in_dtype == HRS_BF16 ? launch_dk<64, uint16_t>(args, tree, capture, n, s)
-                                  : launch_dk<64, float>(args, tree, capture, n, s);
+      e = d->in_dtype == HRS_BF16 ? launch_dk<64, uint16_t>(args, tree, capture, n, s, e0, e1)
+                                  : launch_dk<64, float>(args, tree, capture, n, s, e0, e1);
     if (e != hipSuccess) return HRS_EDEVICE;
   }
   return HRS_OK;
+}
+
+extern "C" int gdn_verify_span(const hrs_gdn_desc* d, const void* q, const void* k, const void* v,
+                               const void* a, const void* b, float* state, float* ckpt, float* out,
+                               void* stream) {
+  return gdn_span_impl(d, q, k, v, a, b, state, ckpt, out, stream, nullptr, nullptr);
+}
+
+extern "C" int gdn_verify_span_timed(const hrs_gdn_desc* d, const void* q, const void* k, const void* v,
+                                     const void* a, const void* b, float* state, float* ckpt, float* out,
+                                     void* stream, void* start_event, void* stop_event) {
+  return gdn_span_impl(d, q, k, v, a, b, state, ckpt, out, stream, start_event, stop_event);
 }
 
 extern "C" const char* hrs_last_hip_error_string(void) {

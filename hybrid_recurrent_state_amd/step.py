@@ -180,13 +180,14 @@ class VerifyStep:
 
     # -- pieces -------------------------------------------------------------
     def launch_layer(self, l: int, stream: int, events=None) -> None:
+        """conv then GDN of layer l. events: optional (start, stop) raw
+        hipEvent_t handles recorded by the GDN dispatch itself."""
         conv_a, gdn_a = self.layer_args[l]
         _check(lib.conv1d_verify_span(self.conv_p, *conv_a, stream), "conv1d_verify_span")
-        if events is not None:
-            events[0].record()
-        _check(lib.gdn_verify_span(self.gdn_p, *gdn_a, stream), "gdn_verify_span")
-        if events is not None:
-            events[1].record()
+        if events is None:
+            _check(lib.gdn_verify_span(self.gdn_p, *gdn_a, stream), "gdn_verify_span")
+        else:
+            _check(lib.gdn_verify_span_timed(self.gdn_p, *gdn_a, stream, events[0], events[1]), "gdn_verify_span")
 
     def launch_accept(self, stream: int) -> None:
         if self.accept_desc is not None:
@@ -208,8 +209,8 @@ class VerifyStep:
     def launch(self, stream=None, gdn_events=None) -> None:
         """Issue the whole step on ``stream`` (torch stream or raw handle); no sync.
 
-        gdn_events: optional list of (start, end) torch events per layer,
-        recorded around each gdn_verify_span launch (same stream).
+        gdn_events: optional list of (start, stop) raw hipEvent_t handles per
+        layer (see ``event_handle``), recorded by each GDN dispatch.
         """
         import torch
         if stream is None:

@@ -160,6 +160,19 @@ int gdn_verify_span(const hrs_gdn_desc* desc, const void* q, const void* k,
                     const void* v, const void* a, const void* b, float* state,
                     float* ckpt, float* out, void* stream);
 
+/*
+ * gdn_verify_span_timed - gdn_verify_span whose kernel dispatch also records
+ * two caller-created hipEvent_t (from the same HIP runtime as `stream`):
+ * `start_event` as the kernel starts and `stop_event` as it ends. The events
+ * travel inside the dispatch, so no extra command sits between kernels and
+ * the interval is the kernel's own execution. Either event may be NULL.
+ * Measurement support; arguments, results and errors as gdn_verify_span.
+ */
+int gdn_verify_span_timed(const hrs_gdn_desc* desc, const void* q, const void* k,
+                          const void* v, const void* a, const void* b, float* state,
+                          float* ckpt, float* out, void* stream, void* start_event,
+                          void* stop_event);
+
 /* ------------------------------------------------------------------------ */
 /* Causal depthwise conv1d over the span                                    */
 /* ------------------------------------------------------------------------ */
