@@ -11,19 +11,28 @@
 //
 // MI355X design
 //  * The d_v rows of S evolve independently given (k, a, b, v_row), so one
-//    head is split into row blocks: a wave owns 64/LPR rows, LPR lanes per
-//    row, and each lane keeps its DK/LPR columns of S in VGPRs for the whole
-//    span. No MFMA: the span is bound by checkpoint writes (about 1.6 flop
-//    per byte), far below the fp32 ridge point.
-//  * Lane l of a row owns float4 chunks l, l+LPR, ... of the row, so one
-//    store instruction writes LPR consecutive 16-byte chunks per row: whole
-//    128-byte lines. Checkpoints are written with nontemporal stores; they
-//    are not read again until rollback.
-//  * The two row dot products (S k and S q) are butterfly sums over the LPR
+//    head is split into row units: a wave owns 4 rows, 16 lanes per row, and
+//    each lane keeps its DK/16 columns of S in VGPRs for the whole span. No
+//    MFMA: the span is bound by checkpoint writes (about 1.6 flop per byte),
+//    far below the fp32 ridge point.
+//  * Lane l of a row owns float4 chunks l, l+16, ... of the row, so one store
+//    instruction writes 16 consecutive 16-byte chunks per row: whole 128-byte
+//    lines. Checkpoints are written with nontemporal stores; they are not
+//    read again until rollback (normal stores measured ~12% slower).
+//  * Work order: units are numbered row block fastest, then head, then
+//    request, and a block walks units W, W + gridDim.x, ... When there are at
+//    least as many 32-row units as compute units, the grid is one 8-wave block
+//    per CU: all CUs then advance through the positions together and each
+//    position's checkpoint region (2 MiB per request) is written as one
+//    contiguous sweep. Measured on the 16-request Qwen shape: 6.0 TB/s versus
+//    5.1 TB/s for one block per unit, and 75% of HBM peak, at the plain
+//    store-stream ceiling. Smaller problems use one 4-wave block per 16-row
+//    unit to spread over more CUs.
+//  * The two row dot products (S k and S q) are butterfly sums over the 16
 //    lanes with DPP moves; the association order is fixed, so the arithmetic
-//    of a position never depends on span length or topology.
+//    of a position never depends on span length, topology or launch shape.
 //  * k, q (times q_scale), v rows, a and b of a window of positions are
-//    staged once per block into LDS as f32.
+//    staged once per unit into LDS as f32.
 //  * Tree mode: a node whose parent is not the previous position reloads the
 //    parent's checkpoint rows (this lane's own earlier writes) before its
 //    update; the root starts from `state`.
@@ -38,7 +47,7 @@
 namespace hrs {
 namespace {
 
-constexpr int kWaves = 4;        // waves per block
+constexpr int kLanesPerRow = 16; // lanes sharing one row of S
 constexpr int kWindow = 32;      // positions staged in LDS at a time
 
 struct GdnArgs {
@@ -56,14 +65,16 @@ struct GdnArgs {
   int32_t d_v;
   int32_t group;   // Hv / Hk
   int32_t req0;    // first request of this launch
+  int32_t n_units; // row units of this launch: (d_v / rows per unit) * Hv * requests
   float q_scale;
   int8_t parent[kGeomBytes];  // tree mode: [requests of this launch][n_pos]
 };
 
-template <int DK, int LPR, typename TIn, bool TREE, bool CAPTURE>
-__global__ __launch_bounds__(kWaves * 64) void gdn_span_kernel(const GdnArgs args) {
+template <int DK, int NW, typename TIn, bool TREE, bool CAPTURE>
+__global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
+  constexpr int LPR = kLanesPerRow;
   constexpr int RPW = 64 / LPR;          // rows per wave
-  constexpr int RPB = RPW * kWaves;      // rows per block
+  constexpr int RPB = RPW * NW;          // rows per unit
   constexpr int NCH = DK / (4 * LPR);    // float4 chunks per lane
   static_assert(NCH >= 1 && DK % (4 * LPR) == 0, "lane mapping");
   constexpr int POS_FLOATS = 2 * DK + RPB + 2;
@@ -72,153 +83,170 @@ __global__ __launch_bounds__(kWaves * 64) void gdn_span_kernel(const GdnArgs arg
 
   const int T = args.n_pos;
   const int Hv = args.n_vheads;
+  const int Hk = args.n_kheads;
   const int dv = args.d_v;
-  const int h = blockIdx.y;
-  const int rl = blockIdx.z;                 // request within the launch
-  const int r = args.req0 + rl;
-  const int g = h / args.group;
+  const int nrb = dv / RPB;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int li = lane % LPR;
   const int row_blk = wave * RPW + lane / LPR;
-  const int row0 = blockIdx.x * RPB;
-  const int row = row0 + row_blk;
-
   const size_t head_elems = static_cast<size_t>(dv) * DK;
   const size_t pos_stride = static_cast<size_t>(Hv) * head_elems;   // one position of ckpt
-  float* state_row = args.state + (static_cast<size_t>(r) * Hv + h) * head_elems + static_cast<size_t>(row) * DK;
-  float* ckpt_row0 = nullptr;
-  if (CAPTURE)
-    ckpt_row0 = args.ckpt + static_cast<size_t>(r) * T * pos_stride + static_cast<size_t>(h) * head_elems +
-                static_cast<size_t>(row) * DK;
-  float* out_r = args.out + (static_cast<size_t>(r) * T * Hv + h) * dv + row;
-
-  // This lane's columns: chunk m covers [4 (li + LPR m), +4).
-  f32x4 s[NCH];
-#pragma unroll
-  for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(state_row + 4 * (li + LPR * m));
-
   const TIn* qg = static_cast<const TIn*>(args.q);
   const TIn* kg = static_cast<const TIn*>(args.k);
   const TIn* vg = static_cast<const TIn*>(args.v);
   const TIn* ag = static_cast<const TIn*>(args.a);
   const TIn* bg = static_cast<const TIn*>(args.b);
-  const int Hk = args.n_kheads;
 
-  for (int t0 = 0; t0 < T; t0 += kWindow) {
-    const int tn = min(kWindow, T - t0);
-    __syncthreads();  // the previous window's LDS reads are done
-    // Stage k and q (scaled) of key head g, 8 elements per thread-step.
-    {
-      constexpr int V8 = DK / 8;
-      for (int e = tid; e < tn * V8; e += kWaves * 64) {
-        const int tt = e / V8;
-        const int j = (e % V8) * 8;
-        const size_t src = ((static_cast<size_t>(r) * T + t0 + tt) * Hk + g) * DK + j;
-        float kv[8], qv[8];
-        load8<TIn>(kg + src, kv);
-        load8<TIn>(qg + src, qv);
-        float* lk = lds + tt * POS_FLOATS + j;
-        float* lq = lk + DK;
+  for (int W = blockIdx.x; W < args.n_units; W += gridDim.x) {
+    const int rb = W % nrb;
+    const int h = (W / nrb) % Hv;
+    const int rl = W / (nrb * Hv);           // request within the launch
+    const int r = args.req0 + rl;
+    const int g = h / args.group;
+    const int row0 = rb * RPB;
+    const int row = row0 + row_blk;
+
+    float* state_row = args.state + (static_cast<size_t>(r) * Hv + h) * head_elems + static_cast<size_t>(row) * DK;
+    float* ckpt_row0 = nullptr;
+    if (CAPTURE)
+      ckpt_row0 = args.ckpt + static_cast<size_t>(r) * T * pos_stride + static_cast<size_t>(h) * head_elems +
+                  static_cast<size_t>(row) * DK;
+    float* out_r = args.out + (static_cast<size_t>(r) * T * Hv + h) * dv + row;
+
+    // This lane's columns: chunk m covers [4 (li + LPR m), +4).
+    f32x4 s[NCH];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          lk[i] = kv[i];
-          lq[i] = qv[i] * args.q_scale;
+    for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(state_row + 4 * (li + LPR * m));
+
+    for (int t0 = 0; t0 < T; t0 += kWindow) {
+      const int tn = min(kWindow, T - t0);
+      __syncthreads();  // LDS reads of the previous window (or unit) are done
+      // Stage k and q (scaled) of key head g, 8 elements per thread-step.
+      {
+        constexpr int V8 = DK / 8;
+        for (int e = tid; e < tn * V8; e += NW * 64) {
+          const int tt = e / V8;
+          const int j = (e % V8) * 8;
+          const size_t src = ((static_cast<size_t>(r) * T + t0 + tt) * Hk + g) * DK + j;
+          float kv[8], qv[8];
+          load8<TIn>(kg + src, kv);
+          load8<TIn>(qg + src, qv);
+          float* lk = lds + tt * POS_FLOATS + j;
+          float* lq = lk + DK;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            lk[i] = kv[i];
+            lq[i] = qv[i] * args.q_scale;
+          }
+        }
+        for (int e = tid; e < tn * RPB; e += NW * 64) {
+          const int tt = e / RPB;
+          const int i = e % RPB;
+          const size_t src = ((static_cast<size_t>(r) * T + t0 + tt) * Hv + h) * dv + row0 + i;
+          lds[tt * POS_FLOATS + 2 * DK + i] = load_elem<TIn>(vg, src);
+        }
+        for (int e = tid; e < tn; e += NW * 64) {
+          const size_t src = (static_cast<size_t>(r) * T + t0 + e) * Hv + h;
+          lds[e * POS_FLOATS + 2 * DK + RPB] = load_elem<TIn>(ag, src);
+          lds[e * POS_FLOATS + 2 * DK + RPB + 1] = load_elem<TIn>(bg, src);
         }
       }
-      for (int e = tid; e < tn * RPB; e += kWaves * 64) {
-        const int tt = e / RPB;
-        const int i = e % RPB;
-        const size_t src = ((static_cast<size_t>(r) * T + t0 + tt) * Hv + h) * dv + row0 + i;
-        lds[tt * POS_FLOATS + 2 * DK + i] = load_elem<TIn>(vg, src);
-      }
-      for (int e = tid; e < tn; e += kWaves * 64) {
-        const size_t src = (static_cast<size_t>(r) * T + t0 + e) * Hv + h;
-        lds[e * POS_FLOATS + 2 * DK + RPB] = load_elem<TIn>(ag, src);
-        lds[e * POS_FLOATS + 2 * DK + RPB + 1] = load_elem<TIn>(bg, src);
-      }
-    }
-    __syncthreads();
+      __syncthreads();
 
-    for (int tt = 0; tt < tn; ++tt) {
-      const int t = t0 + tt;
-      if (TREE && t > 0) {
-        const int p = args.parent[rl * T + t];
-        if (p != t - 1) {
-          const float* src = ckpt_row0 + static_cast<size_t>(p) * pos_stride;
+      for (int tt = 0; tt < tn; ++tt) {
+        const int t = t0 + tt;
+        if (TREE && t > 0) {
+          const int p = args.parent[rl * T + t];
+          if (p != t - 1) {
+            const float* src = ckpt_row0 + static_cast<size_t>(p) * pos_stride;
 #pragma unroll
-          for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(src + 4 * (li + LPR * m));
+            for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(src + 4 * (li + LPR * m));
+          }
         }
-      }
-      const float* lp = lds + tt * POS_FLOATS;
-      f32x4 kk[NCH];
+        const float* lp = lds + tt * POS_FLOATS;
+        f32x4 kk[NCH];
 #pragma unroll
-      for (int m = 0; m < NCH; ++m) kk[m] = *reinterpret_cast<const f32x4*>(lp + 4 * (li + LPR * m));
-      float u = 0.0f;
+        for (int m = 0; m < NCH; ++m) kk[m] = *reinterpret_cast<const f32x4*>(lp + 4 * (li + LPR * m));
+        float u = 0.0f;
 #pragma unroll
-      for (int m = 0; m < NCH; ++m) {
-        u = __builtin_fmaf(s[m].x, kk[m].x, u);
-        u = __builtin_fmaf(s[m].y, kk[m].y, u);
-        u = __builtin_fmaf(s[m].z, kk[m].z, u);
-        u = __builtin_fmaf(s[m].w, kk[m].w, u);
-      }
-      u = group_sum<LPR>(u);
-      const float at = lp[2 * DK + RPB];
-      const float bt = lp[2 * DK + RPB + 1];
-      const float vt = lp[2 * DK + row_blk];
-      const float c = bt * __builtin_fmaf(-at, u, vt);
+        for (int m = 0; m < NCH; ++m) {
+          u = __builtin_fmaf(s[m].x, kk[m].x, u);
+          u = __builtin_fmaf(s[m].y, kk[m].y, u);
+          u = __builtin_fmaf(s[m].z, kk[m].z, u);
+          u = __builtin_fmaf(s[m].w, kk[m].w, u);
+        }
+        u = group_sum<LPR>(u);
+        const float at = lp[2 * DK + RPB];
+        const float bt = lp[2 * DK + RPB + 1];
+        const float vt = lp[2 * DK + row_blk];
+        const float c = bt * __builtin_fmaf(-at, u, vt);
 #pragma unroll
-      for (int m = 0; m < NCH; ++m) {
-        s[m].x = __builtin_fmaf(c, kk[m].x, at * s[m].x);
-        s[m].y = __builtin_fmaf(c, kk[m].y, at * s[m].y);
-        s[m].z = __builtin_fmaf(c, kk[m].z, at * s[m].z);
-        s[m].w = __builtin_fmaf(c, kk[m].w, at * s[m].w);
-      }
-      if (CAPTURE) {
-        float* dst = ckpt_row0 + static_cast<size_t>(t) * pos_stride;
+        for (int m = 0; m < NCH; ++m) {
+          s[m].x = __builtin_fmaf(c, kk[m].x, at * s[m].x);
+          s[m].y = __builtin_fmaf(c, kk[m].y, at * s[m].y);
+          s[m].z = __builtin_fmaf(c, kk[m].z, at * s[m].z);
+          s[m].w = __builtin_fmaf(c, kk[m].w, at * s[m].w);
+        }
+        if (CAPTURE) {
+          float* dst = ckpt_row0 + static_cast<size_t>(t) * pos_stride;
 #pragma unroll
-        for (int m = 0; m < NCH; ++m)
-          __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(dst + 4 * (li + LPR * m)));
-      }
-      float o = 0.0f;
+          for (int m = 0; m < NCH; ++m)
+            __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(dst + 4 * (li + LPR * m)));
+        }
+        float o = 0.0f;
 #pragma unroll
-      for (int m = 0; m < NCH; ++m) {
-        const f32x4 qq = *reinterpret_cast<const f32x4*>(lp + DK + 4 * (li + LPR * m));
-        o = __builtin_fmaf(s[m].x, qq.x, o);
-        o = __builtin_fmaf(s[m].y, qq.y, o);
-        o = __builtin_fmaf(s[m].z, qq.z, o);
-        o = __builtin_fmaf(s[m].w, qq.w, o);
+        for (int m = 0; m < NCH; ++m) {
+          const f32x4 qq = *reinterpret_cast<const f32x4*>(lp + DK + 4 * (li + LPR * m));
+          o = __builtin_fmaf(s[m].x, qq.x, o);
+          o = __builtin_fmaf(s[m].y, qq.y, o);
+          o = __builtin_fmaf(s[m].z, qq.z, o);
+          o = __builtin_fmaf(s[m].w, qq.w, o);
+        }
+        o = group_sum<LPR>(o);
+        if (li == 0) out_r[static_cast<size_t>(t) * Hv * dv] = o;
       }
-      o = group_sum<LPR>(o);
-      if (li == 0) out_r[static_cast<size_t>(t) * Hv * dv] = o;
     }
-  }
-  if (!CAPTURE) {
+    if (!CAPTURE) {
 #pragma unroll
-    for (int m = 0; m < NCH; ++m) *reinterpret_cast<f32x4*>(state_row + 4 * (li + LPR * m)) = s[m];
+      for (int m = 0; m < NCH; ++m) *reinterpret_cast<f32x4*>(state_row + 4 * (li + LPR * m)) = s[m];
+    }
   }
 }
 
 // Launch through hipExtLaunchKernelGGL so that optional timing events are
 // recorded by the dispatch itself (no extra stream commands between kernels).
-template <int DK, int LPR, typename TIn, bool TREE, bool CAPTURE>
-hipError_t launch_one(GdnArgs& args, int n_req_launch, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  constexpr int RPB = (64 / LPR) * kWaves;
+template <int DK, int NW, typename TIn, bool TREE, bool CAPTURE>
+hipError_t launch_one(GdnArgs& args, int grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  constexpr int RPB = (64 / kLanesPerRow) * NW;
   const int window = std::min(kWindow, static_cast<int>(args.n_pos));
   const size_t lds = static_cast<size_t>(window) * (2 * DK + RPB + 2) * sizeof(float);
-  dim3 grid(args.d_v / RPB, args.n_vheads, n_req_launch);
-  hipExtLaunchKernelGGL((gdn_span_kernel<DK, LPR, TIn, TREE, CAPTURE>), grid, dim3(kWaves * 64), lds, stream,
+  hipExtLaunchKernelGGL((gdn_span_kernel<DK, NW, TIn, TREE, CAPTURE>), dim3(grid), dim3(NW * 64), lds, stream,
                         start, stop, 0, args);
   return launch_error();
 }
 
+template <int DK, int NW, typename TIn>
+hipError_t launch_mode(GdnArgs& args, bool tree, bool capture, int grid, hipStream_t s, hipEvent_t e0,
+                       hipEvent_t e1) {
+  if (tree) return launch_one<DK, NW, TIn, true, true>(args, grid, s, e0, e1);
+  if (capture) return launch_one<DK, NW, TIn, false, true>(args, grid, s, e0, e1);
+  return launch_one<DK, NW, TIn, false, false>(args, grid, s, e0, e1);
+}
+
+// Launch shape: 32-row units on a one-block-per-CU grid when there are at
+// least as many such units as CUs, else one 4-wave block per 16-row unit.
 template <int DK, typename TIn>
-hipError_t launch_dk(GdnArgs& args, bool tree, bool capture, int n, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  constexpr int LPR = 16;
-  if (tree) return launch_one<DK, LPR, TIn, true, true>(args, n, s, e0, e1);
-  if (capture) return launch_one<DK, LPR, TIn, false, true>(args, n, s, e0, e1);
-  return launch_one<DK, LPR, TIn, false, false>(args, n, s, e0, e1);
+hipError_t launch_dk(GdnArgs& args, int n_req_launch, int n_cu, bool tree, bool capture, hipStream_t s,
+                     hipEvent_t e0, hipEvent_t e1) {
+  const int units32 = (args.d_v % 32 == 0) ? (args.d_v / 32) * args.n_vheads * n_req_launch : 0;
+  if (units32 >= n_cu && n_cu > 0) {
+    args.n_units = units32;
+    return launch_mode<DK, 8, TIn>(args, tree, capture, n_cu, s, e0, e1);
+  }
+  args.n_units = (args.d_v / 16) * args.n_vheads * n_req_launch;
+  return launch_mode<DK, 4, TIn>(args, tree, capture, args.n_units, s, e0, e1);
 }
 
 }  // namespace
@@ -236,7 +264,7 @@ static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, co
   if (d->topo != HRS_CHAIN && d->topo != HRS_TREE) return HRS_EINVAL;
   if (!q || !k || !v || !a || !b || !state || !out) return HRS_EINVAL;
   if (d->topo == HRS_TREE && ckpt == nullptr) return HRS_EINVAL;
-  if (d->n_vheads > 65535 || d->n_req > 65535 * 64) return HRS_EINVAL;
+  if (static_cast<int64_t>(d->d_v) * d->n_vheads > (1 << 20) || d->n_req > (1 << 20)) return HRS_EINVAL;
   const int geo = check_topology(d->topo, d->parent, d->n_req, d->n_pos);
   if (geo != HRS_OK) return geo;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(a) || !aligned16(b) ||
@@ -253,9 +281,13 @@ static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, co
 
   const bool tree = d->topo == HRS_TREE;
   const bool capture = ckpt != nullptr;
-  const int per_launch = tree ? std::max(1, kGeomBytes / d->n_pos) : 65535;
+  const int per_launch = tree ? std::max(1, kGeomBytes / d->n_pos) : 4096;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n_cu = 0;  // falls back to one block per 16-row unit
   for (int r0 = 0; r0 < d->n_req; r0 += per_launch) {
     const int n = std::min(per_launch, d->n_req - r0);
     args.req0 = r0;
@@ -268,11 +300,11 @@ static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, co
     }
     hipError_t e;
     if (d->d_k == 128)
-      e = d->in_dtype == HRS_BF16 ? launch_dk<128, uint16_t>(args, tree, capture, n, s, e0, e1)
-                                  : launch_dk<128, float>(args, tree, capture, n, s, e0, e1);
+      e = d->in_dtype == HRS_BF16 ? launch_dk<128, uint16_t>(args, n, n_cu, tree, capture, s, e0, e1)
+                                  : launch_dk<128, float>(args, n, n_cu, tree, capture, s, e0, e1);
     else
-      e = d->in_dtype == HRS_BF16 ? launch_dk<64, uint16_t>(args, tree, capture, n, s, e0, e1)
-                                  : launch_dk<64, float>(args, tree, capture, n, s, e0, e1);
+      e = d->in_dtype == HRS_BF16 ? launch_dk<64, uint16_t>(args, n, n_cu, tree, capture, s, e0, e1)
+                                  : launch_dk<64, float>(args, n, n_cu, tree, capture, s, e0, e1);
     if (e != hipSuccess) return HRS_EDEVICE;
   }
   return HRS_OK;
