@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default=str(DEFAULT_WORKLOAD))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="launch each step as one captured HIP graph (the same kernels)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before warmup, run a plain device copy of this many MiB three times "
                          "(reference kernel for scaling the FETCH_SIZE/WRITE_SIZE counters)")
@@ -154,12 +156,19 @@ def main():
 
     L, K = w.n_layers, args.steps
     # Timed region 1 (throughput): K whole steps, nothing inserted between kernels.
-    log(f"timing {K} steps")
+    if args.graph:
+        step.capture_graph()
+        for _ in range(args.warmup):
+            step.replay()
+    log(f"timing {K} steps" + (" (graph replay)" if args.graph else ""))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(K):
-        step.launch(stream)
-        step.finish()
+        if args.graph:
+            step.replay()
+        else:
+            step.launch(stream)
+            step.finish()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
@@ -226,7 +235,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded; Qwen3.6-27B-shaped GDN layers, no weights)",
-        "config": {"workload": name, "n_req": R, "n_layers": L, "n_pos": T, "draft_tokens": T - 1,
+        "config": {"workload": name, "launch": "hip graph" if args.graph else "stream", "n_req": R, "n_layers": L, "n_pos": T, "draft_tokens": T - 1,
                    "topology": "tree" if w.tree else "chain", "n_kheads": w.n_kheads, "n_vheads": w.n_vheads,
                    "d_k": w.d_k, "d_v": w.d_v, "inputs": w.dtype, "state": "f32",
                    "conv_channels": w.conv_channels, "conv_width": w.conv_width, "vocab": w.vocab,

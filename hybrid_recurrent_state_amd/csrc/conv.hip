@@ -7,11 +7,13 @@
 // (lucebox PR #533, "feat: DFlash support for tensor-parallel Qwen3.6
 // targets", Changes).
 //
-// MI355X design: in capture mode every (position, 8-channel group) is an
-// independent thread. The host turns the parent array into a table that
+// MI355X design: in capture mode for a chain, one thread takes 8 channels of
+// two consecutive positions and slides the window over five loaded rows
+// (measured 8.5 us versus 10.4 us for one position per thread on 16
+// requests x 8192 channels). For a tree every (position, 8-channel group) is
+// an independent thread: the host turns the parent array into a table that
 // names, for each position and window slot, the x row or conv-state row to
-// read, so chain and tree run the same code and all T positions proceed in
-// parallel (x rows are re-read from L2 by up to W threads). Loads and stores
+// read (x rows are re-read from L2 by up to W threads). Loads and stores
 // are 16 bytes per lane, coalesced along channels. Captured states are raw
 // copies of input bits, so they are exact in any dtype. Without capture
 // (decode, chain only) one thread walks its channels through the positions
@@ -132,6 +134,46 @@ __global__ __launch_bounds__(kThreads) void conv_capture_kernel(const ConvArgs a
   for (int m = 0; m < kBack; ++m) win[m + 1].store(dst + static_cast<size_t>(m) * C);
 }
 
+// Capture mode, chain: one thread per (kChainPos consecutive positions,
+// 8-channel group); the window slides over kChainPos + W - 1 loaded rows.
+constexpr int kChainPos = 2;
+template <typename T>
+__global__ __launch_bounds__(kThreads) void conv_chain_kernel(const ConvArgs args) {
+  const int C = args.channels;
+  const int c0 = (blockIdx.x * kThreads + threadIdx.x) * 8;
+  if (c0 >= C) return;
+  const int T_ = args.n_pos;
+  const int t0 = blockIdx.y * kChainPos;
+  const int tn = min(kChainPos, T_ - t0);
+  const int r = args.req0 + blockIdx.z;
+  const T* x = static_cast<const T*>(args.x);
+  const T* cs = static_cast<const T*>(args.conv_state);
+  T* ck = static_cast<T*>(args.conv_ckpt);
+  // rows[i] is sequence element t0 - kBack + i of [conv_state rows, x rows].
+  Raw8<T> rows[kChainPos + kBack];
+#pragma unroll
+  for (int i = 0; i < kChainPos + kBack; ++i) {
+    const int s = t0 - kBack + i;
+    if (s < 0)
+      rows[i].load(cs + (static_cast<size_t>(r) * kBack + (s + kBack)) * C + c0);
+    else if (s < t0 + tn)
+      rows[i].load(x + (static_cast<size_t>(r) * T_ + s) * C + c0);
+  }
+  float wt[8][kWidth];
+  load_weights<T>(static_cast<const T*>(args.w), c0, wt);
+#pragma unroll
+  for (int j = 0; j < kChainPos; ++j) {
+    if (j < tn) {
+      const int t = t0 + j;
+      const Raw8<T> win[kWidth] = {rows[j], rows[j + 1], rows[j + 2], rows[j + 3]};
+      conv_out<T>(wt, win, args.silu, args.y + (static_cast<size_t>(r) * T_ + t) * C + c0);
+      T* dst = ck + (static_cast<size_t>(r) * T_ + t) * kBack * C + c0;
+#pragma unroll
+      for (int m = 0; m < kBack; ++m) win[m + 1].store(dst + static_cast<size_t>(m) * C);
+    }
+  }
+}
+
 // No capture (chain): one thread per 8-channel group walks the positions.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void conv_inplace_kernel(const ConvArgs args) {
@@ -158,10 +200,13 @@ __global__ __launch_bounds__(kThreads) void conv_inplace_kernel(const ConvArgs a
 }
 
 template <typename T>
-hipError_t launch(ConvArgs& args, bool capture, int n, hipStream_t s) {
+hipError_t launch(ConvArgs& args, bool capture, bool tree, int n, hipStream_t s) {
   const int groups = args.channels / 8;
   dim3 block(kThreads);
-  if (capture) {
+  if (capture && !tree) {
+    dim3 grid((groups + kThreads - 1) / kThreads, (args.n_pos + kChainPos - 1) / kChainPos, n);
+    hipLaunchKernelGGL(conv_chain_kernel<T>, grid, block, 0, s, args);
+  } else if (capture) {
     dim3 grid((groups + kThreads - 1) / kThreads, args.n_pos, n);
     hipLaunchKernelGGL(conv_capture_kernel<T>, grid, block, 0, s, args);
   } else {
@@ -212,8 +257,8 @@ extern "C" int conv1d_verify_span(const hrs_conv_desc* d, const void* x, const v
     if (tree)
       for (int i = 0; i < n; ++i)
         conv_window_sources(d->parent + static_cast<size_t>(r0 + i) * T_, T_, kWidth, args.src + i * table);
-    const hipError_t e = d->dtype == HRS_BF16 ? launch<uint16_t>(args, capture, n, s)
-                                              : launch<float>(args, capture, n, s);
+    const hipError_t e = d->dtype == HRS_BF16 ? launch<uint16_t>(args, capture, tree, n, s)
+                                              : launch<float>(args, capture, tree, n, s);
     if (e != hipSuccess) return HRS_EDEVICE;
   }
   return HRS_OK;

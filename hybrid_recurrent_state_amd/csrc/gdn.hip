@@ -33,9 +33,14 @@
 //    of a position never depends on span length, topology or launch shape.
 //  * k, q (times q_scale), v rows, a and b of a window of positions are
 //    staged once per unit into LDS as f32.
-//  * Tree mode: a node whose parent is not the previous position reloads the
-//    parent's checkpoint rows (this lane's own earlier writes) before its
-//    update; the root starts from `state`.
+//  * Tree mode: the host turns each request's parent array into a stash
+//    schedule. A position with a child that is not the next position keeps
+//    its state in one of 8 register slots (wave-uniform slot index, fully
+//    unrolled, so restores are scalar branches and register moves); a child
+//    restores from that slot instead of re-reading its parent's checkpoint
+//    from memory. Trees that need more than 8 live slots reload the parent's
+//    checkpoint rows (this lane's own earlier writes) for the rest. The root
+//    starts from `state`.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -67,7 +72,11 @@ struct GdnArgs {
   int32_t req0;    // first request of this launch
   int32_t n_units; // row units of this launch: (d_v / rows per unit) * Hv * requests
   float q_scale;
-  int8_t parent[kGeomBytes];  // tree mode: [requests of this launch][n_pos]
+  // Tree mode, each [requests of this launch][n_pos]: parent index, restore
+  // code and save slot (gdn_tree_schedule).
+  int8_t parent[kGeomBytes / 3];
+  int8_t restore[kGeomBytes / 3];
+  int8_t save[kGeomBytes / 3];
 };
 
 template <int DK, int NW, typename TIn, bool TREE, bool CAPTURE>
@@ -117,6 +126,7 @@ __global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
 
     // This lane's columns: chunk m covers [4 (li + LPR m), +4).
     f32x4 s[NCH];
+    f32x4 stash[TREE ? kStashSlots : 1][NCH];
 #pragma unroll
     for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(state_row + 4 * (li + LPR * m));
 
@@ -157,9 +167,17 @@ __global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
 
       for (int tt = 0; tt < tn; ++tt) {
         const int t = t0 + tt;
-        if (TREE && t > 0) {
-          const int p = args.parent[rl * T + t];
-          if (p != t - 1) {
+        if constexpr (TREE) {
+          const int rs = args.restore[rl * T + t];
+          if (rs >= 0) {
+#pragma unroll
+            for (int i = 0; i < kStashSlots; ++i)
+              if (rs == i) {
+#pragma unroll
+                for (int m = 0; m < NCH; ++m) s[m] = stash[i][m];
+              }
+          } else if (rs == kFromGlobal) {
+            const int p = args.parent[rl * T + t];
             const float* src = ckpt_row0 + static_cast<size_t>(p) * pos_stride;
 #pragma unroll
             for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(src + 4 * (li + LPR * m));
@@ -194,6 +212,15 @@ __global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
 #pragma unroll
           for (int m = 0; m < NCH; ++m)
             __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(dst + 4 * (li + LPR * m)));
+        }
+        if constexpr (TREE) {
+          const int sv = args.save[rl * T + t];
+#pragma unroll
+          for (int i = 0; i < kStashSlots; ++i)
+            if (sv == i) {
+#pragma unroll
+              for (int m = 0; m < NCH; ++m) stash[i][m] = s[m];
+            }
         }
         float o = 0.0f;
 #pragma unroll
@@ -281,7 +308,7 @@ static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, co
 
   const bool tree = d->topo == HRS_TREE;
   const bool capture = ckpt != nullptr;
-  const int per_launch = tree ? std::max(1, kGeomBytes / d->n_pos) : 4096;
+  const int per_launch = tree ? std::max(1, (kGeomBytes / 3) / d->n_pos) : 4096;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   int dev = 0, n_cu = 0;
@@ -295,8 +322,12 @@ static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, co
     hipEvent_t e0 = r0 == 0 ? static_cast<hipEvent_t>(start_event) : nullptr;
     hipEvent_t e1 = r0 + n >= d->n_req ? static_cast<hipEvent_t>(stop_event) : nullptr;
     if (tree) {
-      for (int i = 0; i < n * d->n_pos; ++i)
-        args.parent[i] = static_cast<int8_t>(d->parent[static_cast<size_t>(r0) * d->n_pos + i]);
+      const int T_ = d->n_pos;
+      for (int i = 0; i < n * T_; ++i)
+        args.parent[i] = static_cast<int8_t>(d->parent[static_cast<size_t>(r0) * T_ + i]);
+      for (int j = 0; j < n; ++j)
+        gdn_tree_schedule(d->parent + static_cast<size_t>(r0 + j) * T_, T_, args.restore + j * T_,
+                          args.save + j * T_);
     }
     hipError_t e;
     if (d->d_k == 128)

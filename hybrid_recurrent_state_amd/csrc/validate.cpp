@@ -75,6 +75,38 @@ int check_topology(int topo, const int32_t* parent, int32_t n_req, int32_t n_pos
   return HRS_OK;
 }
 
+void gdn_tree_schedule(const int32_t* parent, int32_t n_pos, int8_t* restore, int8_t* save) {
+  std::vector<int32_t> last_child(n_pos, -1);   // last child that is not the next position
+  for (int32_t c = 1; c < n_pos; ++c) {
+    const int32_t p = parent[c];
+    if (c != p + 1) last_child[p] = c;
+  }
+  std::vector<int32_t> slot_of(n_pos, -1);
+  bool busy[kStashSlots] = {false};
+  for (int32_t t = 0; t < n_pos; ++t) {
+    const int32_t p = parent[t];
+    if (t == 0 || p == t - 1) {
+      restore[t] = kFromPrevious;
+    } else if (slot_of[p] >= 0) {
+      restore[t] = static_cast<int8_t>(slot_of[p]);
+      if (last_child[p] == t) busy[slot_of[p]] = false;   // last reader frees the slot
+    } else {
+      restore[t] = kFromGlobal;
+    }
+    save[t] = -1;
+    if (last_child[t] >= 0) {
+      for (int i = 0; i < kStashSlots; ++i) {
+        if (!busy[i]) {
+          busy[i] = true;
+          slot_of[t] = i;
+          save[t] = static_cast<int8_t>(i);
+          break;
+        }
+      }
+    }
+  }
+}
+
 void conv_window_sources(const int32_t* parent, int32_t n_pos, int32_t width, int8_t* out) {
   // The window of position t is the last `width` entries of the sequence
   // [conv_state rows..., x along t's root path]; slot m < width-1 is

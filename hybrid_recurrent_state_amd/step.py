@@ -222,15 +222,45 @@ class VerifyStep:
         self.launch_rollback(h)
         self.launch_ring(h)
 
-    def finish(self):
-        """The step's single host sync: accepted lengths and bonus tokens."""
+    def _gather(self) -> None:
+        """Device-side gather of accepted lengths and bonus tokens into one buffer."""
         b = self.bufs
         R = self.bufs.shape.n_req
         b.dev_result[:R].copy_(b.accept_len)
         b.dev_result[R:].copy_(b.bonus)
+
+    def _host(self):
+        b = self.bufs
+        R = self.bufs.shape.n_req
         b.host_result.copy_(b.dev_result)   # blocking copy into pinned memory
         return b.host_result[:R].numpy().copy(), b.host_result[R:].numpy().copy()
+
+    def finish(self):
+        """The step's single host sync: accepted lengths and bonus tokens."""
+        self._gather()
+        return self._host()
 
     def run(self, stream=None):
         self.launch(stream)
         return self.finish()
+
+    # -- graph launch ---------------------------------------------------------
+    def capture_graph(self) -> None:
+        """Record the whole step (every kernel and the device-side gather of
+        the results) into one HIP graph. Buffers, descriptors and pointers
+        are fixed, so replaying the graph is exactly one step. The graph holds
+        kernel launches and device copies only (no memset nodes)."""
+        import torch
+        self.graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(self.graph, stream=side):
+            self.launch(side)
+            self._gather()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+
+    def replay(self):
+        """One step by graph replay, then the step's single host sync."""
+        self.graph.replay()
+        return self._host()

@@ -103,6 +103,38 @@ def test_gdn_tree_qwen_r2(hrs):
     check_gdn_vs_oracle(units, ck, out, parents=parents, what="tree")
 
 
+TREE_SHAPES = {
+    "comb": [-1] + [0] * 11,                                   # one slot reused by 11 children
+    "binary": [-1, 0, 0, 1, 1, 2, 2, 3, 3, 4, 4, 5, 5],
+    "overflow": [-1] + list(range(10)) + list(range(10)),      # 10 live branch points > 8 stash slots
+    "late-siblings": [-1, 0, 1, 2, 3, 4, 5, 6, 2, 8, 4, 0, 11],
+}
+
+
+@pytest.mark.parametrize("shape", sorted(TREE_SHAPES))
+@pytest.mark.parametrize("n_req", [1, 3])
+def test_gdn_tree_shapes(hrs, shape, n_req):
+    """Stash schedule: slot reuse, slot overflow to checkpoint reloads, late
+    siblings; R=1 uses 16-row units, R=3 the one-block-per-CU grid."""
+    par = np.array(TREE_SHAPES[shape], dtype=np.int32)
+    T = len(par)
+    w = scaled(QWEN_LAYER_CHAIN, n_req=n_req, n_pos=T)
+    units = [gen_unit(w, 0, r) for r in range(n_req)]
+    parents = np.tile(par, (n_req, 1))
+    ck, out, _ = gpu_gdn(hrs, units, parent=parents)
+    check_gdn_vs_oracle(units, ck, out, parents=parents, what=f"tree {shape}")
+
+
+def test_gdn_random_long_trees(hrs):
+    rng = np.random.default_rng(33)
+    for T in (40, 64):
+        par = np.array([-1] + [int(rng.integers(0, i)) for i in range(1, T)], dtype=np.int32)
+        w = scaled(QWEN_LAYER_CHAIN, n_kheads=4, n_vheads=8, n_pos=T)
+        units = [gen_unit(w, 0, 0)]
+        ck, out, _ = gpu_gdn(hrs, units, parent=par[None])
+        check_gdn_vs_oracle(units, ck, out, parents=par[None], what=f"random tree T={T}")
+
+
 def test_gdn_tree_with_chain_parent_equals_chain(hrs):
     w = scaled(QWEN_LAYER_CHAIN, n_req=2)
     units = [gen_unit(w, 0, r) for r in range(2)]
@@ -198,6 +230,8 @@ def gpu_conv(hrs, units, wt, parent=None, capture=True, silu=False, conv_state=N
 
 
 @pytest.mark.parametrize("wl,silu", [(TINY_CHAIN, False), (TINY_CHAIN, True),
+                                     (scaled(QWEN_LAYER_CHAIN, n_req=2, n_pos=6, conv_channels=1024), False),
+                                     (scaled(QWEN_LAYER_CHAIN, n_req=1, n_pos=1, conv_channels=1024), True),
                                      (scaled(QWEN_LAYER_CHAIN, n_req=2), False),
                                      (scaled(QWEN_LAYER_CHAIN, n_req=2), True),
                                      (scaled(QWEN_LAYER_CHAIN, conv_channels=776, n_pos=3), False)])
