@@ -34,13 +34,15 @@
 //  * k, q (times q_scale), v rows, a and b of a window of positions are
 //    staged once per unit into LDS as f32.
 //  * Tree mode: the host turns each request's parent array into a stash
-//    schedule. A position with a child that is not the next position keeps
-//    its state in one of 8 register slots (wave-uniform slot index, fully
-//    unrolled, so restores are scalar branches and register moves); a child
-//    restores from that slot instead of re-reading its parent's checkpoint
-//    from memory. Trees that need more than 8 live slots reload the parent's
-//    checkpoint rows (this lane's own earlier writes) for the rest. The root
-//    starts from `state`.
+//    schedule. A position with a child that is not the next position saves
+//    its state rows into an LDS slot (each lane its own 32 bytes, addressed
+//    by the wave-uniform slot index, so there are no selects and no extra
+//    registers); the child restores from the slot instead of re-reading the
+//    parent's checkpoint. Up to 8 slots, as many as fit beside the staging
+//    buffer. Trees that need more live slots use a kernel variant that
+//    reloads the parent's checkpoint rows (this lane's own earlier writes);
+//    only that variant has a vector-memory load inside the position loop.
+//    The root starts from `state`.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -53,7 +55,22 @@ namespace hrs {
 namespace {
 
 constexpr int kLanesPerRow = 16; // lanes sharing one row of S
+// s_waitcnt immediate for gfx9-family: vmcnt = 0, expcnt and lgkmcnt left at
+// their maxima (no wait).
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kWindow = 32;      // positions staged in LDS at a time
+
+// LDS floats per staged position: k, q (scaled), the unit's v rows, a, b and
+// the tree code, padded to 16 bytes so every position's k and q rows stay
+// aligned for 16-byte LDS reads.
+constexpr int pos_floats(int dk, int rows) { return (2 * dk + rows + 3 + 3) / 4 * 4; }
+
+constexpr size_t staging_bytes(int dk, int rows, int window) {
+  return static_cast<size_t>(window) * pos_floats(dk, rows) * sizeof(float);
+}
+
+// LDS bytes of one tree stash slot: every lane's dk / 16 floats of its row.
+constexpr size_t slot_bytes(int dk, int waves) { return static_cast<size_t>(waves) * 64 * (dk / 16) * sizeof(float); }
 
 struct GdnArgs {
   const void* q;
@@ -71,6 +88,7 @@ struct GdnArgs {
   int32_t group;   // Hv / Hk
   int32_t req0;    // first request of this launch
   int32_t n_units; // row units of this launch: (d_v / rows per unit) * Hv * requests
+  int32_t window;  // positions staged in LDS at a time (min(n_pos, kWindow))
   float q_scale;
   // Tree mode, each [requests of this launch][n_pos]: parent index, restore
   // code and save slot (gdn_tree_schedule).
@@ -79,16 +97,24 @@ struct GdnArgs {
   int8_t save[kGeomBytes / 3];
 };
 
-template <int DK, int NW, typename TIn, bool TREE, bool CAPTURE>
+// TREE: positions follow the launch's stash schedule; RELOAD: some position
+// reloads its parent's checkpoint from memory (trees with more than
+// kStashSlots live branch points). Without RELOAD the position loop holds no
+// vector-memory load at all, so the compiler never has to wait on the
+// in-order vector-memory counter (which the checkpoint stores also occupy).
+template <int DK, int NW, typename TIn, bool TREE, bool RELOAD, bool CAPTURE>
 __global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
   constexpr int LPR = kLanesPerRow;
   constexpr int RPW = 64 / LPR;          // rows per wave
   constexpr int RPB = RPW * NW;          // rows per unit
   constexpr int NCH = DK / (4 * LPR);    // float4 chunks per lane
   static_assert(NCH >= 1 && DK % (4 * LPR) == 0, "lane mapping");
-  constexpr int POS_FLOATS = 2 * DK + RPB + 2;
+  constexpr int POS_FLOATS = pos_floats(DK, RPB);
 
   extern __shared__ float lds[];
+  // Tree stash: [slot][chunk][thread] float4, after the staged positions.
+  f32x4* const stash = reinterpret_cast<f32x4*>(lds + args.window * POS_FLOATS);
+  constexpr int NTHREADS = NW * 64;
 
   const int T = args.n_pos;
   const int Hv = args.n_vheads;
@@ -126,7 +152,6 @@ __global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
 
     // This lane's columns: chunk m covers [4 (li + LPR m), +4).
     f32x4 s[NCH];
-    f32x4 stash[TREE ? kStashSlots : 1][NCH];
 #pragma unroll
     for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(state_row + 4 * (li + LPR * m));
 
@@ -161,29 +186,42 @@ __global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
           const size_t src = (static_cast<size_t>(r) * T + t0 + e) * Hv + h;
           lds[e * POS_FLOATS + 2 * DK + RPB] = load_elem<TIn>(ag, src);
           lds[e * POS_FLOATS + 2 * DK + RPB + 1] = load_elem<TIn>(bg, src);
+          if constexpr (TREE) {
+            // The tree code travels through LDS: reading the kernel-argument
+            // bytes inside the position loop would be a vector load whose wait
+            // also drains every outstanding checkpoint store.
+            const int gi = rl * T + t0 + e;
+            const uint32_t code = static_cast<uint8_t>(args.parent[gi]) |
+                                  (static_cast<uint32_t>(static_cast<uint8_t>(args.restore[gi])) << 8) |
+                                  (static_cast<uint32_t>(static_cast<uint8_t>(args.save[gi])) << 16);
+            lds[e * POS_FLOATS + 2 * DK + RPB + 2] = __uint_as_float(code);
+          }
         }
       }
       __syncthreads();
 
       for (int tt = 0; tt < tn; ++tt) {
         const int t = t0 + tt;
+        const float* lp = lds + tt * POS_FLOATS;
+        int tree_code = 0;
         if constexpr (TREE) {
-          const int rs = args.restore[rl * T + t];
+          tree_code = __builtin_amdgcn_readfirstlane(__float_as_int(lp[2 * DK + RPB + 2]));
+          const int rs = static_cast<int8_t>((tree_code >> 8) & 0xFF);
           if (rs >= 0) {
 #pragma unroll
-            for (int i = 0; i < kStashSlots; ++i)
-              if (rs == i) {
-#pragma unroll
-                for (int m = 0; m < NCH; ++m) s[m] = stash[i][m];
-              }
-          } else if (rs == kFromGlobal) {
-            const int p = args.parent[rl * T + t];
+            for (int m = 0; m < NCH; ++m) s[m] = stash[(rs * NCH + m) * NTHREADS + tid];
+          } else if (RELOAD && rs == kFromGlobal) {
+            const int p = static_cast<int8_t>(tree_code & 0xFF);
             const float* src = ckpt_row0 + static_cast<size_t>(p) * pos_stride;
 #pragma unroll
             for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(src + 4 * (li + LPR * m));
+            // Wait here, inside the rare reload branch: otherwise the compiler
+            // waits at every later use of s on every position, and since the
+            // vector-memory counter retires in order, each such wait would also
+            // drain all outstanding checkpoint stores.
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
           }
         }
-        const float* lp = lds + tt * POS_FLOATS;
         f32x4 kk[NCH];
 #pragma unroll
         for (int m = 0; m < NCH; ++m) kk[m] = *reinterpret_cast<const f32x4*>(lp + 4 * (li + LPR * m));
@@ -214,13 +252,11 @@ __global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
             __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(dst + 4 * (li + LPR * m)));
         }
         if constexpr (TREE) {
-          const int sv = args.save[rl * T + t];
+          const int sv = static_cast<int8_t>((tree_code >> 16) & 0xFF);
+          if (sv >= 0) {
 #pragma unroll
-          for (int i = 0; i < kStashSlots; ++i)
-            if (sv == i) {
-#pragma unroll
-              for (int m = 0; m < NCH; ++m) stash[i][m] = s[m];
-            }
+            for (int m = 0; m < NCH; ++m) stash[(sv * NCH + m) * NTHREADS + tid] = s[m];
+          }
         }
         float o = 0.0f;
 #pragma unroll
@@ -244,36 +280,47 @@ __global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
 
 // Launch through hipExtLaunchKernelGGL so that optional timing events are
 // recorded by the dispatch itself (no extra stream commands between kernels).
-template <int DK, int NW, typename TIn, bool TREE, bool CAPTURE>
-hipError_t launch_one(GdnArgs& args, int grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+template <int DK, int NW, typename TIn, bool TREE, bool RELOAD, bool CAPTURE>
+hipError_t launch_one(GdnArgs& args, int grid, int n_slots, hipStream_t stream, hipEvent_t start,
+                      hipEvent_t stop) {
   constexpr int RPB = (64 / kLanesPerRow) * NW;
-  const int window = std::min(kWindow, static_cast<int>(args.n_pos));
-  const size_t lds = static_cast<size_t>(window) * (2 * DK + RPB + 2) * sizeof(float);
-  hipExtLaunchKernelGGL((gdn_span_kernel<DK, NW, TIn, TREE, CAPTURE>), dim3(grid), dim3(NW * 64), lds, stream,
-                        start, stop, 0, args);
+  const size_t lds = staging_bytes(DK, RPB, args.window) + (TREE ? n_slots * slot_bytes(DK, NW) : 0);
+  hipExtLaunchKernelGGL((gdn_span_kernel<DK, NW, TIn, TREE, RELOAD, CAPTURE>), dim3(grid), dim3(NW * 64), lds,
+                        stream, start, stop, 0, args);
   return launch_error();
 }
 
+enum class Mode { kChainNoCapture, kChain, kTree, kTreeReload };
+
 template <int DK, int NW, typename TIn>
-hipError_t launch_mode(GdnArgs& args, bool tree, bool capture, int grid, hipStream_t s, hipEvent_t e0,
+hipError_t launch_mode(GdnArgs& args, Mode mode, int grid, int n_slots, hipStream_t s, hipEvent_t e0,
                        hipEvent_t e1) {
-  if (tree) return launch_one<DK, NW, TIn, true, true>(args, grid, s, e0, e1);
-  if (capture) return launch_one<DK, NW, TIn, false, true>(args, grid, s, e0, e1);
-  return launch_one<DK, NW, TIn, false, false>(args, grid, s, e0, e1);
+  switch (mode) {
+    case Mode::kTreeReload: return launch_one<DK, NW, TIn, true, true, true>(args, grid, n_slots, s, e0, e1);
+    case Mode::kTree: return launch_one<DK, NW, TIn, true, false, true>(args, grid, n_slots, s, e0, e1);
+    case Mode::kChain: return launch_one<DK, NW, TIn, false, false, true>(args, grid, 0, s, e0, e1);
+    default: return launch_one<DK, NW, TIn, false, false, false>(args, grid, 0, s, e0, e1);
+  }
 }
 
 // Launch shape: 32-row units on a one-block-per-CU grid when there are at
 // least as many such units as CUs, else one 4-wave block per 16-row unit.
+// Launch shape: 32-row units on a one-block-per-CU grid when there are at
+// least as many such units as CUs, else one 4-wave block per 16-row unit.
+int waves_for(int d_v, int n_vheads, int n_req_launch, int n_cu) {
+  const int units32 = (d_v % 32 == 0) ? (d_v / 32) * n_vheads * n_req_launch : 0;
+  return (units32 >= n_cu && n_cu > 0) ? 8 : 4;
+}
+
 template <int DK, typename TIn>
-hipError_t launch_dk(GdnArgs& args, int n_req_launch, int n_cu, bool tree, bool capture, hipStream_t s,
-                     hipEvent_t e0, hipEvent_t e1) {
-  const int units32 = (args.d_v % 32 == 0) ? (args.d_v / 32) * args.n_vheads * n_req_launch : 0;
-  if (units32 >= n_cu && n_cu > 0) {
-    args.n_units = units32;
-    return launch_mode<DK, 8, TIn>(args, tree, capture, n_cu, s, e0, e1);
+hipError_t launch_dk(GdnArgs& args, int n_req_launch, int n_cu, int waves, Mode mode, int n_slots,
+                     hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (waves == 8) {
+    args.n_units = (args.d_v / 32) * args.n_vheads * n_req_launch;
+    return launch_mode<DK, 8, TIn>(args, mode, n_cu, n_slots, s, e0, e1);
   }
   args.n_units = (args.d_v / 16) * args.n_vheads * n_req_launch;
-  return launch_mode<DK, 4, TIn>(args, tree, capture, args.n_units, s, e0, e1);
+  return launch_mode<DK, 4, TIn>(args, mode, args.n_units, n_slots, s, e0, e1);
 }
 
 }  // namespace
@@ -311,31 +358,47 @@ static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, co
   const int per_launch = tree ? std::max(1, (kGeomBytes / 3) / d->n_pos) : 4096;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  int dev = 0, n_cu = 0;
+  int dev = 0, n_cu = 0, max_lds = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     n_cu = 0;  // falls back to one block per 16-row unit
+  if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    max_lds = 64 * 1024;
+  args.window = std::min(kWindow, static_cast<int>(d->n_pos));
   for (int r0 = 0; r0 < d->n_req; r0 += per_launch) {
     const int n = std::min(per_launch, d->n_req - r0);
     args.req0 = r0;
     // The first launch records the start event, the last one the stop event.
     hipEvent_t e0 = r0 == 0 ? static_cast<hipEvent_t>(start_event) : nullptr;
     hipEvent_t e1 = r0 + n >= d->n_req ? static_cast<hipEvent_t>(stop_event) : nullptr;
+    Mode mode = capture ? Mode::kChain : Mode::kChainNoCapture;
+    const int waves = waves_for(d->d_v, d->n_vheads, n, n_cu);
+    int n_slots = 0;
     if (tree) {
       const int T_ = d->n_pos;
+      // Stash slots that fit in LDS beside the staging buffer.
+      const size_t stage = staging_bytes(d->d_k, 4 * waves, args.window);
+      const size_t per_slot = slot_bytes(d->d_k, waves);
+      const size_t room = static_cast<size_t>(max_lds) > stage ? static_cast<size_t>(max_lds) - stage : 0;
+      const int fit = static_cast<int>(std::min<size_t>(kStashSlots, room / per_slot));
       for (int i = 0; i < n * T_; ++i)
         args.parent[i] = static_cast<int8_t>(d->parent[static_cast<size_t>(r0) * T_ + i]);
       for (int j = 0; j < n; ++j)
-        gdn_tree_schedule(d->parent + static_cast<size_t>(r0 + j) * T_, T_, args.restore + j * T_,
+        gdn_tree_schedule(d->parent + static_cast<size_t>(r0 + j) * T_, T_, fit, args.restore + j * T_,
                           args.save + j * T_);
+      mode = Mode::kTree;
+      for (int i = 0; i < n * T_; ++i) {
+        if (args.restore[i] == kFromGlobal) mode = Mode::kTreeReload;
+        if (args.save[i] >= n_slots) n_slots = args.save[i] + 1;
+      }
     }
     hipError_t e;
     if (d->d_k == 128)
-      e = d->in_dtype == HRS_BF16 ? launch_dk<128, uint16_t>(args, n, n_cu, tree, capture, s, e0, e1)
-                                  : launch_dk<128, float>(args, n, n_cu, tree, capture, s, e0, e1);
+      e = d->in_dtype == HRS_BF16 ? launch_dk<128, uint16_t>(args, n, n_cu, waves, mode, n_slots, s, e0, e1)
+                                  : launch_dk<128, float>(args, n, n_cu, waves, mode, n_slots, s, e0, e1);
     else
-      e = d->in_dtype == HRS_BF16 ? launch_dk<64, uint16_t>(args, n, n_cu, tree, capture, s, e0, e1)
-                                  : launch_dk<64, float>(args, n, n_cu, tree, capture, s, e0, e1);
+      e = d->in_dtype == HRS_BF16 ? launch_dk<64, uint16_t>(args, n, n_cu, waves, mode, n_slots, s, e0, e1)
+                                  : launch_dk<64, float>(args, n, n_cu, waves, mode, n_slots, s, e0, e1);
     if (e != hipSuccess) return HRS_EDEVICE;
   }
   return HRS_OK;

@@ -19,7 +19,7 @@ constexpr int kGeomBytes = 3072;
 // state comes from and whether its result must be kept for later children.
 constexpr int8_t kFromPrevious = -1;  // restore: continue from position t-1
 constexpr int8_t kFromGlobal = -2;    // restore: reload checkpoint of parent[t]
-constexpr int kStashSlots = 8;        // register slots for branch-point states
+constexpr int kStashSlots = 8;        // most stash slots a schedule uses
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -36,13 +36,13 @@ int check_topology(int topo, const int32_t* parent, int32_t n_req, int32_t n_pos
 void set_last_hip_error(int err);
 
 // Stash schedule of one request's tree (parent[0] == -1, parent[t] < t).
-// restore[t]: kFromPrevious, kFromGlobal, or a slot in [0, kStashSlots) that
-// holds parent[t]'s state. save[t]: a slot to store position t's state in
+// restore[t]: kFromPrevious, kFromGlobal, or a slot in [0, n_slots) that
+// holds parent[t]'s state (n_slots <= kStashSlots). save[t]: a slot to store position t's state in
 // after computing it, or -1. A position's state is stashed when one of its
 // children is not the next position; slots are assigned greedily (lowest free
 // slot, freed after the last child reads it); when no slot is free the
 // children reload the parent's checkpoint from memory.
-void gdn_tree_schedule(const int32_t* parent, int32_t n_pos, int8_t* restore, int8_t* save);
+void gdn_tree_schedule(const int32_t* parent, int32_t n_pos, int n_slots, int8_t* restore, int8_t* save);
 
 // Conv window sources of every position of one request: for window slot m
 // (0 = oldest, W-2 = the slot before the current input) the x row to read

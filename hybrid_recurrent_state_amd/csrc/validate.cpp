@@ -75,7 +75,8 @@ int check_topology(int topo, const int32_t* parent, int32_t n_req, int32_t n_pos
   return HRS_OK;
 }
 
-void gdn_tree_schedule(const int32_t* parent, int32_t n_pos, int8_t* restore, int8_t* save) {
+void gdn_tree_schedule(const int32_t* parent, int32_t n_pos, int n_slots, int8_t* restore, int8_t* save) {
+  if (n_slots > kStashSlots) n_slots = kStashSlots;
   std::vector<int32_t> last_child(n_pos, -1);   // last child that is not the next position
   for (int32_t c = 1; c < n_pos; ++c) {
     const int32_t p = parent[c];
@@ -95,7 +96,7 @@ void gdn_tree_schedule(const int32_t* parent, int32_t n_pos, int8_t* restore, in
     }
     save[t] = -1;
     if (last_child[t] >= 0) {
-      for (int i = 0; i < kStashSlots; ++i) {
+      for (int i = 0; i < n_slots; ++i) {
         if (!busy[i]) {
           busy[i] = true;
           slot_of[t] = i;

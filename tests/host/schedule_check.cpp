@@ -15,10 +15,10 @@
 
 using namespace hrs;
 
-static int check_schedule(const std::vector<int32_t>& parent, int* used_global) {
+static int check_schedule(const std::vector<int32_t>& parent, int n_slots, int* used_global) {
   const int T = static_cast<int>(parent.size());
   std::vector<int8_t> restore(T), save(T);
-  gdn_tree_schedule(parent.data(), T, restore.data(), save.data());
+  gdn_tree_schedule(parent.data(), T, n_slots, restore.data(), save.data());
   int cur = -1;
   int slot[kStashSlots];
   for (int i = 0; i < kStashSlots; ++i) slot[i] = -100;
@@ -26,13 +26,13 @@ static int check_schedule(const std::vector<int32_t>& parent, int* used_global) 
     int src;
     if (restore[t] == kFromPrevious) src = cur;
     else if (restore[t] == kFromGlobal) { src = parent[t]; ++*used_global; }
-    else if (restore[t] >= 0 && restore[t] < kStashSlots) src = slot[restore[t]];
+    else if (restore[t] >= 0 && restore[t] < n_slots) src = slot[restore[t]];
     else { std::printf("bad restore code %d at %d\n", restore[t], t); return 1; }
     const int want = t == 0 ? -1 : parent[t];
     if (src != want) { std::printf("position %d starts from %d, parent is %d\n", t, src, want); return 1; }
     cur = t;
     if (save[t] >= 0) {
-      if (save[t] >= kStashSlots) { std::printf("bad save slot\n"); return 1; }
+      if (save[t] >= n_slots) { std::printf("bad save slot\n"); return 1; }
       slot[save[t]] = t;
     }
   }
@@ -80,7 +80,11 @@ int main() {
   int global = 0, overflow_case = 0;
   for (size_t c = 0; c < cases.size(); ++c) {
     int g = 0;
-    if (check_schedule(cases[c], &g)) { std::printf("schedule case %zu failed\n", c); return 1; }
+    for (int ns = 0; ns <= kStashSlots; ++ns) {
+      int g0 = 0;
+      if (check_schedule(cases[c], ns, &g0)) { std::printf("schedule case %zu slots %d failed\n", c, ns); return 1; }
+      if (ns == kStashSlots) g = g0;
+    }
     if (check_window(cases[c], false)) { std::printf("window case %zu failed\n", c); return 1; }
     if (c == 4) overflow_case = g;
     global += g;
