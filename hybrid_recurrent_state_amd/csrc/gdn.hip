@@ -60,13 +60,18 @@ constexpr int kLanesPerRow = 16; // lanes sharing one row of S
 constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kWindow = 32;      // positions staged in LDS at a time
 
-// LDS floats per staged position: k, q (scaled), the unit's v rows, a, b and
-// the tree code, padded to 16 bytes so every position's k and q rows stay
-// aligned for 16-byte LDS reads.
-constexpr int pos_floats(int dk, int rows) { return (2 * dk + rows + 3 + 3) / 4 * 4; }
+// LDS floats per staged position: k, q (scaled), the unit's v rows, a, b and,
+// for trees, the tree code. Chain spans use the unpadded stride, so every
+// other position's k and q rows are 8-byte aligned and are read with 16-byte
+// LDS reads that the hardware splits; a 16-byte-aligned stride (and a layout
+// with separate k, q and v arrays) measured 3% and 7% slower on the
+// 16-request Qwen shape. Tree spans need the extra code word and pad to 16 bytes.
+constexpr int pos_floats(int dk, int rows, bool tree) {
+  return tree ? (2 * dk + rows + 3 + 3) / 4 * 4 : 2 * dk + rows + 2;
+}
 
-constexpr size_t staging_bytes(int dk, int rows, int window) {
-  return static_cast<size_t>(window) * pos_floats(dk, rows) * sizeof(float);
+constexpr size_t staging_bytes(int dk, int rows, int window, bool tree) {
+  return static_cast<size_t>(window) * pos_floats(dk, rows, tree) * sizeof(float);
 }
 
 // LDS bytes of one tree stash slot: every lane's dk / 16 floats of its row.
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
   constexpr int RPB = RPW * NW;          // rows per unit
   constexpr int NCH = DK / (4 * LPR);    // float4 chunks per lane
   static_assert(NCH >= 1 && DK % (4 * LPR) == 0, "lane mapping");
-  constexpr int POS_FLOATS = pos_floats(DK, RPB);
+  constexpr int POS_FLOATS = pos_floats(DK, RPB, TREE);
 
   extern __shared__ float lds[];
   // Tree stash: [slot][chunk][thread] float4, after the staged positions.
@@ -284,7 +289,7 @@ template <int DK, int NW, typename TIn, bool TREE, bool RELOAD, bool CAPTURE>
 hipError_t launch_one(GdnArgs& args, int grid, int n_slots, hipStream_t stream, hipEvent_t start,
                       hipEvent_t stop) {
   constexpr int RPB = (64 / kLanesPerRow) * NW;
-  const size_t lds = staging_bytes(DK, RPB, args.window) + (TREE ? n_slots * slot_bytes(DK, NW) : 0);
+  const size_t lds = staging_bytes(DK, RPB, args.window, TREE) + (TREE ? n_slots * slot_bytes(DK, NW) : 0);
   hipExtLaunchKernelGGL((gdn_span_kernel<DK, NW, TIn, TREE, RELOAD, CAPTURE>), dim3(grid), dim3(NW * 64), lds,
                         stream, start, stop, 0, args);
   return launch_error();
@@ -377,7 +382,7 @@ static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, co
     if (tree) {
       const int T_ = d->n_pos;
       // Stash slots that fit in LDS beside the staging buffer.
-      const size_t stage = staging_bytes(d->d_k, 4 * waves, args.window);
+      const size_t stage = staging_bytes(d->d_k, 4 * waves, args.window, true);
       const size_t per_slot = slot_bytes(d->d_k, waves);
       const size_t room = static_cast<size_t>(max_lds) > stage ? static_cast<size_t>(max_lds) - stage : 0;
       const int fit = static_cast<int>(std::min<size_t>(kStashSlots, room / per_slot));
