@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--workload", default=str(DEFAULT_WORKLOAD))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true", help="skip the measured NEXT-row variants")
     ap.add_argument("--graph", action="store_true",
                     help="launch each step as one captured HIP graph (the same kernels)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -217,6 +218,44 @@ def main():
     log(f"step {ms_per_step:.3f} ms (with GDN events {(t3 - t2) * 1e3 / K:.3f} ms); gdn launch avg "
         f"{gdn_avg_s * 1e6:.1f} us = {achieved:.0f} GB/s; traffic {traffic}; phases {phases}")
 
+    next_rows = None
+    if not args.no_next:
+        next_rows = {}
+        # f3: the same step captured once and launched as one HIP graph.
+        if not args.graph:
+            step.capture_graph()
+            for _ in range(args.warmup):
+                step.replay()
+            torch.cuda.synchronize()
+            g0 = time.perf_counter()
+            for _ in range(K):
+                step.replay()
+            torch.cuda.synchronize()
+            ms_g = (time.perf_counter() - g0) * 1e3 / K
+            next_rows["f3_hip_graph_step"] = {"ms_per_step": ms_g, "value": R * T * L / (ms_g / 1e3),
+                                              "vs_stream_launch": ms_per_step / ms_g}
+            log(f"f3 graph step {ms_g:.3f} ms")
+        # f2: zero-copy rollback + compact conv state (same kernels for the spans,
+        # nothing copied to roll back; a second checkpoint buffer alternates).
+        if w.vocab:
+            from hybrid_recurrent_state_amd.step import ZeroCopyVerifyStep
+            zc = ZeroCopyVerifyStep(bufs, parent=loaded.parent, runs=loaded.runs)
+            for _ in range(args.warmup):
+                zc.run(stream)
+            torch.cuda.synchronize()
+            z0 = time.perf_counter()
+            for _ in range(K):
+                zc.launch(stream)
+                zc.finish()
+            torch.cuda.synchronize()
+            ms_z = (time.perf_counter() - z0) * 1e3 / K
+            next_rows["f2_zero_copy_rollback_step"] = {"ms_per_step": ms_z, "value": R * T * L / (ms_z / 1e3),
+                                                       "vs_copy_rollback": ms_per_step / ms_z}
+            log(f"f2 zero-copy step {ms_z:.3f} ms")
+            del zc
+            bufs.ckpt2 = None
+            torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
@@ -246,6 +285,7 @@ def main():
                      "avg_launch_us": gdn_avg_s * 1e6},
         "gdn_tokens_per_s_per_layer": R * T / gdn_avg_s,
         "phases_ms": phases,
+        "next_rows": next_rows,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -59,6 +59,15 @@ class AcceptDesc(ctypes.Structure):
                 ("topo", _i32), ("parent", ctypes.POINTER(_i32))]
 
 
+class SpanSource(ctypes.Structure):
+    _fields_ = [("ckpt", _p), ("node", _p), ("n_pos", _i32)]
+
+
+class ConvAdvanceDesc(ctypes.Structure):
+    _fields_ = [("n_layers", _i32), ("n_req", _i32), ("n_pos", _i32), ("channels", _i32), ("width", _i32),
+                ("dtype", _i32)]
+
+
 class RollbackDesc(ctypes.Structure):
     _fields_ = [("n_layers", _i32), ("n_req", _i32), ("n_pos", _i32), ("n_vheads", _i32),
                 ("d_k", _i32), ("d_v", _i32), ("conv_channels", _i32), ("conv_width", _i32),
@@ -79,6 +88,10 @@ _SIGNATURES = {
     "hrs_validate_tree": (_i32, [ctypes.POINTER(_i32), _i32, _i32, ctypes.POINTER(_i32)]),
     "gdn_verify_span": (_i32, [ctypes.POINTER(GdnDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "gdn_verify_span_timed": (_i32, [ctypes.POINTER(GdnDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "gdn_verify_span_from": (_i32, [ctypes.POINTER(GdnDesc), ctypes.POINTER(SpanSource), _p, _p, _p, _p, _p, _p,
+                                    _p, _p, _p]),
+    "conv1d_verify_span_nocapture": (_i32, [ctypes.POINTER(ConvDesc), _p, _p, _p, _p, _p]),
+    "conv_state_advance": (_i32, [ctypes.POINTER(ConvAdvanceDesc), _p, _p, _p, _p, _p, _p]),
     "conv1d_verify_span": (_i32, [ctypes.POINTER(ConvDesc), _p, _p, _p, _p, _p, _p]),
     "accept_greedy_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AcceptDesc)]),
     "accept_greedy": (_i32, [ctypes.POINTER(AcceptDesc), _p, _p, _p, _p, _p, _p, _p, _p,
@@ -228,6 +241,42 @@ def gdn_verify_span(q, k, v, a, b, state, ckpt, out, parent=None, q_scale: float
     else:
         st = lib.gdn_verify_span_timed(*args, event_handle(events[0]), event_handle(events[1]))
     _check(st, "gdn_verify_span")
+
+
+def gdn_verify_span_from(src_ckpt, src_node, q, k, v, a, b, ckpt, out, parent=None, status=None,
+                         q_scale: float = 1.0, stream=None):
+    """Zero-copy rollback: like gdn_verify_span, but request r starts from
+    src_ckpt[r][src_node[r]] (src_ckpt [R,Tp,Hv,dv,dk] f32, src_node [R] int32,
+    both on the device) instead of a state buffer."""
+    R, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    par, par_p = _parent_array(parent, R, T)
+    d = GdnDesc(R, T, Hk, Hv, dk, dv, _dtype_code(q), float(q_scale),
+                HRS_TREE if parent is not None else HRS_CHAIN, par_p)
+    src = SpanSource(_ptr(src_ckpt), _ptr(src_node), src_ckpt.shape[1])
+    st = lib.gdn_verify_span_from(ctypes.byref(d), ctypes.byref(src), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                  _ptr(ckpt), _ptr(out), _ptr(status), _stream(stream))
+    _check(st, "gdn_verify_span_from")
+
+
+def conv1d_verify_span_nocapture(x, w, conv_state, y, parent=None, silu: bool = False, stream=None):
+    """conv output y only; conv_state [R,W-1,C] is read only."""
+    R, T, C = x.shape
+    W = w.shape[1]
+    par, par_p = _parent_array(parent, R, T)
+    d = ConvDesc(R, T, C, W, _dtype_code(x), int(bool(silu)), HRS_TREE if parent is not None else HRS_CHAIN, par_p)
+    st = lib.conv1d_verify_span_nocapture(ctypes.byref(d), _ptr(x), _ptr(w), _ptr(conv_state), _ptr(y),
+                                          _stream(stream))
+    _check(st, "conv1d_verify_span_nocapture")
+
+
+def conv_state_advance(x, conv_state, path, accept_len, status=None, stream=None):
+    """x [L,R,T,C]; conv_state [L,R,W-1,C]; path [R,T], accept_len [R] int32 (device)."""
+    L, R, T, C = x.shape
+    d = ConvAdvanceDesc(L, R, T, C, conv_state.shape[2] + 1, _dtype_code(x))
+    st = lib.conv_state_advance(ctypes.byref(d), _ptr(x), _ptr(conv_state), _ptr(path), _ptr(accept_len),
+                                _ptr(status), _stream(stream))
+    _check(st, "conv_state_advance")
 
 
 def conv1d_verify_span(x, w, conv_state, conv_ckpt, y, parent=None, silu: bool = False, stream=None):

@@ -101,7 +101,7 @@ __device__ __forceinline__ void conv_out(const float (&wt)[8][kWidth], const Raw
 }
 
 // Capture mode: one thread per (position, 8-channel group).
-template <typename T>
+template <typename T, bool STORE>
 __global__ __launch_bounds__(kThreads) void conv_capture_kernel(const ConvArgs args) {
   const int C = args.channels;
   const int c0 = (blockIdx.x * kThreads + threadIdx.x) * 8;
@@ -129,15 +129,17 @@ __global__ __launch_bounds__(kThreads) void conv_capture_kernel(const ConvArgs a
   load_weights<T>(static_cast<const T*>(args.w), c0, wt);
 
   conv_out<T>(wt, win, args.silu, args.y + (static_cast<size_t>(r) * T_ + t) * C + c0);
-  T* dst = ck + (static_cast<size_t>(r) * T_ + t) * kBack * C + c0;
+  if (STORE) {
+    T* dst = ck + (static_cast<size_t>(r) * T_ + t) * kBack * C + c0;
 #pragma unroll
-  for (int m = 0; m < kBack; ++m) win[m + 1].store(dst + static_cast<size_t>(m) * C);
+    for (int m = 0; m < kBack; ++m) win[m + 1].store(dst + static_cast<size_t>(m) * C);
+  }
 }
 
 // Capture mode, chain: one thread per (kChainPos consecutive positions,
 // 8-channel group); the window slides over kChainPos + W - 1 loaded rows.
 constexpr int kChainPos = 2;
-template <typename T>
+template <typename T, bool STORE>
 __global__ __launch_bounds__(kThreads) void conv_chain_kernel(const ConvArgs args) {
   const int C = args.channels;
   const int c0 = (blockIdx.x * kThreads + threadIdx.x) * 8;
@@ -167,9 +169,11 @@ __global__ __launch_bounds__(kThreads) void conv_chain_kernel(const ConvArgs arg
       const int t = t0 + j;
       const Raw8<T> win[kWidth] = {rows[j], rows[j + 1], rows[j + 2], rows[j + 3]};
       conv_out<T>(wt, win, args.silu, args.y + (static_cast<size_t>(r) * T_ + t) * C + c0);
-      T* dst = ck + (static_cast<size_t>(r) * T_ + t) * kBack * C + c0;
+      if (STORE) {
+        T* dst = ck + (static_cast<size_t>(r) * T_ + t) * kBack * C + c0;
 #pragma unroll
-      for (int m = 0; m < kBack; ++m) win[m + 1].store(dst + static_cast<size_t>(m) * C);
+        for (int m = 0; m < kBack; ++m) win[m + 1].store(dst + static_cast<size_t>(m) * C);
+      }
     }
   }
 }
@@ -199,21 +203,98 @@ __global__ __launch_bounds__(kThreads) void conv_inplace_kernel(const ConvArgs a
   for (int m = 0; m < kBack; ++m) win[m].store(cs + (static_cast<size_t>(r) * kBack + m) * C + c0);
 }
 
+// Modes: capture (y and conv checkpoints), y only with a read-only conv
+// state, or in-place decode (chain, conv_state advanced).
+enum class ConvMode { kCapture, kOutputOnly, kInPlace };
+
 template <typename T>
-hipError_t launch(ConvArgs& args, bool capture, bool tree, int n, hipStream_t s) {
+hipError_t launch(ConvArgs& args, ConvMode mode, bool tree, int n, hipStream_t s) {
   const int groups = args.channels / 8;
   dim3 block(kThreads);
-  if (capture && !tree) {
-    dim3 grid((groups + kThreads - 1) / kThreads, (args.n_pos + kChainPos - 1) / kChainPos, n);
-    hipLaunchKernelGGL(conv_chain_kernel<T>, grid, block, 0, s, args);
-  } else if (capture) {
-    dim3 grid((groups + kThreads - 1) / kThreads, args.n_pos, n);
-    hipLaunchKernelGGL(conv_capture_kernel<T>, grid, block, 0, s, args);
+  const unsigned gx = (groups + kThreads - 1) / kThreads;
+  if (mode == ConvMode::kInPlace) {
+    hipLaunchKernelGGL(conv_inplace_kernel<T>, dim3(gx, 1, n), block, 0, s, args);
+  } else if (!tree) {
+    dim3 grid(gx, (args.n_pos + kChainPos - 1) / kChainPos, n);
+    if (mode == ConvMode::kCapture)
+      hipLaunchKernelGGL((conv_chain_kernel<T, true>), grid, block, 0, s, args);
+    else
+      hipLaunchKernelGGL((conv_chain_kernel<T, false>), grid, block, 0, s, args);
   } else {
-    dim3 grid((groups + kThreads - 1) / kThreads, 1, n);
-    hipLaunchKernelGGL(conv_inplace_kernel<T>, grid, block, 0, s, args);
+    dim3 grid(gx, args.n_pos, n);
+    if (mode == ConvMode::kCapture)
+      hipLaunchKernelGGL((conv_capture_kernel<T, true>), grid, block, 0, s, args);
+    else
+      hipLaunchKernelGGL((conv_capture_kernel<T, false>), grid, block, 0, s, args);
   }
   return launch_error();
+}
+
+struct AdvanceArgs {
+  const void* x;
+  void* conv_state;
+  const int32_t* path;
+  const int32_t* accept_len;
+  int32_t* status;
+  int32_t n_req;
+  int32_t n_pos;
+  int32_t channels;
+};
+
+// conv_state[l][r] <- last W-1 rows of [conv_state[l][r], x[l][r][path...]].
+// Grid (channel groups / kThreads, R, L). Each thread loads the rows it needs
+// for its 8 channels before storing any, so the in-place shift of old state
+// rows is safe.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void conv_advance_kernel(const AdvanceArgs args) {
+  const int C = args.channels;
+  const int T_ = args.n_pos;
+  const int r = blockIdx.y;
+  const int l = blockIdx.z;
+  if (args.status != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
+    int32_t bad = 0;
+    for (int i = 0; i < args.n_req; ++i) {
+      const int32_t len = args.accept_len[i];
+      bool ok = len >= 0 && len < T_;
+      for (int j = 0; ok && j <= len; ++j) {
+        const int32_t p = args.path[static_cast<size_t>(i) * T_ + j];
+        ok = p >= 0 && p < T_;
+      }
+      bad += ok ? 0 : 1;
+    }
+    *args.status = bad;
+  }
+  const int c0 = (blockIdx.x * kThreads + threadIdx.x) * 8;
+  if (c0 >= C) return;
+  const int len = args.accept_len[r];
+  if (len < 0 || len >= T_) return;
+  const int n = len + 1;  // positions on the accepted path
+  const int32_t* path = args.path + static_cast<size_t>(r) * T_;
+  const size_t lr = static_cast<size_t>(l) * args.n_req + r;
+  const T* x = static_cast<const T*>(args.x) + lr * T_ * C;
+  T* cs = static_cast<T*>(args.conv_state) + lr * kBack * C;
+  int src[kBack];
+#pragma unroll
+  for (int m = 0; m < kBack; ++m) {
+    const int j = n + m;  // index into [state rows 0..W-2, x rows of the path]
+    if (j < kBack) {
+      src[m] = -1 - j;
+    } else {
+      const int p = path[j - kBack];
+      if (p < 0 || p >= T_) return;
+      src[m] = p;
+    }
+  }
+  Raw8<T> rows[kBack];
+#pragma unroll
+  for (int m = 0; m < kBack; ++m) {
+    if (src[m] >= 0)
+      rows[m].load(x + static_cast<size_t>(src[m]) * C + c0);
+    else
+      rows[m].load(cs + static_cast<size_t>(-1 - src[m]) * C + c0);
+  }
+#pragma unroll
+  for (int m = 0; m < kBack; ++m) rows[m].store(cs + static_cast<size_t>(m) * C + c0);
 }
 
 }  // namespace
@@ -221,14 +302,14 @@ hipError_t launch(ConvArgs& args, bool capture, bool tree, int n, hipStream_t s)
 
 using namespace hrs;
 
-extern "C" int conv1d_verify_span(const hrs_conv_desc* d, const void* x, const void* w, void* conv_state,
-                                  void* conv_ckpt, float* y, void* stream) {
+static int conv_span_impl(const hrs_conv_desc* d, const void* x, const void* w, void* conv_state,
+                          void* conv_ckpt, float* y, void* stream, bool output_only) {
   if (d == nullptr) return HRS_EINVAL;
   if (d->n_req < 1 || d->channels < 8 || d->channels % 8 != 0 || d->width < 2) return HRS_EINVAL;
   if (!dtype_ok(d->dtype)) return HRS_EINVAL;
   if (d->topo != HRS_CHAIN && d->topo != HRS_TREE) return HRS_EINVAL;
   if (!x || !w || !conv_state || !y) return HRS_EINVAL;
-  if (d->topo == HRS_TREE && conv_ckpt == nullptr) return HRS_EINVAL;
+  if (d->topo == HRS_TREE && conv_ckpt == nullptr && !output_only) return HRS_EINVAL;
   if (d->n_req > 65535 * 64) return HRS_EINVAL;
   const int geo = check_topology(d->topo, d->parent, d->n_req, d->n_pos);
   if (geo != HRS_OK) return geo;
@@ -241,7 +322,8 @@ extern "C" int conv1d_verify_span(const hrs_conv_desc* d, const void* x, const v
   args.x = x; args.w = w; args.conv_state = conv_state; args.conv_ckpt = conv_ckpt; args.y = y;
   args.n_pos = d->n_pos; args.channels = d->channels; args.silu = d->silu != 0;
   const bool tree = d->topo == HRS_TREE;
-  const bool capture = conv_ckpt != nullptr;
+  const ConvMode mode = output_only ? ConvMode::kOutputOnly
+                                    : (conv_ckpt != nullptr ? ConvMode::kCapture : ConvMode::kInPlace);
   const int T_ = d->n_pos;
   const int table = T_ * kBack;
   int per_launch = 65535;
@@ -257,9 +339,43 @@ extern "C" int conv1d_verify_span(const hrs_conv_desc* d, const void* x, const v
     if (tree)
       for (int i = 0; i < n; ++i)
         conv_window_sources(d->parent + static_cast<size_t>(r0 + i) * T_, T_, kWidth, args.src + i * table);
-    const hipError_t e = d->dtype == HRS_BF16 ? launch<uint16_t>(args, capture, tree, n, s)
-                                              : launch<float>(args, capture, tree, n, s);
+    const hipError_t e = d->dtype == HRS_BF16 ? launch<uint16_t>(args, mode, tree, n, s)
+                                              : launch<float>(args, mode, tree, n, s);
     if (e != hipSuccess) return HRS_EDEVICE;
   }
   return HRS_OK;
+}
+
+extern "C" int conv1d_verify_span(const hrs_conv_desc* d, const void* x, const void* w, void* conv_state,
+                                  void* conv_ckpt, float* y, void* stream) {
+  return conv_span_impl(d, x, w, conv_state, conv_ckpt, y, stream, false);
+}
+
+extern "C" int conv1d_verify_span_nocapture(const hrs_conv_desc* d, const void* x, const void* w,
+                                            const void* conv_state, float* y, void* stream) {
+  return conv_span_impl(d, x, w, const_cast<void*>(conv_state), nullptr, y, stream, true);
+}
+
+extern "C" int conv_state_advance(const hrs_conv_advance_desc* d, const void* x, void* conv_state,
+                                  const int32_t* path, const int32_t* accept_len, int32_t* status, void* stream) {
+  if (d == nullptr) return HRS_EINVAL;
+  if (d->n_layers < 1 || d->n_req < 1 || d->n_pos < 1 || d->n_pos > HRS_MAX_POS || d->channels < 8 ||
+      d->channels % 8 != 0 || d->width < 2 || !dtype_ok(d->dtype))
+    return HRS_EINVAL;
+  if (!x || !conv_state || !path || !accept_len) return HRS_EINVAL;
+  if (d->n_req > 65535 || d->n_layers > 65535) return HRS_EINVAL;
+  if (!aligned16(x) || !aligned16(conv_state) || !aligned16(path) || !aligned16(accept_len) ||
+      (status && !aligned16(status)))
+    return HRS_EALIGN;
+  if (d->width != kWidth) return HRS_EUNSUPPORTED;
+  AdvanceArgs args;
+  args.x = x; args.conv_state = conv_state; args.path = path; args.accept_len = accept_len; args.status = status;
+  args.n_req = d->n_req; args.n_pos = d->n_pos; args.channels = d->channels;
+  const dim3 grid((d->channels / 8 + kThreads - 1) / kThreads, d->n_req, d->n_layers);
+  (void)hipGetLastError();
+  if (d->dtype == HRS_BF16)
+    hipLaunchKernelGGL(conv_advance_kernel<uint16_t>, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), args);
+  else
+    hipLaunchKernelGGL(conv_advance_kernel<float>, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), args);
+  return launch_error() == hipSuccess ? HRS_OK : HRS_EDEVICE;
 }

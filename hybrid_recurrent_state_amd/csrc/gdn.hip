@@ -95,6 +95,13 @@ struct GdnArgs {
   int32_t n_units; // row units of this launch: (d_v / rows per unit) * Hv * requests
   int32_t window;  // positions staged in LDS at a time (min(n_pos, kWindow))
   float q_scale;
+  // Zero-copy source of the initial state (gdn_verify_span_from): when
+  // src_ckpt is set, request r starts from src_ckpt[r][src_node[r]].
+  const float* src_ckpt;
+  const int32_t* src_node;
+  int32_t src_npos;
+  int32_t n_req_total;
+  int32_t* status;  // optional: number of requests whose src_node is out of range
   // Tree mode, each [requests of this launch][n_pos]: parent index, restore
   // code and save slot (gdn_tree_schedule).
   int8_t parent[kGeomBytes / 3];
@@ -139,6 +146,14 @@ __global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
   const TIn* ag = static_cast<const TIn*>(args.a);
   const TIn* bg = static_cast<const TIn*>(args.b);
 
+  if (args.status != nullptr && args.req0 == 0 && blockIdx.x == 0 && threadIdx.x == 0) {
+    int32_t bad = 0;
+    for (int i = 0; i < args.n_req_total; ++i) {
+      const int32_t u = args.src_node[i];
+      bad += (u < 0 || u >= args.src_npos) ? 1 : 0;
+    }
+    *args.status = bad;
+  }
   for (int W = blockIdx.x; W < args.n_units; W += gridDim.x) {
     const int rb = W % nrb;
     const int h = (W / nrb) % Hv;
@@ -148,7 +163,19 @@ __global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
     const int row0 = rb * RPB;
     const int row = row0 + row_blk;
 
-    float* state_row = args.state + (static_cast<size_t>(r) * Hv + h) * head_elems + static_cast<size_t>(row) * DK;
+    float* state_row =
+        args.state ? args.state + (static_cast<size_t>(r) * Hv + h) * head_elems + static_cast<size_t>(row) * DK
+                   : nullptr;
+    const float* init_row = state_row;
+    if (args.src_ckpt != nullptr) {
+      // Zero-copy rollback: start from the previous span's checkpoint of its
+      // accepted position. A request with an index outside the previous span
+      // writes nothing (reported through the status word).
+      const int node = args.src_node[r];
+      if (node < 0 || node >= args.src_npos) continue;
+      init_row = args.src_ckpt + ((static_cast<size_t>(r) * args.src_npos + node) * Hv + h) * head_elems +
+                 static_cast<size_t>(row) * DK;
+    }
     float* ckpt_row0 = nullptr;
     if (CAPTURE)
       ckpt_row0 = args.ckpt + static_cast<size_t>(r) * T * pos_stride + static_cast<size_t>(h) * head_elems +
@@ -158,7 +185,7 @@ __global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
     // This lane's columns: chunk m covers [4 (li + LPR m), +4).
     f32x4 s[NCH];
 #pragma unroll
-    for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(state_row + 4 * (li + LPR * m));
+    for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(init_row + 4 * (li + LPR * m));
 
     for (int t0 = 0; t0 < T; t0 += kWindow) {
       const int tn = min(kWindow, T - t0);
@@ -335,19 +362,30 @@ using namespace hrs;
 
 static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, const void* v, const void* a,
                          const void* b, float* state, float* ckpt, float* out, void* stream, void* start_event,
-                         void* stop_event) {
+                         void* stop_event, const hrs_span_source* src = nullptr, int32_t* status = nullptr) {
   if (d == nullptr) return HRS_EINVAL;
   if (d->n_req < 1 || d->n_kheads < 1 || d->n_vheads < 1 || d->d_k < 1 || d->d_v < 1) return HRS_EINVAL;
   if (d->n_vheads % d->n_kheads != 0) return HRS_EINVAL;
   if (!dtype_ok(d->in_dtype)) return HRS_EINVAL;
   if (d->topo != HRS_CHAIN && d->topo != HRS_TREE) return HRS_EINVAL;
-  if (!q || !k || !v || !a || !b || !state || !out) return HRS_EINVAL;
+  if (!q || !k || !v || !a || !b || !out) return HRS_EINVAL;
+  if (src == nullptr && !state) return HRS_EINVAL;
+  if (src != nullptr) {
+    if (!src->ckpt || !src->node || ckpt == nullptr) return HRS_EINVAL;
+    if (src->n_pos < 1 || src->n_pos > HRS_MAX_POS) return HRS_EINVAL;
+    // The new checkpoints must not overwrite the ones the span starts from.
+    const size_t elems = static_cast<size_t>(d->n_vheads) * d->d_v * d->d_k * sizeof(float) * d->n_req;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(ckpt), a1 = a0 + elems * d->n_pos;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(src->ckpt), b1 = b0 + elems * src->n_pos;
+    if (a0 < b1 && b0 < a1) return HRS_EINVAL;
+    if (!aligned16(src->ckpt) || !aligned16(src->node) || (status && !aligned16(status))) return HRS_EALIGN;
+  }
   if (d->topo == HRS_TREE && ckpt == nullptr) return HRS_EINVAL;
   if (static_cast<int64_t>(d->d_v) * d->n_vheads > (1 << 20) || d->n_req > (1 << 20)) return HRS_EINVAL;
   const int geo = check_topology(d->topo, d->parent, d->n_req, d->n_pos);
   if (geo != HRS_OK) return geo;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(a) || !aligned16(b) ||
-      !aligned16(state) || !aligned16(out) || (ckpt && !aligned16(ckpt)))
+      (state && !aligned16(state)) || !aligned16(out) || (ckpt && !aligned16(ckpt)))
     return HRS_EALIGN;
   if (d->d_k != 64 && d->d_k != 128) return HRS_EUNSUPPORTED;
   if (d->d_v % 16 != 0 || d->d_v > 256) return HRS_EUNSUPPORTED;
@@ -357,6 +395,11 @@ static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, co
   args.state = state; args.ckpt = ckpt; args.out = out;
   args.n_pos = d->n_pos; args.n_kheads = d->n_kheads; args.n_vheads = d->n_vheads;
   args.d_v = d->d_v; args.group = d->n_vheads / d->n_kheads; args.q_scale = d->q_scale;
+  args.src_ckpt = src ? src->ckpt : nullptr;
+  args.src_node = src ? src->node : nullptr;
+  args.src_npos = src ? src->n_pos : 0;
+  args.n_req_total = d->n_req;
+  args.status = src ? status : nullptr;
 
   const bool tree = d->topo == HRS_TREE;
   const bool capture = ckpt != nullptr;
@@ -413,6 +456,13 @@ extern "C" int gdn_verify_span(const hrs_gdn_desc* d, const void* q, const void*
                                const void* a, const void* b, float* state, float* ckpt, float* out,
                                void* stream) {
   return gdn_span_impl(d, q, k, v, a, b, state, ckpt, out, stream, nullptr, nullptr);
+}
+
+extern "C" int gdn_verify_span_from(const hrs_gdn_desc* d, const hrs_span_source* src, const void* q, const void* k,
+                                    const void* v, const void* a, const void* b, float* ckpt, float* out,
+                                    int32_t* status, void* stream) {
+  if (src == nullptr) return HRS_EINVAL;
+  return gdn_span_impl(d, q, k, v, a, b, nullptr, ckpt, out, stream, nullptr, nullptr, src, status);
 }
 
 extern "C" int gdn_verify_span_timed(const hrs_gdn_desc* d, const void* q, const void* k, const void* v,

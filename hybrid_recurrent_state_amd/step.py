@@ -23,8 +23,8 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import (AcceptDesc, ConvDesc, GdnDesc, HRS_BF16, HRS_CHAIN, HRS_F32, HRS_TREE, HrsError, RingDesc,
-               RingRun, RollbackDesc, accept_greedy_workspace_bytes, lib)
+from . import (AcceptDesc, ConvAdvanceDesc, ConvDesc, GdnDesc, HRS_BF16, HRS_CHAIN, HRS_F32, HRS_TREE, HrsError,
+               RingDesc, RingRun, RollbackDesc, SpanSource, accept_greedy_workspace_bytes, lib)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -264,3 +264,83 @@ class VerifyStep:
         """One step by graph replay, then the step's single host sync."""
         self.graph.replay()
         return self._host()
+
+
+class ZeroCopyVerifyStep(VerifyStep):
+    """Verify step with zero-copy rollback (gdn_verify_span_from) and compact
+    conv state (conv1d_verify_span_nocapture + conv_state_advance).
+
+    Two checkpoint buffers alternate between steps: step i writes buffer i % 2
+    and its spans start from buffer (i - 1) % 2 at the accepted position that
+    step i - 1's acceptance left in ``accept_node`` (the first step starts from
+    ``state``). Nothing is copied to roll back; the conv state is rebuilt from
+    the x rows along the accepted path. ``materialize()`` writes the canonical
+    recurrent state into ``state`` (rollback_restore) when a caller needs it.
+    Needs logits (acceptance produces the path the conv state follows).
+    """
+
+    def __init__(self, bufs: StepBuffers, parent=None, runs: Optional[Sequence[tuple]] = None,
+                 silu: bool = False, q_scale: float = 1.0):
+        import torch
+        super().__init__(bufs, parent, runs, silu, q_scale)
+        s = bufs.shape
+        if not s.vocab:
+            raise ValueError("zero-copy rollback needs logits: the conv state follows the accepted path")
+        L, R, T = s.n_layers, s.n_req, s.n_pos
+        if getattr(bufs, "ckpt2", None) is None:
+            bufs.ckpt2 = torch.empty_like(bufs.ckpt)
+        self.ckpts = (bufs.ckpt, bufs.ckpt2)
+        b = bufs
+        dt = HRS_BF16 if s.bf16 else HRS_F32
+        self.adv_desc = ConvAdvanceDesc(L, R, T, s.conv_channels, s.conv_width, dt)
+        self.adv_p = ctypes.byref(self.adv_desc)
+        self.adv_args = (b.x.data_ptr(), b.conv_state.data_ptr(), b.path.data_ptr(), b.accept_len.data_ptr(), None)
+        ptr = lambda t, l: t[l].data_ptr()
+        self.conv_args = [(ptr(b.x, l), ptr(b.w, l), ptr(b.conv_state, l), ptr(b.y, l)) for l in range(L)]
+        # [c][l]: inputs and outputs of layer l when writing checkpoint buffer c.
+        self.srcs = [[SpanSource(ptr(self.ckpts[1 - c], l), b.accept_node.data_ptr(), T) for l in range(L)]
+                     for c in range(2)]
+        self.gdn_io = [[(ptr(b.q, l), ptr(b.k, l), ptr(b.v, l), ptr(b.a, l), ptr(b.b, l), ptr(self.ckpts[c], l),
+                         ptr(b.out, l)) for l in range(L)] for c in range(2)]
+        self.first = True
+        self.cur = 0
+
+    def launch_layer(self, l: int, stream: int, events=None) -> None:
+        _check(lib.conv1d_verify_span_nocapture(self.conv_p, *self.conv_args[l], stream),
+               "conv1d_verify_span_nocapture")
+        q, k, v, a, bb, ck, out = self.gdn_io[self.cur][l]
+        if self.first:
+            _check(lib.gdn_verify_span(self.gdn_p, q, k, v, a, bb, self.layer_args[l][1][5], ck, out, stream),
+                   "gdn_verify_span")
+        else:
+            _check(lib.gdn_verify_span_from(self.gdn_p, ctypes.byref(self.srcs[self.cur][l]), q, k, v, a, bb, ck,
+                                            out, None, stream), "gdn_verify_span_from")
+
+    def launch_rollback(self, stream: int) -> None:
+        # The rollback of the recurrent state is the next step's source index;
+        # only the conv state is rebuilt.
+        _check(lib.conv_state_advance(self.adv_p, *self.adv_args, stream), "conv_state_advance")
+
+    def launch(self, stream=None, gdn_events=None) -> None:
+        super().launch(stream, gdn_events=None)
+        self.first = False
+        self.cur ^= 1
+
+    def current_ckpt(self):
+        """Checkpoint buffer written by the last launched step."""
+        return self.ckpts[self.cur ^ 1]
+
+    def materialize(self, stream=None) -> None:
+        """state <- checkpoint of the accepted position of the last step (all layers)."""
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        h = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        s = self.bufs.shape
+        d = RollbackDesc(s.n_layers, s.n_req, s.n_pos, s.n_vheads, s.d_k, s.d_v, 0, 0, HRS_F32)
+        b = self.bufs
+        _check(lib.rollback_restore(ctypes.byref(d), self.current_ckpt().data_ptr(), b.state.data_ptr(), None, None,
+                                    b.accept_node.data_ptr(), b.status.data_ptr(), h), "rollback_restore")
+
+    def capture_graph(self) -> None:
+        raise NotImplementedError("the zero-copy step alternates buffers; launch it eagerly")

@@ -160,6 +160,32 @@ int gdn_verify_span(const hrs_gdn_desc* desc, const void* q, const void* k,
                     const void* v, const void* a, const void* b, float* state,
                     float* ckpt, float* out, void* stream);
 
+/* Where a span's initial state comes from when it is not `state`. */
+typedef struct {
+  const float* ckpt;    /* device: the previous span's checkpoints of this layer,
+                           [R][n_pos][Hv][d_v][d_k] float32 */
+  const int32_t* node;  /* device [R]: the accepted position of that span
+                           (accept_node of accept_greedy) */
+  int32_t n_pos;        /* positions of the previous span, in [1, HRS_MAX_POS] */
+} hrs_span_source;
+
+/*
+ * gdn_verify_span_from - zero-copy rollback: gdn_verify_span whose initial
+ * state for request r is src->ckpt[r][src->node[r]], read in place on the
+ * device, instead of `state`. Rolling back to the accepted checkpoint then
+ * costs nothing: no copy into `state` happens at all ([P3] Summary restores
+ * the accepted F32 checkpoint; this reads it where it already is). Capture is
+ * required (ckpt != NULL) and ckpt must not overlap src->ckpt, so callers
+ * alternate two checkpoint buffers between consecutive spans. A request whose
+ * node is outside [0, src->n_pos) writes no checkpoint or output; status
+ * (optional device int32, may be NULL) receives the number of such requests.
+ * The canonical state can be materialised any time with rollback_restore.
+ * Arithmetic, layouts and other errors as gdn_verify_span.
+ */
+int gdn_verify_span_from(const hrs_gdn_desc* desc, const hrs_span_source* src, const void* q,
+                         const void* k, const void* v, const void* a, const void* b, float* ckpt,
+                         float* out, int32_t* status, void* stream);
+
 /*
  * gdn_verify_span_timed - gdn_verify_span whose kernel dispatch also records
  * two caller-created hipEvent_t (from the same HIP runtime as `stream`):
@@ -211,6 +237,44 @@ typedef struct {
  */
 int conv1d_verify_span(const hrs_conv_desc* desc, const void* x, const void* w,
                        void* conv_state, void* conv_ckpt, float* y, void* stream);
+
+/*
+ * conv1d_verify_span_nocapture - conv1d_verify_span that writes only y (chain
+ * or tree); conv_state is read only and no per-position conv state is
+ * written. With conv_state_advance below this replaces the [T][W-1][C] conv
+ * checkpoint: the conv state after any position is the last W-1 entries of
+ * [conv_state rows, x along that position's root path], so it can be rebuilt
+ * from inputs the caller already holds.
+ */
+int conv1d_verify_span_nocapture(const hrs_conv_desc* desc, const void* x, const void* w,
+                                 const void* conv_state, float* y, void* stream);
+
+typedef struct {
+  int32_t n_layers;  /* L */
+  int32_t n_req;     /* R */
+  int32_t n_pos;     /* T of the span just verified */
+  int32_t channels;  /* C, multiple of 8 */
+  int32_t width;     /* W; 4 is built */
+  hrs_dtype dtype;   /* dtype of x and the conv state */
+} hrs_conv_advance_desc;
+
+/*
+ * conv_state_advance - conv-state rollback without checkpoints: for every
+ * layer l and request r, with n = accept_len[r] + 1 positions on the accepted
+ * path path[r][0..n-1] (from accept_greedy),
+ *     conv_state[l][r] = last W-1 rows of [conv_state[l][r], x[l][r][path[0]], ...,
+ *                                          x[l][r][path[n-1]]]
+ * in one launch, reading the index data on the device ([P1] Changes: conv
+ * state restored on device). Bit-exact copies of input rows.
+ * Layouts: x [L][R][T][C], conv_state [L][R][W-1][C] (dtype); path [R][T],
+ * accept_len [R] int32 device. A request whose accept_len is outside [0, T)
+ * or whose path holds an index outside [0, T) is left untouched; status
+ * (optional device int32) receives the number of such requests.
+ * Errors: HRS_EINVAL, HRS_EALIGN, HRS_EUNSUPPORTED (W != 4), HRS_EDEVICE.
+ */
+int conv_state_advance(const hrs_conv_advance_desc* desc, const void* x, void* conv_state,
+                       const int32_t* path, const int32_t* accept_len, int32_t* status,
+                       void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Greedy acceptance                                                        */

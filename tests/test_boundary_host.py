@@ -245,3 +245,46 @@ def test_ring_rejections():
     # get: two runs writing the same packed rows are rejected, same slots are fine
     assert ring_call(False, runs=((0, 14, 3, 0), (1, 0, 2, 2))) == E.HRS_EINVAL
     assert ring_call(False, runs=((0, 14, 3, 0), (0, 14, 3, 3))) in (E.HRS_EDEVICE, E.HRS_OK)
+
+
+def test_zero_copy_entry_rejections():
+    E = hrs
+    desc = hrs.GdnDesc(2, 4, 2, 4, 128, 128, hrs.HRS_BF16, 1.0, hrs.HRS_CHAIN, None)
+    ck_bytes = 2 * 4 * 4 * 128 * 128 * 4
+
+    def call(src_ckpt=FAKE + (1 << 32), node=FAKE, n_pos=4, ckpt=FAKE, status=None, src=True):
+        s = hrs.SpanSource(src_ckpt, node, n_pos)
+        return hrs.lib.gdn_verify_span_from(ctypes.byref(desc), ctypes.byref(s) if src else None, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, ckpt, FAKE, status, None)
+    assert call(src=False) == E.HRS_EINVAL
+    assert call(src_ckpt=None) == E.HRS_EINVAL
+    assert call(node=None) == E.HRS_EINVAL
+    assert call(ckpt=None) == E.HRS_EINVAL                  # capture required
+    assert call(n_pos=0) == E.HRS_EINVAL
+    assert call(n_pos=65) == E.HRS_EINVAL
+    assert call(src_ckpt=FAKE + ck_bytes // 2) == E.HRS_EINVAL   # new checkpoints overlap the source
+    assert call(src_ckpt=FAKE + ck_bytes) in (E.HRS_EDEVICE, E.HRS_OK)   # adjacent, no overlap
+    assert call(node=MIS) == E.HRS_EALIGN
+    assert call(status=MIS) == E.HRS_EALIGN
+    assert call() in (E.HRS_EDEVICE, E.HRS_OK)
+
+
+def test_conv_nocapture_and_advance_rejections():
+    E = hrs
+    d = hrs.ConvDesc(1, 4, 64, 4, hrs.HRS_BF16, 0, hrs.HRS_TREE, None)
+    assert hrs.lib.conv1d_verify_span_nocapture(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) == E.HRS_EGEOMETRY
+    par = np.array([-1, 0, 0, 1], dtype=np.int32)
+    d = hrs.ConvDesc(1, 4, 64, 4, hrs.HRS_BF16, 0, hrs.HRS_TREE, par.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    assert hrs.lib.conv1d_verify_span_nocapture(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) in (E.HRS_EDEVICE, E.HRS_OK)
+    assert hrs.lib.conv1d_verify_span_nocapture(ctypes.byref(d), FAKE, FAKE, None, FAKE, None) == E.HRS_EINVAL
+
+    def adv(L=2, R=3, T=5, C=64, W=4, dt=hrs.HRS_BF16, x=FAKE, cs=FAKE, path=FAKE, ln=FAKE, st=None):
+        a = hrs.ConvAdvanceDesc(L, R, T, C, W, dt)
+        return hrs.lib.conv_state_advance(ctypes.byref(a), x, cs, path, ln, st, None)
+    assert adv(L=0) == E.HRS_EINVAL
+    assert adv(T=65) == E.HRS_EINVAL
+    assert adv(C=12) == E.HRS_EINVAL
+    assert adv(path=None) == E.HRS_EINVAL
+    assert adv(cs=MIS) == E.HRS_EALIGN
+    assert adv(W=3) == E.HRS_EUNSUPPORTED
+    assert adv() in (E.HRS_EDEVICE, E.HRS_OK)
