@@ -35,8 +35,10 @@ What each module computes and where it comes from:
               Changes: one get_2d and one set_2d per non-wrapping run).
   geometry  - the draft-tree geometry guard (lucebox PR #506, Safety
               boundary).
+  fused     - one layer in its own order: conv with SiLU, split into q/k/v
+              heads, q/k L2 norm, gated delta rule (composition of the above).
 
 Parity status of each function is stated in its module header.
 """
-from . import accept, conv, gdn, geometry, ring, rollback  # noqa: F401
+from . import accept, conv, fused, gdn, geometry, ring, rollback  # noqa: F401
 from .common import widen  # noqa: F401
