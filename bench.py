@@ -253,6 +253,25 @@ def main():
                                                        "vs_copy_rollback": ms_per_step / ms_z}
             log(f"f2 zero-copy step {ms_z:.3f} ms")
             del zc
+            # f1: the same zero-copy step with every layer fused into one
+            # kernel (conv, SiLU, split, q/k L2 norm, gated delta rule).
+            if shape.conv_channels == 2 * w.n_kheads * w.d_k + w.n_vheads * w.d_v:
+                from hybrid_recurrent_state_amd.step import FusedVerifyStep
+                fs = FusedVerifyStep(bufs, parent=loaded.parent, runs=loaded.runs)
+                for _ in range(args.warmup):
+                    fs.run(stream)
+                torch.cuda.synchronize()
+                f0 = time.perf_counter()
+                for _ in range(K):
+                    fs.launch(stream)
+                    fs.finish()
+                torch.cuda.synchronize()
+                ms_f = (time.perf_counter() - f0) * 1e3 / K
+                next_rows["f1_fused_layer_step"] = {
+                    "ms_per_step": ms_f, "value": R * T * L / (ms_f / 1e3), "vs_zero_copy_step": ms_z / ms_f,
+                    "layer_bytes_per_launch": shape.layer_bytes_per_layer}
+                log(f"f1 fused-layer step {ms_f:.3f} ms")
+                del fs
             bufs.ckpt2 = None
             torch.cuda.empty_cache()
 

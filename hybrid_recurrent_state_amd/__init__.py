@@ -49,6 +49,10 @@ class GdnDesc(ctypes.Structure):
                 ("topo", _i32), ("parent", ctypes.POINTER(_i32))]
 
 
+class GdnLayerDesc(ctypes.Structure):
+    _fields_ = [("gdn", GdnDesc), ("conv_width", _i32), ("silu", _i32), ("l2_eps", ctypes.c_float)]
+
+
 class ConvDesc(ctypes.Structure):
     _fields_ = [("n_req", _i32), ("n_pos", _i32), ("channels", _i32), ("width", _i32),
                 ("dtype", _i32), ("silu", _i32), ("topo", _i32), ("parent", ctypes.POINTER(_i32))]
@@ -90,6 +94,8 @@ _SIGNATURES = {
     "gdn_verify_span_timed": (_i32, [ctypes.POINTER(GdnDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "gdn_verify_span_from": (_i32, [ctypes.POINTER(GdnDesc), ctypes.POINTER(SpanSource), _p, _p, _p, _p, _p, _p,
                                     _p, _p, _p]),
+    "gdn_layer_verify_span": (_i32, [ctypes.POINTER(GdnLayerDesc), _p, _p, _p, _p, _p, _p,
+                                     ctypes.POINTER(SpanSource), _p, _p, _p, _p]),
     "conv1d_verify_span_nocapture": (_i32, [ctypes.POINTER(ConvDesc), _p, _p, _p, _p, _p]),
     "conv_state_advance": (_i32, [ctypes.POINTER(ConvAdvanceDesc), _p, _p, _p, _p, _p, _p]),
     "conv1d_verify_span": (_i32, [ctypes.POINTER(ConvDesc), _p, _p, _p, _p, _p, _p]),
@@ -257,6 +263,29 @@ def gdn_verify_span_from(src_ckpt, src_node, q, k, v, a, b, ckpt, out, parent=No
     st = lib.gdn_verify_span_from(ctypes.byref(d), ctypes.byref(src), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
                                   _ptr(ckpt), _ptr(out), _ptr(status), _stream(stream))
     _check(st, "gdn_verify_span_from")
+
+
+def gdn_layer_verify_span(x, conv_w, conv_state, a, b, ckpt, out, n_kheads: int, d_k: int, state=None,
+                          src_ckpt=None, src_node=None, parent=None, status=None, q_scale: float = 1.0,
+                          l2_eps: float = 1e-6, silu: bool = True, stream=None):
+    """One GDN layer in its own order (conv, SiLU, split, q/k L2 norm, gated
+    delta rule) in one kernel. x [R,T,C] with C = 2*Hk*dk + Hv*dv, channels
+    [q | k | v]; conv_w [C,4]; conv_state [R,3,C] (read only); a, b [R,T,Hv];
+    ckpt [R,T,Hv,dv,dk] f32; out [R,T,Hv,dv] f32. The initial state is either
+    state [R,Hv,dv,dk] f32 or src_ckpt[r][src_node[r]] (zero-copy)."""
+    R, T, C = x.shape
+    Hv = a.shape[2]
+    dv = (C - 2 * n_kheads * d_k) // Hv
+    par, par_p = _parent_array(parent, R, T)
+    g = GdnDesc(R, T, n_kheads, Hv, d_k, dv, _dtype_code(x), float(q_scale),
+                HRS_TREE if parent is not None else HRS_CHAIN, par_p)
+    d = GdnLayerDesc(g, conv_w.shape[1], int(bool(silu)), float(l2_eps))
+    src = None
+    if src_ckpt is not None:
+        src = ctypes.byref(SpanSource(_ptr(src_ckpt), _ptr(src_node), src_ckpt.shape[1]))
+    st = lib.gdn_layer_verify_span(ctypes.byref(d), _ptr(x), _ptr(conv_w), _ptr(conv_state), _ptr(a), _ptr(b),
+                                   _ptr(state), src, _ptr(ckpt), _ptr(out), _ptr(status), _stream(stream))
+    _check(st, "gdn_layer_verify_span")
 
 
 def conv1d_verify_span_nocapture(x, w, conv_state, y, parent=None, silu: bool = False, stream=None):

@@ -70,8 +70,20 @@ constexpr int pos_floats(int dk, int rows, bool tree) {
   return tree ? (2 * dk + rows + 3 + 3) / 4 * 4 : 2 * dk + rows + 2;
 }
 
+// LDS floats of one staging buffer (rounded to 16 bytes).
+constexpr int staging_floats(int window, int pos_fl) { return (window * pos_fl + 3) / 4 * 4; }
+
 constexpr size_t staging_bytes(int dk, int rows, int window, bool tree) {
-  return static_cast<size_t>(window) * pos_floats(dk, rows, tree) * sizeof(float);
+  return static_cast<size_t>(staging_floats(window, pos_floats(dk, rows, tree))) * sizeof(float);
+}
+
+// Producer waves of the capturing chain kernel (one per SIMD).
+constexpr int kProducerWaves = 4;
+
+// LDS bytes of the producer/consumer kernel: two staging buffers, one unit's
+// state rows and a flag word.
+constexpr size_t pipelined_bytes(int dk, int rows, int window) {
+  return 2 * staging_bytes(dk, rows, window, false) + (static_cast<size_t>(rows) * dk + 4) * sizeof(float);
 }
 
 // LDS bytes of one tree stash slot: every lane's dk / 16 floats of its row.
@@ -102,51 +114,399 @@ struct GdnArgs {
   int32_t src_npos;
   int32_t n_req_total;
   int32_t* status;  // optional: number of requests whose src_node is out of range
-  // Tree mode, each [requests of this launch][n_pos]: parent index, restore
-  // code and save slot (gdn_tree_schedule).
-  int8_t parent[kGeomBytes / 3];
-  int8_t restore[kGeomBytes / 3];
-  int8_t save[kGeomBytes / 3];
+  // Fused layer (gdn_layer_verify_span): conv input, weights and state; q, k
+  // and v are computed from them instead of read.
+  const void* x;           // [R][T][C], C = 2*Hk*dk + Hv*dv, channels [q | k | v]
+  const void* conv_w;      // [C][4]
+  const void* conv_state;  // [R][3][C]
+  int32_t conv_c;
+  int32_t silu;
+  float l2_eps;
+  // Tree mode, for the n = geom_req requests of this launch, each array
+  // [n][n_pos]: parent index at 0, restore code at n*T, save slot at 2*n*T
+  // (gdn_tree_schedule); fused layers add the conv window sources
+  // [n][n_pos][3] at 3*n*T (conv_window_sources).
+  int32_t geom_req;
+  int8_t geom[kGeomBytes];
 };
 
+// Sixteen consecutive elements as f32 (the source must be 16-byte aligned).
+template <typename TIn>
+__device__ __forceinline__ void load16(const TIn* p, float* o) {
+  load8<TIn>(p, o);
+  load8<TIn>(p + 8, o + 8);
+}
+
+// One row unit: rows [row0, row0 + RPB) of value head h of request r.
+struct Unit {
+  int r;     // request
+  int rl;    // request within this launch
+  int h;     // value head
+  int g;     // key head
+  int row0;  // first row
+};
+
+// Units are numbered row block fastest, then value head, then request.
+__device__ __forceinline__ Unit unit_of(const GdnArgs& args, int W, int rpb) {
+  const int nrb = args.d_v / rpb;
+  Unit u;
+  u.row0 = (W % nrb) * rpb;
+  u.h = (W / nrb) % args.n_vheads;
+  u.rl = W / (nrb * args.n_vheads);
+  u.r = args.req0 + u.rl;
+  u.g = u.h / args.group;
+  return u;
+}
+
+// Staging, plain inputs: k and q (times q_scale) of key head g and the unit's
+// v rows for positions [t0, t0 + tn), 8 elements per item, by the NTH staging
+// threads (p is the thread's index among them). q/k and v items share one
+// index space, so a thread's loads for all its items are issued together.
+template <int DK, int NTH, int RPB, int POS_FLOATS, typename TIn>
+__device__ __forceinline__ void stage_plain(const GdnArgs& args, float* buf, const Unit& u, int t0, int tn, int p) {
+  const int T = args.n_pos;
+  const TIn* qg = static_cast<const TIn*>(args.q);
+  const TIn* kg = static_cast<const TIn*>(args.k);
+  const TIn* vg = static_cast<const TIn*>(args.v);
+  constexpr int V8 = DK / 8;
+  constexpr int R8 = RPB / 8;
+  const int n_qk = tn * V8;
+  const int total = n_qk + tn * R8;
+  for (int e = p; e < total; e += NTH) {
+    if (e < n_qk) {
+      const int tt = e / V8;
+      const int j = (e % V8) * 8;
+      const size_t src = ((static_cast<size_t>(u.r) * T + t0 + tt) * args.n_kheads + u.g) * DK + j;
+      float kv[8], qv[8];
+      load8<TIn>(kg + src, kv);
+      load8<TIn>(qg + src, qv);
+      float* lk = buf + tt * POS_FLOATS + j;
+      float* lq = lk + DK;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lk[i] = kv[i];
+        lq[i] = qv[i] * args.q_scale;
+      }
+    } else {
+      const int ev = e - n_qk;
+      const int tt = ev / R8;
+      const int i0 = (ev % R8) * 8;
+      const size_t src =
+          ((static_cast<size_t>(u.r) * T + t0 + tt) * args.n_vheads + u.h) * args.d_v + u.row0 + i0;
+      float vv[8];
+      load8<TIn>(vg + src, vv);
+      float* lv = buf + tt * POS_FLOATS + 2 * DK + i0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) lv[i] = vv[i];
+    }
+  }
+}
+
+// Staging, fused layer: for every staged position, the conv (and SiLU) of
+// the unit's channels, written where the plain staging puts q, k and v: q
+// and k of key head g scaled to unit L2 norm (q also by q_scale), and the
+// unit's v rows. One item is 16 channels of one position; the DK / 16 items
+// of a q or k row sit in adjacent lanes, so the row's sum of squares is a DPP
+// group sum and the normalisation needs no extra pass or barrier. Window rows
+// come from x or the conv state: for a chain position t they are positions
+// t-3..t-1 (conv-state row t+m when negative); for a tree the host table
+// names them. Weight w[c][3] multiplies the current input.
+template <int DK, int NTH, int RPB, int POS_FLOATS, typename TIn, bool TREE>
+__device__ __forceinline__ void stage_fused(const GdnArgs& args, float* buf, const Unit& u, int t0, int tn, int p) {
+  constexpr int CPI = 16;            // channels per item
+  constexpr int QL = DK / CPI;       // items of one q or k row (4 or 8: a DPP group)
+  constexpr int VI = RPB / CPI;      // items of the unit's v rows at one position
+  static_assert(QL == 4 || QL == 8, "q/k row items form a DPP group");
+  static_assert(NTH % QL == 0, "staging threads cover whole q/k rows");
+  const int T = args.n_pos;
+  const int C = args.conv_c;
+  const int Hk = args.n_kheads;
+  const TIn* x = static_cast<const TIn*>(args.x);
+  const TIn* cs = static_cast<const TIn*>(args.conv_state);
+  const TIn* wc = static_cast<const TIn*>(args.conv_w);
+  const int n_qk = tn * 2 * QL;
+  const int total = n_qk + tn * VI;
+  for (int e = p; e < total; e += NTH) {
+    int tt, ch, part;   // part: 0 q, 1 k, 2 v
+    float* dst;
+    if (e < n_qk) {
+      const int row = e / QL;
+      const int cg = e % QL;
+      tt = row >> 1;
+      part = row & 1;
+      ch = part * Hk * DK + u.g * DK + cg * CPI;
+      dst = buf + tt * POS_FLOATS + (part ? 0 : DK) + cg * CPI;   // k first, then q
+    } else {
+      const int i = e - n_qk;
+      tt = i / VI;
+      part = 2;
+      ch = 2 * Hk * DK + u.h * args.d_v + u.row0 + (i % VI) * CPI;
+      dst = buf + tt * POS_FLOATS + 2 * DK + (i % VI) * CPI;
+    }
+    const int t = t0 + tt;
+    float win[4][CPI];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      int src;
+      if constexpr (TREE) {
+        src = args.geom[3 * args.geom_req * T + (u.rl * T + t) * 3 + m];
+      } else {
+        const int sq = t - 3 + m;
+        src = sq >= 0 ? sq : -1 - (t + m);
+      }
+      const TIn* ptr = src >= 0 ? x + (static_cast<size_t>(u.r) * T + src) * C + ch
+                                : cs + (static_cast<size_t>(u.r) * 3 + (-1 - src)) * C + ch;
+      load16<TIn>(ptr, win[m]);
+    }
+    load16<TIn>(x + (static_cast<size_t>(u.r) * T + t) * C + ch, win[3]);
+    float w[4 * CPI];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load16<TIn>(wc + static_cast<size_t>(ch) * 4 + CPI * i, w + CPI * i);
+    float y[CPI];
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPI; ++c) {
+      float acc = w[c * 4] * win[0][c];
+#pragma unroll
+      for (int m = 1; m < 4; ++m) acc = __builtin_fmaf(w[c * 4 + m], win[m][c], acc);
+      y[c] = args.silu ? acc / (1.0f + expf(-acc)) : acc;
+      ss = __builtin_fmaf(y[c], y[c], ss);
+    }
+    if (part < 2) {
+      // Every lane of a row's group takes this branch together (n_qk and the
+      // loop stride are multiples of QL).
+      ss = group_sum<QL>(ss);
+      const float scale = (part ? 1.0f : args.q_scale) / sqrtf(ss + args.l2_eps);
+#pragma unroll
+      for (int c = 0; c < CPI; ++c) y[c] *= scale;
+    }
+#pragma unroll
+    for (int c = 0; c < CPI; ++c) dst[c] = y[c];
+  }
+}
+
+// Staging, per position: a, b and (trees) the position's tree code. The tree
+// code travels through LDS: reading the kernel-argument bytes inside the
+// position loop would be a vector load whose wait also drains every
+// outstanding checkpoint store.
+template <int DK, int NTH, int RPB, int POS_FLOATS, typename TIn, bool TREE>
+__device__ __forceinline__ void stage_gates(const GdnArgs& args, float* buf, const Unit& u, int t0, int tn, int p) {
+  const int T = args.n_pos;
+  const TIn* ag = static_cast<const TIn*>(args.a);
+  const TIn* bg = static_cast<const TIn*>(args.b);
+  for (int e = p; e < tn; e += NTH) {
+    const size_t src = (static_cast<size_t>(u.r) * T + t0 + e) * args.n_vheads + u.h;
+    buf[e * POS_FLOATS + 2 * DK + RPB] = load_elem<TIn>(ag, src);
+    buf[e * POS_FLOATS + 2 * DK + RPB + 1] = load_elem<TIn>(bg, src);
+    if constexpr (TREE) {
+      const int gi = u.rl * T + t0 + e;
+      const int nT = args.geom_req * T;
+      const uint32_t code = static_cast<uint8_t>(args.geom[gi]) |
+                            (static_cast<uint32_t>(static_cast<uint8_t>(args.geom[nT + gi])) << 8) |
+                            (static_cast<uint32_t>(static_cast<uint8_t>(args.geom[2 * nT + gi])) << 16);
+      buf[e * POS_FLOATS + 2 * DK + RPB + 2] = __uint_as_float(code);
+    }
+  }
+}
+
+template <int DK, int NTH, int RPB, int POS_FLOATS, typename TIn, bool TREE, bool FUSED>
+__device__ __forceinline__ void stage_window(const GdnArgs& args, float* buf, const Unit& u, int t0, int tn, int p) {
+  if constexpr (FUSED)
+    stage_fused<DK, NTH, RPB, POS_FLOATS, TIn, TREE>(args, buf, u, t0, tn, p);
+  else
+    stage_plain<DK, NTH, RPB, POS_FLOATS, TIn>(args, buf, u, t0, tn, p);
+  stage_gates<DK, NTH, RPB, POS_FLOATS, TIn, TREE>(args, buf, u, t0, tn, p);
+}
+
+// The unit's initial state rows: `state`, or for a zero-copy span the
+// previous span's checkpoint at the request's accepted position. nullptr when
+// that index is out of range (the request then writes nothing).
+template <int DK>
+__device__ __forceinline__ const float* initial_rows(const GdnArgs& args, const Unit& u) {
+  const size_t head_elems = static_cast<size_t>(args.d_v) * DK;
+  if (args.src_ckpt != nullptr) {
+    const int node = args.src_node[u.r];
+    if (node < 0 || node >= args.src_npos) return nullptr;
+    return args.src_ckpt + ((static_cast<size_t>(u.r) * args.src_npos + node) * args.n_vheads + u.h) * head_elems +
+           static_cast<size_t>(u.row0) * DK;
+  }
+  return args.state + (static_cast<size_t>(u.r) * args.n_vheads + u.h) * head_elems +
+         static_cast<size_t>(u.row0) * DK;
+}
+
+// Positions [t0, t0 + tn) of one unit, for the consumer threads: S rows in
+// VGPRs, staged inputs from LDS, checkpoint and output stores. No barrier and
+// (without RELOAD) no vector-memory load.
+template <int DK, int NW, int RPB, int POS_FLOATS, bool TREE, bool RELOAD, bool CAPTURE>
+__device__ __forceinline__ void run_positions(const float* buf, f32x4* stash, f32x4 (&s)[DK / 64], int t0, int tn,
+                                              float* ckpt_row0, float* out_r, size_t pos_stride, int out_stride) {
+  constexpr int LPR = kLanesPerRow;
+  constexpr int NCH = DK / (4 * LPR);
+  constexpr int NTHREADS = NW * 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int li = lane % LPR;
+  const int row_blk = (tid >> 6) * (64 / LPR) + lane / LPR;
+  for (int tt = 0; tt < tn; ++tt) {
+    const int t = t0 + tt;
+    const float* lp = buf + tt * POS_FLOATS;
+    int tree_code = 0;
+    if constexpr (TREE) {
+      tree_code = __builtin_amdgcn_readfirstlane(__float_as_int(lp[2 * DK + RPB + 2]));
+      const int rs = static_cast<int8_t>((tree_code >> 8) & 0xFF);
+      if (rs >= 0) {
+#pragma unroll
+        for (int m = 0; m < NCH; ++m) s[m] = stash[(rs * NCH + m) * NTHREADS + tid];
+      } else if (RELOAD && rs == kFromGlobal) {
+        const int p = static_cast<int8_t>(tree_code & 0xFF);
+        const float* src = ckpt_row0 + static_cast<size_t>(p) * pos_stride;
+#pragma unroll
+        for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(src + 4 * (li + LPR * m));
+        // Wait here, inside the rare reload branch: otherwise the compiler
+        // waits at every later use of s on every position, and since the
+        // vector-memory counter retires in order, each such wait would also
+        // drain all outstanding checkpoint stores.
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      }
+    }
+    f32x4 kk[NCH];
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) kk[m] = *reinterpret_cast<const f32x4*>(lp + 4 * (li + LPR * m));
+    float u = 0.0f;
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      u = __builtin_fmaf(s[m].x, kk[m].x, u);
+      u = __builtin_fmaf(s[m].y, kk[m].y, u);
+      u = __builtin_fmaf(s[m].z, kk[m].z, u);
+      u = __builtin_fmaf(s[m].w, kk[m].w, u);
+    }
+    u = group_sum<LPR>(u);
+    const float at = lp[2 * DK + RPB];
+    const float bt = lp[2 * DK + RPB + 1];
+    const float vt = lp[2 * DK + row_blk];
+    const float c = bt * __builtin_fmaf(-at, u, vt);
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      s[m].x = __builtin_fmaf(c, kk[m].x, at * s[m].x);
+      s[m].y = __builtin_fmaf(c, kk[m].y, at * s[m].y);
+      s[m].z = __builtin_fmaf(c, kk[m].z, at * s[m].z);
+      s[m].w = __builtin_fmaf(c, kk[m].w, at * s[m].w);
+    }
+    if (CAPTURE) {
+      float* dst = ckpt_row0 + static_cast<size_t>(t) * pos_stride;
+#pragma unroll
+      for (int m = 0; m < NCH; ++m)
+        __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(dst + 4 * (li + LPR * m)));
+    }
+    if constexpr (TREE) {
+      const int sv = static_cast<int8_t>((tree_code >> 16) & 0xFF);
+      if (sv >= 0) {
+#pragma unroll
+        for (int m = 0; m < NCH; ++m) stash[(sv * NCH + m) * NTHREADS + tid] = s[m];
+      }
+    }
+    float o = 0.0f;
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      const f32x4 qq = *reinterpret_cast<const f32x4*>(lp + DK + 4 * (li + LPR * m));
+      o = __builtin_fmaf(s[m].x, qq.x, o);
+      o = __builtin_fmaf(s[m].y, qq.y, o);
+      o = __builtin_fmaf(s[m].z, qq.z, o);
+      o = __builtin_fmaf(s[m].w, qq.w, o);
+    }
+    o = group_sum<LPR>(o);
+    if (li == 0) out_r[static_cast<size_t>(t) * out_stride] = o;
+  }
+}
+
+// Producer staging of one item (a window of positions of one unit) into buf,
+// by NTH threads (p = index among them); at a unit's first window also its
+// initial state rows and the valid flag. ONE_WAIT: the state-row and gate
+// loads are issued before the input loads and all are written afterwards, so
+// the thread waits for memory once; otherwise each part waits in turn.
+template <int DK, int NTH, int RPB, int POS_FLOATS, typename TIn, bool FUSED, bool ONE_WAIT>
+__device__ __forceinline__ void produce_item(const GdnArgs& args, float* buf, float* state_lds, int* flag_lds,
+                                             const Unit& u, int t0, int tn, int p) {
+  constexpr int N4 = RPB * DK / 4;   // float4 chunks of a unit's state rows
+  constexpr int SPT = (N4 + NTH - 1) / NTH;
+  static_assert(kWindow <= NTH, "one gate pair per staging thread");
+  const int T = args.n_pos;
+  const float* init = t0 == 0 ? initial_rows<DK>(args, u) : nullptr;
+  if constexpr (ONE_WAIT) {
+    const TIn* ag = static_cast<const TIn*>(args.a);
+    const TIn* bg = static_cast<const TIn*>(args.b);
+    const size_t gsrc = (static_cast<size_t>(u.r) * T + t0 + min(p, tn - 1)) * args.n_vheads + u.h;
+    const float ga = load_elem<TIn>(ag, gsrc);
+    const float gb = load_elem<TIn>(bg, gsrc);
+    f32x4 sv[SPT];
+    if (init != nullptr) {
+#pragma unroll
+      for (int k = 0; k < SPT; ++k) sv[k] = reinterpret_cast<const f32x4*>(init)[min(p + k * NTH, N4 - 1)];
+    }
+    if constexpr (FUSED)
+      stage_fused<DK, NTH, RPB, POS_FLOATS, TIn, false>(args, buf, u, t0, tn, p);
+    else
+      stage_plain<DK, NTH, RPB, POS_FLOATS, TIn>(args, buf, u, t0, tn, p);
+    if (p < tn) {
+      buf[p * POS_FLOATS + 2 * DK + RPB] = ga;
+      buf[p * POS_FLOATS + 2 * DK + RPB + 1] = gb;
+    }
+    if (init != nullptr) {
+#pragma unroll
+      for (int k = 0; k < SPT; ++k)
+        if (p + k * NTH < N4) reinterpret_cast<f32x4*>(state_lds)[p + k * NTH] = sv[k];
+    }
+  } else {
+    if (init != nullptr) {
+      f32x4 sv[SPT];
+#pragma unroll
+      for (int k = 0; k < SPT; ++k) sv[k] = reinterpret_cast<const f32x4*>(init)[min(p + k * NTH, N4 - 1)];
+#pragma unroll
+      for (int k = 0; k < SPT; ++k)
+        if (p + k * NTH < N4) reinterpret_cast<f32x4*>(state_lds)[p + k * NTH] = sv[k];
+    }
+    stage_window<DK, NTH, RPB, POS_FLOATS, TIn, false, FUSED>(args, buf, u, t0, tn, p);
+  }
+  if (t0 == 0 && p == 0) flag_lds[0] = init != nullptr;
+}
+
+// NW waves own the unit's rows (the consumers). NP == 0: the same waves also
+// stage every window before processing it. NP > 0: NP further waves (the
+// producers) stage window i+1 (and, at a unit's start, its initial state
+// rows) into the other half of a double buffer while the consumers process
+// window i. Every wave has its own vector-memory counter, so the producers'
+// loads never wait for the consumers' checkpoint stores, and the consumers
+// issue no vector-memory load at all: the store stream does not stop between
+// units.
 // TREE: positions follow the launch's stash schedule; RELOAD: some position
 // reloads its parent's checkpoint from memory (trees with more than
-// kStashSlots live branch points). Without RELOAD the position loop holds no
-// vector-memory load at all, so the compiler never has to wait on the
-// in-order vector-memory counter (which the checkpoint stores also occupy).
-template <int DK, int NW, typename TIn, bool TREE, bool RELOAD, bool CAPTURE>
-__global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
+// kStashSlots live branch points). FUSED: one layer in its own order; the
+// staging computes q, k and v from the conv input (conv, SiLU, split, q/k L2
+// norm) instead of loading them.
+template <int DK, int NW, int NP, typename TIn, bool TREE, bool RELOAD, bool CAPTURE, bool FUSED>
+__global__ __launch_bounds__((NW + NP) * 64) void gdn_span_kernel(const GdnArgs args) {
   constexpr int LPR = kLanesPerRow;
   constexpr int RPW = 64 / LPR;          // rows per wave
   constexpr int RPB = RPW * NW;          // rows per unit
   constexpr int NCH = DK / (4 * LPR);    // float4 chunks per lane
   static_assert(NCH >= 1 && DK % (4 * LPR) == 0, "lane mapping");
+  static_assert(NP == 0 || (!TREE && CAPTURE), "only the capturing chain kernel has producer waves");
   constexpr int POS_FLOATS = pos_floats(DK, RPB, TREE);
+  constexpr int NC = NW * 64;            // consumer threads
 
   extern __shared__ float lds[];
-  // Tree stash: [slot][chunk][thread] float4, after the staged positions.
-  f32x4* const stash = reinterpret_cast<f32x4*>(lds + args.window * POS_FLOATS);
-  constexpr int NTHREADS = NW * 64;
-
   const int T = args.n_pos;
   const int Hv = args.n_vheads;
-  const int Hk = args.n_kheads;
   const int dv = args.d_v;
-  const int nrb = dv / RPB;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
   const int lane = tid & 63;
   const int li = lane % LPR;
-  const int row_blk = wave * RPW + lane / LPR;
+  const int row_blk = (tid >> 6) * RPW + lane / LPR;
   const size_t head_elems = static_cast<size_t>(dv) * DK;
   const size_t pos_stride = static_cast<size_t>(Hv) * head_elems;   // one position of ckpt
-  const TIn* qg = static_cast<const TIn*>(args.q);
-  const TIn* kg = static_cast<const TIn*>(args.k);
-  const TIn* vg = static_cast<const TIn*>(args.v);
-  const TIn* ag = static_cast<const TIn*>(args.a);
-  const TIn* bg = static_cast<const TIn*>(args.b);
+  const int out_stride = Hv * dv;
 
-  if (args.status != nullptr && args.req0 == 0 && blockIdx.x == 0 && threadIdx.x == 0) {
+  if (args.status != nullptr && args.req0 == 0 && blockIdx.x == 0 && tid == (NP > 0 ? NC : 0)) {
     int32_t bad = 0;
     for (int i = 0; i < args.n_req_total; ++i) {
       const int32_t u = args.src_node[i];
@@ -154,189 +514,132 @@ __global__ __launch_bounds__(NW * 64) void gdn_span_kernel(const GdnArgs args) {
     }
     *args.status = bad;
   }
-  for (int W = blockIdx.x; W < args.n_units; W += gridDim.x) {
-    const int rb = W % nrb;
-    const int h = (W / nrb) % Hv;
-    const int rl = W / (nrb * Hv);           // request within the launch
-    const int r = args.req0 + rl;
-    const int g = h / args.group;
-    const int row0 = rb * RPB;
-    const int row = row0 + row_blk;
 
-    float* state_row =
-        args.state ? args.state + (static_cast<size_t>(r) * Hv + h) * head_elems + static_cast<size_t>(row) * DK
+  // Consumer pointers of the current unit.
+  auto ckpt_of = [&](const Unit& u) -> float* {
+    return CAPTURE ? args.ckpt + static_cast<size_t>(u.r) * T * pos_stride + static_cast<size_t>(u.h) * head_elems +
+                         static_cast<size_t>(u.row0 + row_blk) * DK
                    : nullptr;
-    const float* init_row = state_row;
-    if (args.src_ckpt != nullptr) {
-      // Zero-copy rollback: start from the previous span's checkpoint of its
-      // accepted position. A request with an index outside the previous span
-      // writes nothing (reported through the status word).
-      const int node = args.src_node[r];
-      if (node < 0 || node >= args.src_npos) continue;
-      init_row = args.src_ckpt + ((static_cast<size_t>(r) * args.src_npos + node) * Hv + h) * head_elems +
-                 static_cast<size_t>(row) * DK;
-    }
-    float* ckpt_row0 = nullptr;
-    if (CAPTURE)
-      ckpt_row0 = args.ckpt + static_cast<size_t>(r) * T * pos_stride + static_cast<size_t>(h) * head_elems +
-                  static_cast<size_t>(row) * DK;
-    float* out_r = args.out + (static_cast<size_t>(r) * T * Hv + h) * dv + row;
+  };
+  auto out_of = [&](const Unit& u) -> float* {
+    return args.out + (static_cast<size_t>(u.r) * T * Hv + u.h) * dv + u.row0 + row_blk;
+  };
+  f32x4 s[NCH];
 
-    // This lane's columns: chunk m covers [4 (li + LPR m), +4).
-    f32x4 s[NCH];
+  if constexpr (NP == 0) {
+    f32x4* const stash = reinterpret_cast<f32x4*>(lds + staging_floats(args.window, POS_FLOATS));
+    for (int W = blockIdx.x; W < args.n_units; W += gridDim.x) {
+      const Unit u = unit_of(args, W, RPB);
+      const float* init = initial_rows<DK>(args, u);
+      if (init == nullptr) continue;   // block-uniform: every thread has the same request
+      init += static_cast<size_t>(row_blk) * DK;
 #pragma unroll
-    for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(init_row + 4 * (li + LPR * m));
-
-    for (int t0 = 0; t0 < T; t0 += kWindow) {
-      const int tn = min(kWindow, T - t0);
-      __syncthreads();  // LDS reads of the previous window (or unit) are done
-      // Stage k and q (scaled) of key head g, 8 elements per thread-step.
-      {
-        constexpr int V8 = DK / 8;
-        for (int e = tid; e < tn * V8; e += NW * 64) {
-          const int tt = e / V8;
-          const int j = (e % V8) * 8;
-          const size_t src = ((static_cast<size_t>(r) * T + t0 + tt) * Hk + g) * DK + j;
-          float kv[8], qv[8];
-          load8<TIn>(kg + src, kv);
-          load8<TIn>(qg + src, qv);
-          float* lk = lds + tt * POS_FLOATS + j;
-          float* lq = lk + DK;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            lk[i] = kv[i];
-            lq[i] = qv[i] * args.q_scale;
-          }
-        }
-        for (int e = tid; e < tn * RPB; e += NW * 64) {
-          const int tt = e / RPB;
-          const int i = e % RPB;
-          const size_t src = ((static_cast<size_t>(r) * T + t0 + tt) * Hv + h) * dv + row0 + i;
-          lds[tt * POS_FLOATS + 2 * DK + i] = load_elem<TIn>(vg, src);
-        }
-        for (int e = tid; e < tn; e += NW * 64) {
-          const size_t src = (static_cast<size_t>(r) * T + t0 + e) * Hv + h;
-          lds[e * POS_FLOATS + 2 * DK + RPB] = load_elem<TIn>(ag, src);
-          lds[e * POS_FLOATS + 2 * DK + RPB + 1] = load_elem<TIn>(bg, src);
-          if constexpr (TREE) {
-            // The tree code travels through LDS: reading the kernel-argument
-            // bytes inside the position loop would be a vector load whose wait
-            // also drains every outstanding checkpoint store.
-            const int gi = rl * T + t0 + e;
-            const uint32_t code = static_cast<uint8_t>(args.parent[gi]) |
-                                  (static_cast<uint32_t>(static_cast<uint8_t>(args.restore[gi])) << 8) |
-                                  (static_cast<uint32_t>(static_cast<uint8_t>(args.save[gi])) << 16);
-            lds[e * POS_FLOATS + 2 * DK + RPB + 2] = __uint_as_float(code);
-          }
-        }
+      for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(init + 4 * (li + LPR * m));
+      float* const ckpt_row0 = ckpt_of(u);
+      float* const out_r = out_of(u);
+      for (int t0 = 0; t0 < T; t0 += kWindow) {
+        const int tn = min(kWindow, T - t0);
+        __syncthreads();  // LDS reads of the previous window (or unit) are done
+        stage_window<DK, NC, RPB, POS_FLOATS, TIn, TREE, FUSED>(args, lds, u, t0, tn, tid);
+        __syncthreads();
+        run_positions<DK, NW, RPB, POS_FLOATS, TREE, RELOAD, CAPTURE>(lds, stash, s, t0, tn, ckpt_row0, out_r,
+                                                                      pos_stride, out_stride);
       }
-      __syncthreads();
+      if (!CAPTURE) {
+        float* state_row = args.state + (static_cast<size_t>(u.r) * Hv + u.h) * head_elems +
+                           static_cast<size_t>(u.row0 + row_blk) * DK;
+#pragma unroll
+        for (int m = 0; m < NCH; ++m) *reinterpret_cast<f32x4*>(state_row + 4 * (li + LPR * m)) = s[m];
+      }
+    }
+  } else {
+    constexpr int NTH = NP * 64;           // producer threads
+    const int SB = staging_floats(args.window, POS_FLOATS);
+    float* const state_lds = lds + 2 * SB;
+    int* const flag_lds = reinterpret_cast<int*>(state_lds + RPB * DK);
+    const bool consumer = tid < NC;        // wave-uniform
+    const int p = tid - NC;                // producer index
+    const int nwin = (T + kWindow - 1) / kWindow;
+    const int n_my = static_cast<int>(blockIdx.x) < args.n_units
+                         ? (args.n_units - 1 - static_cast<int>(blockIdx.x)) / static_cast<int>(gridDim.x) + 1
+                         : 0;
+    const int n_items = n_my * nwin;       // (unit, window) pairs of this block, in order
 
-      for (int tt = 0; tt < tn; ++tt) {
-        const int t = t0 + tt;
-        const float* lp = lds + tt * POS_FLOATS;
-        int tree_code = 0;
-        if constexpr (TREE) {
-          tree_code = __builtin_amdgcn_readfirstlane(__float_as_int(lp[2 * DK + RPB + 2]));
-          const int rs = static_cast<int8_t>((tree_code >> 8) & 0xFF);
-          if (rs >= 0) {
-#pragma unroll
-            for (int m = 0; m < NCH; ++m) s[m] = stash[(rs * NCH + m) * NTHREADS + tid];
-          } else if (RELOAD && rs == kFromGlobal) {
-            const int p = static_cast<int8_t>(tree_code & 0xFF);
-            const float* src = ckpt_row0 + static_cast<size_t>(p) * pos_stride;
-#pragma unroll
-            for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(src + 4 * (li + LPR * m));
-            // Wait here, inside the rare reload branch: otherwise the compiler
-            // waits at every later use of s on every position, and since the
-            // vector-memory counter retires in order, each such wait would also
-            // drain all outstanding checkpoint stores.
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-          }
-        }
-        f32x4 kk[NCH];
-#pragma unroll
-        for (int m = 0; m < NCH; ++m) kk[m] = *reinterpret_cast<const f32x4*>(lp + 4 * (li + LPR * m));
-        float u = 0.0f;
-#pragma unroll
-        for (int m = 0; m < NCH; ++m) {
-          u = __builtin_fmaf(s[m].x, kk[m].x, u);
-          u = __builtin_fmaf(s[m].y, kk[m].y, u);
-          u = __builtin_fmaf(s[m].z, kk[m].z, u);
-          u = __builtin_fmaf(s[m].w, kk[m].w, u);
-        }
-        u = group_sum<LPR>(u);
-        const float at = lp[2 * DK + RPB];
-        const float bt = lp[2 * DK + RPB + 1];
-        const float vt = lp[2 * DK + row_blk];
-        const float c = bt * __builtin_fmaf(-at, u, vt);
-#pragma unroll
-        for (int m = 0; m < NCH; ++m) {
-          s[m].x = __builtin_fmaf(c, kk[m].x, at * s[m].x);
-          s[m].y = __builtin_fmaf(c, kk[m].y, at * s[m].y);
-          s[m].z = __builtin_fmaf(c, kk[m].z, at * s[m].z);
-          s[m].w = __builtin_fmaf(c, kk[m].w, at * s[m].w);
-        }
-        if (CAPTURE) {
-          float* dst = ckpt_row0 + static_cast<size_t>(t) * pos_stride;
+    // Stage item i into buffer i % 2: all threads for item 0 (no checkpoint
+    // store is in flight yet), the producers for every later item.
+    auto item_unit = [&](int i) { return unit_of(args, blockIdx.x + (i / nwin) * gridDim.x, RPB); };
+    if (n_items > 0)
+      produce_item<DK, (NW + NP) * 64, RPB, POS_FLOATS, TIn, FUSED, true>(args, lds, state_lds, flag_lds, item_unit(0),
+                                                                          0, min(kWindow, T), tid);
+    __syncthreads();
+    bool valid = false;
+    float* ckpt_row0 = nullptr;
+    float* out_r = nullptr;
+    for (int i = 0; i < n_items; ++i) {
+      const int j = i % nwin;
+      if (consumer && j == 0) {
+        const Unit u = unit_of(args, blockIdx.x + (i / nwin) * gridDim.x, RPB);
+        valid = flag_lds[0] != 0;
+        if (valid) {
 #pragma unroll
           for (int m = 0; m < NCH; ++m)
-            __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(dst + 4 * (li + LPR * m)));
+            s[m] = *reinterpret_cast<const f32x4*>(state_lds + row_blk * DK + 4 * (li + LPR * m));
         }
-        if constexpr (TREE) {
-          const int sv = static_cast<int8_t>((tree_code >> 16) & 0xFF);
-          if (sv >= 0) {
-#pragma unroll
-            for (int m = 0; m < NCH; ++m) stash[(sv * NCH + m) * NTHREADS + tid] = s[m];
-          }
-        }
-        float o = 0.0f;
-#pragma unroll
-        for (int m = 0; m < NCH; ++m) {
-          const f32x4 qq = *reinterpret_cast<const f32x4*>(lp + DK + 4 * (li + LPR * m));
-          o = __builtin_fmaf(s[m].x, qq.x, o);
-          o = __builtin_fmaf(s[m].y, qq.y, o);
-          o = __builtin_fmaf(s[m].z, qq.z, o);
-          o = __builtin_fmaf(s[m].w, qq.w, o);
-        }
-        o = group_sum<LPR>(o);
-        if (li == 0) out_r[static_cast<size_t>(t) * Hv * dv] = o;
+        ckpt_row0 = ckpt_of(u);
+        out_r = out_of(u);
       }
-    }
-    if (!CAPTURE) {
-#pragma unroll
-      for (int m = 0; m < NCH; ++m) *reinterpret_cast<f32x4*>(state_row + 4 * (li + LPR * m)) = s[m];
+      __syncthreads();  // the state rows and flag are read: producers may replace them
+      if (consumer) {
+        if (valid) {
+          const int t0 = j * kWindow;
+          run_positions<DK, NW, RPB, POS_FLOATS, false, false, CAPTURE>(
+              lds + (i & 1) * SB, nullptr, s, t0, min(kWindow, T - t0), ckpt_row0, out_r, pos_stride, out_stride);
+        }
+      } else if (i + 1 < n_items) {
+        const int t0 = ((i + 1) % nwin) * kWindow;
+        // The fused staging issues all its loads before its first wait; the
+        // plain staging measured faster with its loads spread over the item.
+        produce_item<DK, NTH, RPB, POS_FLOATS, TIn, FUSED, FUSED>(args, lds + ((i + 1) & 1) * SB, state_lds, flag_lds,
+                                                                 item_unit(i + 1), t0, min(kWindow, T - t0), p);
+      }
+      __syncthreads();  // window i + 1 is staged; buffer i % 2 is free
     }
   }
 }
 
 // Launch through hipExtLaunchKernelGGL so that optional timing events are
 // recorded by the dispatch itself (no extra stream commands between kernels).
-template <int DK, int NW, typename TIn, bool TREE, bool RELOAD, bool CAPTURE>
+template <int DK, int NW, int NP, typename TIn, bool TREE, bool RELOAD, bool CAPTURE, bool FUSED>
 hipError_t launch_one(GdnArgs& args, int grid, int n_slots, hipStream_t stream, hipEvent_t start,
                       hipEvent_t stop) {
   constexpr int RPB = (64 / kLanesPerRow) * NW;
-  const size_t lds = staging_bytes(DK, RPB, args.window, TREE) + (TREE ? n_slots * slot_bytes(DK, NW) : 0);
-  hipExtLaunchKernelGGL((gdn_span_kernel<DK, NW, TIn, TREE, RELOAD, CAPTURE>), dim3(grid), dim3(NW * 64), lds,
-                        stream, start, stop, 0, args);
+  const size_t lds = NP > 0 ? pipelined_bytes(DK, RPB, args.window)
+                            : staging_bytes(DK, RPB, args.window, TREE) + (TREE ? n_slots * slot_bytes(DK, NW) : 0);
+  hipExtLaunchKernelGGL((gdn_span_kernel<DK, NW, NP, TIn, TREE, RELOAD, CAPTURE, FUSED>), dim3(grid),
+                        dim3((NW + NP) * 64), lds, stream, start, stop, 0, args);
   return launch_error();
 }
 
 enum class Mode { kChainNoCapture, kChain, kTree, kTreeReload };
 
-template <int DK, int NW, typename TIn>
+template <int DK, int NW, typename TIn, bool FUSED>
 hipError_t launch_mode(GdnArgs& args, Mode mode, int grid, int n_slots, hipStream_t s, hipEvent_t e0,
                        hipEvent_t e1) {
+  // f32 conv inputs need twice the registers of bf16 ones in the fused
+  // staging; that variant keeps the single-role kernel (no spills).
+  constexpr int NP = (FUSED && sizeof(TIn) == 4) ? 0 : kProducerWaves;
   switch (mode) {
-    case Mode::kTreeReload: return launch_one<DK, NW, TIn, true, true, true>(args, grid, n_slots, s, e0, e1);
-    case Mode::kTree: return launch_one<DK, NW, TIn, true, false, true>(args, grid, n_slots, s, e0, e1);
-    case Mode::kChain: return launch_one<DK, NW, TIn, false, false, true>(args, grid, 0, s, e0, e1);
-    default: return launch_one<DK, NW, TIn, false, false, false>(args, grid, 0, s, e0, e1);
+    case Mode::kTreeReload:
+      return launch_one<DK, NW, 0, TIn, true, true, true, FUSED>(args, grid, n_slots, s, e0, e1);
+    case Mode::kTree: return launch_one<DK, NW, 0, TIn, true, false, true, FUSED>(args, grid, n_slots, s, e0, e1);
+    case Mode::kChain: return launch_one<DK, NW, NP, TIn, false, false, true, FUSED>(args, grid, 0, s, e0, e1);
+    default:
+      // The fused layer always captures (checked by the entry point).
+      if constexpr (FUSED) return hipErrorInvalidValue;
+      else return launch_one<DK, NW, 0, TIn, false, false, false, false>(args, grid, 0, s, e0, e1);
   }
 }
 
-// Launch shape: 32-row units on a one-block-per-CU grid when there are at
-// least as many such units as CUs, else one 4-wave block per 16-row unit.
 // Launch shape: 32-row units on a one-block-per-CU grid when there are at
 // least as many such units as CUs, else one 4-wave block per 16-row unit.
 int waves_for(int d_v, int n_vheads, int n_req_launch, int n_cu) {
@@ -344,16 +647,35 @@ int waves_for(int d_v, int n_vheads, int n_req_launch, int n_cu) {
   return (units32 >= n_cu && n_cu > 0) ? 8 : 4;
 }
 
-template <int DK, typename TIn>
+template <int DK, typename TIn, bool FUSED>
 hipError_t launch_dk(GdnArgs& args, int n_req_launch, int n_cu, int waves, Mode mode, int n_slots,
                      hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (waves == 8) {
     args.n_units = (args.d_v / 32) * args.n_vheads * n_req_launch;
-    return launch_mode<DK, 8, TIn>(args, mode, n_cu, n_slots, s, e0, e1);
+    return launch_mode<DK, 8, TIn, FUSED>(args, mode, n_cu, n_slots, s, e0, e1);
   }
   args.n_units = (args.d_v / 16) * args.n_vheads * n_req_launch;
-  return launch_mode<DK, 4, TIn>(args, mode, args.n_units, n_slots, s, e0, e1);
+  return launch_mode<DK, 4, TIn, FUSED>(args, mode, args.n_units, n_slots, s, e0, e1);
 }
+
+template <bool FUSED>
+hipError_t launch_any(const hrs_gdn_desc* d, GdnArgs& args, int n, int n_cu, int waves, Mode mode, int n_slots,
+                      hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (d->d_k == 128)
+    return d->in_dtype == HRS_BF16 ? launch_dk<128, uint16_t, FUSED>(args, n, n_cu, waves, mode, n_slots, s, e0, e1)
+                                   : launch_dk<128, float, FUSED>(args, n, n_cu, waves, mode, n_slots, s, e0, e1);
+  return d->in_dtype == HRS_BF16 ? launch_dk<64, uint16_t, FUSED>(args, n, n_cu, waves, mode, n_slots, s, e0, e1)
+                                 : launch_dk<64, float, FUSED>(args, n, n_cu, waves, mode, n_slots, s, e0, e1);
+}
+
+// Inputs of the fused layer: the conv input and weights replace q, k and v.
+struct FusedInputs {
+  const void* x;
+  const void* conv_w;
+  const void* conv_state;
+  int32_t silu;
+  float l2_eps;
+};
 
 }  // namespace
 }  // namespace hrs
@@ -362,13 +684,20 @@ using namespace hrs;
 
 static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, const void* v, const void* a,
                          const void* b, float* state, float* ckpt, float* out, void* stream, void* start_event,
-                         void* stop_event, const hrs_span_source* src = nullptr, int32_t* status = nullptr) {
+                         void* stop_event, const hrs_span_source* src = nullptr, int32_t* status = nullptr,
+                         const FusedInputs* fused = nullptr) {
   if (d == nullptr) return HRS_EINVAL;
   if (d->n_req < 1 || d->n_kheads < 1 || d->n_vheads < 1 || d->d_k < 1 || d->d_v < 1) return HRS_EINVAL;
   if (d->n_vheads % d->n_kheads != 0) return HRS_EINVAL;
   if (!dtype_ok(d->in_dtype)) return HRS_EINVAL;
   if (d->topo != HRS_CHAIN && d->topo != HRS_TREE) return HRS_EINVAL;
-  if (!q || !k || !v || !a || !b || !out) return HRS_EINVAL;
+  if (fused != nullptr) {
+    if (!fused->x || !fused->conv_w || !fused->conv_state || ckpt == nullptr) return HRS_EINVAL;
+    if (!(fused->l2_eps >= 0.0f)) return HRS_EINVAL;
+  } else if (!q || !k || !v) {
+    return HRS_EINVAL;
+  }
+  if (!a || !b || !out) return HRS_EINVAL;
   if (src == nullptr && !state) return HRS_EINVAL;
   if (src != nullptr) {
     if (!src->ckpt || !src->node || ckpt == nullptr) return HRS_EINVAL;
@@ -384,8 +713,11 @@ static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, co
   if (static_cast<int64_t>(d->d_v) * d->n_vheads > (1 << 20) || d->n_req > (1 << 20)) return HRS_EINVAL;
   const int geo = check_topology(d->topo, d->parent, d->n_req, d->n_pos);
   if (geo != HRS_OK) return geo;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(a) || !aligned16(b) ||
+  if ((fused == nullptr && (!aligned16(q) || !aligned16(k) || !aligned16(v))) || !aligned16(a) || !aligned16(b) ||
       (state && !aligned16(state)) || !aligned16(out) || (ckpt && !aligned16(ckpt)))
+    return HRS_EALIGN;
+  if (fused != nullptr &&
+      (!aligned16(fused->x) || !aligned16(fused->conv_w) || !aligned16(fused->conv_state)))
     return HRS_EALIGN;
   if (d->d_k != 64 && d->d_k != 128) return HRS_EUNSUPPORTED;
   if (d->d_v % 16 != 0 || d->d_v > 256) return HRS_EUNSUPPORTED;
@@ -400,10 +732,20 @@ static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, co
   args.src_npos = src ? src->n_pos : 0;
   args.n_req_total = d->n_req;
   args.status = src ? status : nullptr;
+  args.x = fused ? fused->x : nullptr;
+  args.conv_w = fused ? fused->conv_w : nullptr;
+  args.conv_state = fused ? fused->conv_state : nullptr;
+  args.conv_c = 2 * d->n_kheads * d->d_k + d->n_vheads * d->d_v;
+  args.silu = fused ? fused->silu : 0;
+  args.l2_eps = fused ? fused->l2_eps : 0.0f;
+  args.geom_req = 0;
 
   const bool tree = d->topo == HRS_TREE;
   const bool capture = ckpt != nullptr;
-  const int per_launch = tree ? std::max(1, (kGeomBytes / 3) / d->n_pos) : 4096;
+  // Tree geometry bytes per (request, position): parent, restore, save, and
+  // for the fused layer three conv window sources.
+  const int geom_per_pos = fused ? 6 : 3;
+  const int per_launch = tree ? std::max(1, (kGeomBytes / geom_per_pos) / d->n_pos) : 4096;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   int dev = 0, n_cu = 0, max_lds = 0;
@@ -424,29 +766,31 @@ static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, co
     int n_slots = 0;
     if (tree) {
       const int T_ = d->n_pos;
+      const int nT = n * T_;
+      int8_t* g_parent = args.geom;
+      int8_t* g_restore = args.geom + nT;
+      int8_t* g_save = args.geom + 2 * nT;
+      int8_t* g_window = args.geom + 3 * nT;
+      args.geom_req = n;
       // Stash slots that fit in LDS beside the staging buffer.
       const size_t stage = staging_bytes(d->d_k, 4 * waves, args.window, true);
       const size_t per_slot = slot_bytes(d->d_k, waves);
       const size_t room = static_cast<size_t>(max_lds) > stage ? static_cast<size_t>(max_lds) - stage : 0;
       const int fit = static_cast<int>(std::min<size_t>(kStashSlots, room / per_slot));
-      for (int i = 0; i < n * T_; ++i)
-        args.parent[i] = static_cast<int8_t>(d->parent[static_cast<size_t>(r0) * T_ + i]);
-      for (int j = 0; j < n; ++j)
-        gdn_tree_schedule(d->parent + static_cast<size_t>(r0 + j) * T_, T_, fit, args.restore + j * T_,
-                          args.save + j * T_);
+      for (int i = 0; i < nT; ++i) g_parent[i] = static_cast<int8_t>(d->parent[static_cast<size_t>(r0) * T_ + i]);
+      for (int j = 0; j < n; ++j) {
+        const int32_t* par = d->parent + static_cast<size_t>(r0 + j) * T_;
+        gdn_tree_schedule(par, T_, fit, g_restore + j * T_, g_save + j * T_);
+        if (fused) conv_window_sources(par, T_, 4, g_window + j * T_ * 3);
+      }
       mode = Mode::kTree;
-      for (int i = 0; i < n * T_; ++i) {
-        if (args.restore[i] == kFromGlobal) mode = Mode::kTreeReload;
-        if (args.save[i] >= n_slots) n_slots = args.save[i] + 1;
+      for (int i = 0; i < nT; ++i) {
+        if (g_restore[i] == kFromGlobal) mode = Mode::kTreeReload;
+        if (g_save[i] >= n_slots) n_slots = g_save[i] + 1;
       }
     }
-    hipError_t e;
-    if (d->d_k == 128)
-      e = d->in_dtype == HRS_BF16 ? launch_dk<128, uint16_t>(args, n, n_cu, waves, mode, n_slots, s, e0, e1)
-                                  : launch_dk<128, float>(args, n, n_cu, waves, mode, n_slots, s, e0, e1);
-    else
-      e = d->in_dtype == HRS_BF16 ? launch_dk<64, uint16_t>(args, n, n_cu, waves, mode, n_slots, s, e0, e1)
-                                  : launch_dk<64, float>(args, n, n_cu, waves, mode, n_slots, s, e0, e1);
+    const hipError_t e = fused ? launch_any<true>(d, args, n, n_cu, waves, mode, n_slots, s, e0, e1)
+                               : launch_any<false>(d, args, n, n_cu, waves, mode, n_slots, s, e0, e1);
     if (e != hipSuccess) return HRS_EDEVICE;
   }
   return HRS_OK;
@@ -469,6 +813,19 @@ extern "C" int gdn_verify_span_timed(const hrs_gdn_desc* d, const void* q, const
                                      const void* a, const void* b, float* state, float* ckpt, float* out,
                                      void* stream, void* start_event, void* stop_event) {
   return gdn_span_impl(d, q, k, v, a, b, state, ckpt, out, stream, start_event, stop_event);
+}
+
+extern "C" int gdn_layer_verify_span(const hrs_gdn_layer_desc* d, const void* x, const void* conv_w,
+                                     const void* conv_state, const void* a, const void* b, const float* state,
+                                     const hrs_span_source* src, float* ckpt, float* out, int32_t* status,
+                                     void* stream) {
+  if (d == nullptr) return HRS_EINVAL;
+  if (d->conv_width != 4) return HRS_EUNSUPPORTED;
+  if ((state == nullptr) == (src == nullptr)) return HRS_EINVAL;   // exactly one initial state
+  if (ckpt == nullptr) return HRS_EINVAL;
+  FusedInputs f{x, conv_w, conv_state, d->silu != 0 ? 1 : 0, d->l2_eps};
+  return gdn_span_impl(&d->gdn, nullptr, nullptr, nullptr, a, b, const_cast<float*>(state), ckpt, out, stream,
+                       nullptr, nullptr, src, status, &f);
 }
 
 extern "C" const char* hrs_last_hip_error_string(void) {

@@ -23,8 +23,8 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import (AcceptDesc, ConvAdvanceDesc, ConvDesc, GdnDesc, HRS_BF16, HRS_CHAIN, HRS_F32, HRS_TREE, HrsError,
-               RingDesc, RingRun, RollbackDesc, SpanSource, accept_greedy_workspace_bytes, lib)
+from . import (AcceptDesc, ConvAdvanceDesc, ConvDesc, GdnDesc, GdnLayerDesc, HRS_BF16, HRS_CHAIN, HRS_F32, HRS_TREE,
+               HrsError, RingDesc, RingRun, RollbackDesc, SpanSource, accept_greedy_workspace_bytes, lib)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -51,6 +51,19 @@ class StepShape:
         R, T, Hk, Hv, dk, dv = self.n_req, self.n_pos, self.n_kheads, self.n_vheads, self.d_k, self.d_v
         e = 2 if self.bf16 else 4
         reads = R * T * (2 * Hk * dk + Hv * dv + 2 * Hv) * e + R * Hv * dv * dk * 4
+        writes = R * T * Hv * dv * dk * 4 + R * T * Hv * dv * 4
+        return reads + writes
+
+    @property
+    def layer_bytes_per_layer(self) -> int:
+        """Algorithmic HBM bytes of one fused gdn_layer_verify_span call: read
+        x, the conv weights, the conv state, a, b and the initial state once;
+        write every checkpoint and every output once (q, k, v and the conv
+        output never reach memory)."""
+        R, T, Hv, dk, dv, C, W = (self.n_req, self.n_pos, self.n_vheads, self.d_k, self.d_v, self.conv_channels,
+                                  self.conv_width)
+        e = 2 if self.bf16 else 4
+        reads = (R * T * C + C * W + R * (W - 1) * C + 2 * R * T * Hv) * e + R * Hv * dv * dk * 4
         writes = R * T * Hv * dv * dk * 4 + R * T * Hv * dv * 4
         return reads + writes
 
@@ -344,3 +357,37 @@ class ZeroCopyVerifyStep(VerifyStep):
 
     def capture_graph(self) -> None:
         raise NotImplementedError("the zero-copy step alternates buffers; launch it eagerly")
+
+
+class FusedVerifyStep(ZeroCopyVerifyStep):
+    """Zero-copy verify step whose layers run in their own order in one kernel
+    each (gdn_layer_verify_span: conv, SiLU, split, q/k L2 norm and the gated
+    delta rule). q, k and v are computed on the chip from x, so the q, k, v
+    and y buffers are not used. Rollback as in ZeroCopyVerifyStep: the next
+    spans start from the accepted checkpoint, the conv state is rebuilt from
+    the accepted path (conv_state_advance).
+    """
+
+    def __init__(self, bufs: StepBuffers, parent=None, runs: Optional[Sequence[tuple]] = None,
+                 silu: bool = True, q_scale: float = 1.0, l2_eps: float = 1e-6):
+        super().__init__(bufs, parent, runs, silu, q_scale)
+        s = bufs.shape
+        if s.conv_channels != 2 * s.n_kheads * s.d_k + s.n_vheads * s.d_v:
+            raise ValueError("the fused layer needs conv channels = 2*Hk*d_k + Hv*d_v (q | k | v)")
+        self.layer_desc = GdnLayerDesc(self.gdn_desc, s.conv_width, int(silu), float(l2_eps))
+        self.layer_p = ctypes.byref(self.layer_desc)
+        b = bufs
+        L = s.n_layers
+        ptr = lambda t, l: t[l].data_ptr()
+        self.fused_in = [(ptr(b.x, l), ptr(b.w, l), ptr(b.conv_state, l), ptr(b.a, l), ptr(b.b, l))
+                         for l in range(L)]
+        self.fused_out = [[(ptr(self.ckpts[c], l), ptr(b.out, l)) for l in range(L)] for c in range(2)]
+
+    def launch_layer(self, l: int, stream: int, events=None) -> None:
+        ck, out = self.fused_out[self.cur][l]
+        if self.first:
+            state, src = self.layer_args[l][1][5], None
+        else:
+            state, src = None, ctypes.byref(self.srcs[self.cur][l])
+        _check(lib.gdn_layer_verify_span(self.layer_p, *self.fused_in[l], state, src, ck, out, None, stream),
+               "gdn_layer_verify_span")

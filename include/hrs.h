@@ -199,6 +199,50 @@ int gdn_verify_span_timed(const hrs_gdn_desc* desc, const void* q, const void* k
                           float* ckpt, float* out, void* stream, void* start_event,
                           void* stop_event);
 
+typedef struct {
+  hrs_gdn_desc gdn;    /* shapes, dtype, q_scale and topology of the span */
+  int32_t conv_width;  /* W of the conv; 4 is built                        */
+  int32_t silu;        /* nonzero: SiLU after the conv (the layer's order)  */
+  float l2_eps;        /* added to |q|^2 and |k|^2 before the square root   */
+} hrs_gdn_layer_desc;
+
+/*
+ * gdn_layer_verify_span - one GDN layer's verify span in the layer's own
+ * order, in one kernel: the causal depthwise conv of the projected channels
+ * (as conv1d_verify_span, optional SiLU), split into q, k and v heads, q and
+ * k scaled to unit L2 norm per head, then the gated delta rule with a
+ * checkpoint after every position (as gdn_verify_span). The conv and
+ * recurrent states are the layer's hybrid state ([P2] What Changed); the
+ * recurrence and checkpoints are those of gdn_verify_span ([GDN]; [P3]
+ * Summary). The conv output never leaves the chip.
+ *
+ * Per request r and position t with conv output y_t (float32, C channels,
+ * C = 2 Hk d_k + Hv d_v, channel order [q heads | k heads | v heads]):
+ *     q_t[g] = y_t[g d_k .. ) / sqrt(|.|^2 + l2_eps)
+ *     k_t[g] = y_t[Hk d_k + g d_k .. ) / sqrt(|.|^2 + l2_eps)
+ *     v_t[h] = y_t[2 Hk d_k + h d_v .. )
+ * then ckpt and out exactly as gdn_verify_span with q_scale applied to the
+ * normalised q.
+ *
+ * Layouts:  x          [R][T][C]        gdn.in_dtype
+ *           conv_w     [C][W]           gdn.in_dtype; w[c][W-1] multiplies x_t
+ *           conv_state [R][W-1][C]      gdn.in_dtype, read only
+ *           a, b       [R][T][Hv]       gdn.in_dtype
+ *           state      [R][Hv][d_v][d_k] float32, read only
+ *           ckpt, out  as gdn_verify_span (ckpt is required)
+ * Exactly one of `state` and `src` gives the initial state; with `src` the
+ * span starts in place from the previous span's accepted checkpoint as in
+ * gdn_verify_span_from (status, optional, counts requests whose node is out
+ * of range; they write nothing). The conv state after the accepted position
+ * comes from conv_state_advance. Errors: HRS_EINVAL, HRS_EALIGN,
+ * HRS_EGEOMETRY, HRS_EUNSUPPORTED (W != 4, d_k/d_v outside the built set),
+ * HRS_EDEVICE.
+ */
+int gdn_layer_verify_span(const hrs_gdn_layer_desc* desc, const void* x, const void* conv_w,
+                          const void* conv_state, const void* a, const void* b,
+                          const float* state, const hrs_span_source* src, float* ckpt,
+                          float* out, int32_t* status, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Causal depthwise conv1d over the span                                    */
 /* ------------------------------------------------------------------------ */

@@ -288,3 +288,40 @@ def test_conv_nocapture_and_advance_rejections():
     assert adv(cs=MIS) == E.HRS_EALIGN
     assert adv(W=3) == E.HRS_EUNSUPPORTED
     assert adv() in (E.HRS_EDEVICE, E.HRS_OK)
+
+
+def test_layer_entry_rejections():
+    E = hrs
+
+    def call(width=4, silu=1, eps=1e-6, x=FAKE, w=FAKE, cs=FAKE, a=FAKE, state=FAKE, src=None, ckpt=FAKE,
+             d_k=128, n_vheads=4, topo=hrs.HRS_CHAIN, parent=None, desc=True):
+        keep = None
+        par = None
+        if parent is not None:
+            keep = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
+            par = keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        g = hrs.GdnDesc(2, 4, 2, n_vheads, d_k, 128, hrs.HRS_BF16, 1.0, topo, par)
+        d = hrs.GdnLayerDesc(g, width, silu, eps)
+        return hrs.lib.gdn_layer_verify_span(ctypes.byref(d) if desc else None, x, w, cs, a, FAKE, state,
+                                             ctypes.byref(src) if src is not None else None, ckpt, FAKE, None,
+                                             None)
+    assert call(desc=False) == E.HRS_EINVAL
+    assert call(width=3) == E.HRS_EUNSUPPORTED
+    assert call(state=None) == E.HRS_EINVAL                 # no initial state
+    both = hrs.SpanSource(FAKE + (1 << 32), FAKE, 4)
+    assert call(src=both) == E.HRS_EINVAL                    # two initial states
+    assert call(state=None, src=both) in (E.HRS_EDEVICE, E.HRS_OK)
+    assert call(ckpt=None) == E.HRS_EINVAL                   # capture required
+    assert call(x=None) == E.HRS_EINVAL
+    assert call(w=None) == E.HRS_EINVAL
+    assert call(cs=None) == E.HRS_EINVAL
+    assert call(eps=-1.0) == E.HRS_EINVAL
+    assert call(eps=float("nan")) == E.HRS_EINVAL
+    assert call(n_vheads=3) == E.HRS_EINVAL
+    assert call(x=MIS) == E.HRS_EALIGN
+    assert call(cs=MIS) == E.HRS_EALIGN
+    assert call(a=MIS) == E.HRS_EALIGN
+    assert call(d_k=96) == E.HRS_EUNSUPPORTED
+    assert call(topo=hrs.HRS_TREE, parent=[-1, 0, 0, 5, -1, 0, 1, 1]) == E.HRS_EGEOMETRY
+    assert call(topo=hrs.HRS_TREE, parent=[-1, 0, 0, 1, -1, 0, 1, 1]) in (E.HRS_EDEVICE, E.HRS_OK)
+    assert call() in (E.HRS_EDEVICE, E.HRS_OK)
