@@ -78,15 +78,12 @@ def measured_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, seconds: float):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    whole (layer, request) units (conv span, GDN span, acceptance of the
-    request, replay rollback along the accepted path), single-threaded."""
+def _oracle_units(w, units, seconds: float):
+    """Run whole (layer, request) units of the oracle until `seconds` of work
+    are spent; returns (units done, verify tokens, seconds of work)."""
     from threadpoolctl import threadpool_limits
-    import oracle
     from oracle import accept as oacc, conv as oconv, gdn as ogdn, rollback as orb
     from synth import gen_accept, gen_conv_weight, gen_unit
-    units = [(l, r) for r in range(w.n_req) for l in range(w.n_layers)]
     done = 0
     t_work = 0.0
     with threadpool_limits(limits=1):
@@ -101,20 +98,68 @@ def cpu_baseline(w, seconds: float):
             if w.vocab and l == 0:
                 am = oacc.argmax_rows(ai.logits)
                 res = oacc.accept(am, ai.tokens, par)
-                path = res.path
             else:
                 res = oacc.accept(ai.planted_argmax, ai.tokens, par)
-                path = res.path
-            orb.replay_state(u.state, u.q, u.k, u.v, u.a, u.b, path)
-            orb.replay_conv_state(u.conv_state, u.x, path)
+            orb.replay_state(u.state, u.q, u.k, u.v, u.a, u.b, res.path)
+            orb.replay_conv_state(u.conv_state, u.x, res.path)
             t_work += time.perf_counter() - t0
             done += 1
             if t_work >= seconds:
                 break
-    tokens = done * w.n_pos
-    return {"value": tokens / t_work, "unit": "verify tokens/s per layer", "cores": 1, "kind": "oracle",
-            "sample": f"{done} (layer, request) units of {w.name}: conv span, GDN span, acceptance "
-                      f"(argmax once per request), replay rollback; {t_work:.1f} s of CPU work, 1 thread"}
+    return done, done * w.n_pos, t_work
+
+
+def _pool_worker(args):
+    name, units, seconds = args
+    sys.path.insert(0, ROOT)
+    from synth import WORKLOADS
+    return _oracle_units(WORKLOADS[name], units, seconds)
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    whole (layer, request) units (conv span, GDN span, acceptance of the
+    request, replay rollback along the accepted path). First single-threaded;
+    then a pool of worker processes over disjoint units, one per available
+    core (at most 16), each for about seconds / workers."""
+    units = [(l, r) for r in range(w.n_req) for l in range(w.n_layers)]
+    done, tokens, t_work = _oracle_units(w, units, seconds)
+    out = {"value": tokens / t_work, "unit": "verify tokens/s per layer", "cores": 1, "kind": "oracle",
+           "sample": f"{done} (layer, request) units of {w.name}: conv span, GDN span, acceptance "
+                     f"(argmax once per request), replay rollback; {t_work:.1f} s of CPU work, 1 thread"}
+    try:
+        import multiprocessing as mp
+        n = max(1, min(16, len(os.sched_getaffinity(0))))
+        per = max(1.0, seconds / n)
+        chunks = [(w.name, units[i::n], per) for i in range(n)]
+        with mp.get_context("spawn").Pool(n) as pool:
+            res = pool.map(_pool_worker, chunks)
+        rate = sum(tok / t for (_, tok, t) in res if t > 0)
+        out["pool"] = {"value": rate, "cores": n,
+                       "sample": f"{sum(d for d, _, _ in res)} units over {n} worker processes, "
+                                 f"~{per:.1f} s of work each; rate = sum of per-worker rates"}
+    except Exception as e:  # noqa: BLE001 - the pooled figure is optional context
+        out["pool"] = {"error": str(e)}
+    return out
+
+
+def store_stream_gbs(mib: int = 2048, reps: int = 10) -> float:
+    """Reference ceiling: a plain device store stream (torch's fill of one
+    buffer), timed with events over `reps` fills."""
+    import torch
+    buf = torch.empty(mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    buf.fill_(1.0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        buf.fill_(float(i))
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = reps * buf.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return gbs
 
 
 def main():
@@ -192,6 +237,7 @@ def main():
     t3 = time.perf_counter()
     gdn_ms = np.array([[s.elapsed_time(e) for (s, e) in row] for row in ev])
     gdn_avg_s = float(gdn_ms.mean()) / 1e3
+    gdn_med_s = float(np.median(gdn_ms)) / 1e3
 
     # Phase split (separate, untimed pass with events between phases).
     ph = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
@@ -215,6 +261,8 @@ def main():
     gdn_bytes = shape.gdn_bytes_per_layer
     achieved = gdn_bytes / gdn_avg_s / 1e9
     traffic = measured_traffic(name)
+    store_gbs = store_stream_gbs()
+    log(f"store-stream reference {store_gbs:.0f} GB/s")
     log(f"step {ms_per_step:.3f} ms (with GDN events {(t3 - t2) * 1e3 / K:.3f} ms); gdn launch avg "
         f"{gdn_avg_s * 1e6:.1f} us = {achieved:.0f} GB/s; traffic {traffic}; phases {phases}")
 
@@ -301,8 +349,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "gdn_verify_span", "bytes_per_launch": gdn_bytes,
-                     "avg_launch_us": gdn_avg_s * 1e6},
+                     "avg_launch_us": gdn_avg_s * 1e6, "median_launch_us": gdn_med_s * 1e6,
+                     "store_stream_gbs": store_gbs, "frac_of_store_stream": achieved / store_gbs},
         "gdn_tokens_per_s_per_layer": R * T / gdn_avg_s,
+        "draft_tokens_per_s_per_layer": R * (T - 1) * L / (ms_per_step / 1e3),
         "phases_ms": phases,
         "next_rows": next_rows,
         "cpu_baseline": cpu,
