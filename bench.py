@@ -143,6 +143,57 @@ def cpu_baseline(w, seconds: float):
     return out
 
 
+def chunked_prefill_row(reps: int = 10, T: int = 1024, R: int = 1):
+    """f4: one long chain span without capture (prefill length T) on the Qwen
+    GDN layer shape, by gdn_span_chunked (one launch, 64-position chunks,
+    k k^T on the matrix cores) and by the recurrent kernel (gdn_verify_span
+    without capture, T / 64 launches of 64 positions carrying the state in
+    place). Inputs: seeded bf16 q, k (unit norm), v, gates as in synth."""
+    import torch
+    import hybrid_recurrent_state_amd as hrs
+    Hk, Hv, d = 16, 32, 128
+    g = torch.Generator(device="cuda").manual_seed(7)
+    rn = lambda *shape: torch.randn(*shape, device="cuda", generator=g)
+    q = torch.nn.functional.normalize(rn(R, T, Hk, d), dim=-1).to(torch.bfloat16)
+    k = torch.nn.functional.normalize(rn(R, T, Hk, d), dim=-1).to(torch.bfloat16)
+    v = rn(R, T, Hv, d).to(torch.bfloat16)
+    a = torch.sigmoid(-rn(R, T, Hv)).to(torch.bfloat16)
+    b = torch.sigmoid(rn(R, T, Hv)).to(torch.bfloat16)
+    state0 = rn(R, Hv, d, d) * 0.02
+    out = torch.empty(R, T, Hv, d, device="cuda")
+    st = state0.clone()
+
+    def chunked():
+        hrs.gdn_span_chunked(q, k, v, a, b, st, None, out)
+
+    def recurrent():
+        for t0 in range(0, T, 64):
+            sl = slice(t0, min(T, t0 + 64))
+            hrs.gdn_verify_span(q[:, sl], k[:, sl], v[:, sl], a[:, sl], b[:, sl], st, None, out[:, sl])
+
+    if R != 1:
+        raise ValueError("the recurrent baseline slices positions of one request")
+    res = {}
+    for name, fn in (("chunked", chunked), ("recurrent", recurrent)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / reps
+    # both forms from the same state agree (sanity, f32 rounding)
+    st.copy_(state0); chunked(); s1 = st.clone(); o1 = out.clone()
+    st.copy_(state0); recurrent(); s2 = st.clone()
+    rel = float((s1 - s2).abs().max() / s2.abs().max())
+    return {"n_req": R, "n_pos": T, "chunked_ms": res["chunked"], "recurrent_ms": res["recurrent"],
+            "speedup": res["recurrent"] / res["chunked"], "state_rel_diff": rel,
+            "tokens_per_s_per_layer": R * T / (res["chunked"] / 1e3)}
+
+
 def store_stream_gbs(mib: int = 2048, reps: int = 10) -> float:
     """Reference ceiling: a plain device store stream (torch's fill of one
     buffer), timed with events over `reps` fills."""
@@ -322,6 +373,15 @@ def main():
                 del fs
             bufs.ckpt2 = None
             torch.cuda.empty_cache()
+
+    if next_rows is not None:
+        # f4: chunked span for long (prefill-length) spans without capture.
+        try:
+            next_rows["f4_chunked_prefill_span"] = chunked_prefill_row()
+            log(f"f4 chunked prefill {next_rows['f4_chunked_prefill_span']}")
+        except Exception as e:  # noqa: BLE001 - report, do not lose the main line
+            next_rows["f4_chunked_prefill_span"] = {"error": str(e)}
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:

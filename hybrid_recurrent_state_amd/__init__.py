@@ -94,6 +94,7 @@ _SIGNATURES = {
     "gdn_verify_span_timed": (_i32, [ctypes.POINTER(GdnDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "gdn_verify_span_from": (_i32, [ctypes.POINTER(GdnDesc), ctypes.POINTER(SpanSource), _p, _p, _p, _p, _p, _p,
                                     _p, _p, _p]),
+    "gdn_span_chunked": (_i32, [ctypes.POINTER(GdnDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "gdn_layer_verify_span": (_i32, [ctypes.POINTER(GdnLayerDesc), _p, _p, _p, _p, _p, _p,
                                      ctypes.POINTER(SpanSource), _p, _p, _p, _p]),
     "conv1d_verify_span_nocapture": (_i32, [ctypes.POINTER(ConvDesc), _p, _p, _p, _p, _p]),
@@ -263,6 +264,18 @@ def gdn_verify_span_from(src_ckpt, src_node, q, k, v, a, b, ckpt, out, parent=No
     st = lib.gdn_verify_span_from(ctypes.byref(d), ctypes.byref(src), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
                                   _ptr(ckpt), _ptr(out), _ptr(status), _stream(stream))
     _check(st, "gdn_verify_span_from")
+
+
+def gdn_span_chunked(q, k, v, a, b, state, ckpt, out, q_scale: float = 1.0, stream=None):
+    """Chunked (64-position) gated delta rule over a long chain span: same
+    arguments as gdn_verify_span without a parent; ckpt None updates state
+    in place."""
+    R, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    d = GdnDesc(R, T, Hk, Hv, dk, dv, _dtype_code(q), float(q_scale), HRS_CHAIN, None)
+    st = lib.gdn_span_chunked(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(state), _ptr(ckpt),
+                              _ptr(out), _stream(stream))
+    _check(st, "gdn_span_chunked")
 
 
 def gdn_layer_verify_span(x, conv_w, conv_state, a, b, ckpt, out, n_kheads: int, d_k: int, state=None,

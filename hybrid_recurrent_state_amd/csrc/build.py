@@ -24,7 +24,7 @@ PKG = os.path.dirname(CSRC)
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhrs.so")
 
-HIP_SOURCES = ["gdn.hip", "conv.hip", "accept.hip", "rollback.hip", "ring.hip"]
+HIP_SOURCES = ["gdn.hip", "chunked.hip", "conv.hip", "accept.hip", "rollback.hip", "ring.hip"]
 HOST_SOURCES = ["validate.cpp"]
 
 ARCH = "gfx950"

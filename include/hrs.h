@@ -199,6 +199,35 @@ int gdn_verify_span_timed(const hrs_gdn_desc* desc, const void* q, const void* k
                           float* ckpt, float* out, void* stream, void* start_event,
                           void* stop_event);
 
+/* Longest span gdn_span_chunked accepts. */
+#define HRS_MAX_CHUNKED_POS (1 << 20)
+
+/*
+ * gdn_span_chunked - the gated delta rule of gdn_verify_span over a long
+ * chain span (prefill length, up to HRS_MAX_CHUNKED_POS positions), computed
+ * by chunks of 64 positions in the chunkwise form of the delta rule ([GDN]:
+ * the hardware-efficient chunkwise algorithm with the WY/UT representation).
+ * Inside a chunk starting from state S_0 the written values
+ *     w_t = b_t (v_t - a_t S_{t-1} k_t)
+ * solve the unit lower-triangular system
+ *     w_t + sum_{j<t} b_t G[t][j] (k_t . k_j) w_j = b_t (v_t - g_t S_0 k_t),
+ * G[t][j] = a_{j+1}...a_t, g_t = a_0...a_t (products inside the chunk, so
+ * zero or tiny decays are exact), with k k^T on the matrix cores; then
+ * S_t = a_t S_{t-1} + w_t k_t^T and o_t = S_t (q_scale q_t) as in
+ * gdn_verify_span. Same mathematics, different rounding order: results agree
+ * with gdn_verify_span to f32 rounding, not bit for bit.
+ *
+ * Arguments, layouts and capture as gdn_verify_span, chain only (desc->topo
+ * must be HRS_CHAIN; parent is ignored): ckpt != NULL writes every
+ * position's state and leaves `state` unchanged; ckpt == NULL updates `state`
+ * in place to the state after the last position. Errors: HRS_EINVAL (sizes,
+ * NULL pointers, n_pos outside [1, HRS_MAX_CHUNKED_POS]), HRS_EALIGN,
+ * HRS_EUNSUPPORTED (tree topology; d_k or d_v other than 128), HRS_EDEVICE.
+ */
+int gdn_span_chunked(const hrs_gdn_desc* desc, const void* q, const void* k, const void* v,
+                     const void* a, const void* b, float* state, float* ckpt, float* out,
+                     void* stream);
+
 typedef struct {
   hrs_gdn_desc gdn;    /* shapes, dtype, q_scale and topology of the span */
   int32_t conv_width;  /* W of the conv; 4 is built                        */

@@ -1,0 +1,106 @@
+"""GPU parity of the chunked long-span entry point (gdn_span_chunked) against
+the GDN oracle (the plain recurrence), through the C ABI: final states,
+outputs and, with capture, every checkpoint within max relative error 1e-4
+per tile; spans that end inside a chunk, exactly on a chunk boundary and
+within the first chunk; bf16 (matrix-core k k^T) and f32 inputs; zero decays;
+agreement with gdn_verify_span on short spans."""
+import numpy as np
+import pytest
+
+from oracle import gdn as ogdn
+from synth import BF16, F32, QWEN_LAYER_CHAIN, bf16_bits, gen_unit, scaled
+from tests.gpu_util import assert_tiles, say, to_numpy, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hrs():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import hybrid_recurrent_state_amd as m
+    return m
+
+
+def run(hrs, units, capture, q_scale=1.0):
+    import torch
+    st = lambda name: to_torch(np.stack([getattr(u, name) for u in units]))
+    q, k, v, a, b, state = st("q"), st("k"), st("v"), st("a"), st("b"), st("state")
+    R, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    ckpt = torch.full((R, T, Hv, dv, dk), float("nan"), device="cuda") if capture else None
+    out = torch.full((R, T, Hv, dv), float("nan"), device="cuda")
+    hrs.gdn_span_chunked(q, k, v, a, b, state, ckpt, out, q_scale=q_scale)
+    torch.cuda.synchronize()
+    return (to_numpy(ckpt) if capture else None), to_numpy(out), to_numpy(state)
+
+
+def check(units, ck, out, state, capture, q_scale=1.0, what=""):
+    for r, u in enumerate(units):
+        ock, oout = ogdn.gdn_span(u.state, u.q, u.k, u.v, u.a, u.b, None, q_scale)
+        e2 = assert_tiles(out[r], oout, 1, f"{what} out r={r}")
+        if capture:
+            e1 = assert_tiles(ck[r], ock, 2, f"{what} ckpt r={r}")
+            assert np.array_equal(state[r], u.state), "state must be read only with capture"
+        else:
+            e1 = assert_tiles(state[r], ock[-1], 2, f"{what} final state r={r}")
+        say(f"{what} r={r}: state err {e1:.2e}, out err {e2:.2e}")
+
+
+@pytest.mark.parametrize("T,capture", [(150, False), (150, True), (64, False), (1, True), (65, True)])
+def test_chunked_qwen_bf16(hrs, T, capture):
+    w = scaled(QWEN_LAYER_CHAIN, n_req=2, n_pos=T, n_kheads=4, n_vheads=8)
+    units = [gen_unit(w, 0, r) for r in range(w.n_req)]
+    say(f"chunked bf16 R=2 T={T} capture={capture}")
+    ck, out, state = run(hrs, units, capture, q_scale=0.5)
+    check(units, ck, out, state, capture, q_scale=0.5, what=f"bf16 T={T}")
+
+
+def test_chunked_f32_grouped(hrs):
+    w = scaled(QWEN_LAYER_CHAIN, n_req=1, n_pos=130, n_kheads=2, n_vheads=8, dtype=F32)
+    units = [gen_unit(w, 0, 0)]
+    ck, out, state = run(hrs, units, True)
+    check(units, ck, out, state, True, what="f32 grouped")
+
+
+def test_chunked_long_span(hrs):
+    w = scaled(QWEN_LAYER_CHAIN, n_req=1, n_pos=1000, n_kheads=1, n_vheads=2)
+    units = [gen_unit(w, 0, 0)]
+    ck, out, state = run(hrs, units, False)
+    check(units, ck, out, state, False, what="T=1000")
+
+
+def test_chunked_zero_and_unit_decays(hrs):
+    w = scaled(QWEN_LAYER_CHAIN, n_req=1, n_pos=100, n_kheads=2, n_vheads=4)
+    u = gen_unit(w, 0, 0)
+    a = u.a.copy()
+    a[[3, 40, 64, 65, 99], :] = bf16_bits(np.zeros((5, 4), np.float32))        # decay to zero
+    a[[10, 11, 12], :] = bf16_bits(np.ones((3, 4), np.float32))                # no decay
+    u.a = a
+    ck, out, state = run(hrs, [u], True)
+    assert np.isfinite(ck).all() and np.isfinite(out).all()
+    check([u], ck, out, state, True, what="zero decays")
+
+
+def test_chunked_matches_recurrent_kernel_on_short_spans(hrs):
+    import torch
+    w = scaled(QWEN_LAYER_CHAIN, n_req=3, n_pos=17)
+    units = [gen_unit(w, 0, r) for r in range(3)]
+    st = lambda name: to_torch(np.stack([getattr(u, name) for u in units]))
+    q, k, v, a, b, state = st("q"), st("k"), st("v"), st("a"), st("b"), st("state")
+    R, T, Hv, d = 3, 17, 32, 128
+    ck1 = torch.empty((R, T, Hv, d, d), device="cuda"); out1 = torch.empty((R, T, Hv, d), device="cuda")
+    ck2 = torch.empty_like(ck1); out2 = torch.empty_like(out1)
+    hrs.gdn_span_chunked(q, k, v, a, b, state, ck1, out1)
+    hrs.gdn_verify_span(q, k, v, a, b, state, ck2, out2)
+    torch.cuda.synchronize()
+    c1, c2, o1, o2 = to_numpy(ck1), to_numpy(ck2), to_numpy(out1), to_numpy(out2)
+    for r in range(R):
+        assert_tiles(c1[r], c2[r], 2, f"chunked vs recurrent ckpt r={r}")
+        assert_tiles(o1[r], o2[r], 1, f"chunked vs recurrent out r={r}")
+    # the in-place form ends where the capture form's last checkpoint is
+    st2 = state.clone()
+    out3 = torch.empty_like(out1)
+    hrs.gdn_span_chunked(q, k, v, a, b, st2, None, out3)
+    torch.cuda.synchronize()
+    assert torch.equal(st2, ck1[:, -1]) and torch.equal(out3, out1)
