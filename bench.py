@@ -174,6 +174,30 @@ def chunked_prefill_row(reps: int = 10, T: int = 1024, R: int = 1):
     if R != 1:
         raise ValueError("the recurrent baseline slices positions of one request")
     res = {}
+    # Also one 64-position chunk at 16 requests (both forms a single launch):
+    # there the recurrent kernel has parallelism enough and the chunked form
+    # pays for its extra matrix work.
+    R16, T16 = 16, 64
+    q16 = torch.nn.functional.normalize(rn(R16, T16, Hk, d), dim=-1).to(torch.bfloat16)
+    k16 = torch.nn.functional.normalize(rn(R16, T16, Hk, d), dim=-1).to(torch.bfloat16)
+    v16 = rn(R16, T16, Hv, d).to(torch.bfloat16)
+    a16 = torch.sigmoid(-rn(R16, T16, Hv)).to(torch.bfloat16)
+    b16 = torch.sigmoid(rn(R16, T16, Hv)).to(torch.bfloat16)
+    st16 = rn(R16, Hv, d, d) * 0.02
+    out16 = torch.empty(R16, T16, Hv, d, device="cuda")
+    for name, fn in (("chunked_r16", lambda: hrs.gdn_span_chunked(q16, k16, v16, a16, b16, st16, None, out16)),
+                     ("recurrent_r16", lambda: hrs.gdn_verify_span(q16, k16, v16, a16, b16, st16, None, out16))):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / reps
+    del q16, k16, v16, a16, b16, st16, out16
     for name, fn in (("chunked", chunked), ("recurrent", recurrent)):
         for _ in range(2):
             fn()
@@ -191,7 +215,10 @@ def chunked_prefill_row(reps: int = 10, T: int = 1024, R: int = 1):
     rel = float((s1 - s2).abs().max() / s2.abs().max())
     return {"n_req": R, "n_pos": T, "chunked_ms": res["chunked"], "recurrent_ms": res["recurrent"],
             "speedup": res["recurrent"] / res["chunked"], "state_rel_diff": rel,
-            "tokens_per_s_per_layer": R * T / (res["chunked"] / 1e3)}
+            "tokens_per_s_per_layer": R * T / (res["chunked"] / 1e3),
+            "one_chunk_16_requests": {"n_req": R16, "n_pos": T16, "chunked_ms": res["chunked_r16"],
+                                      "recurrent_ms": res["recurrent_r16"],
+                                      "speedup": res["recurrent_r16"] / res["chunked_r16"]}}
 
 
 def store_stream_gbs(mib: int = 2048, reps: int = 10) -> float:

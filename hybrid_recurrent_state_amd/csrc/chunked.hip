@@ -20,7 +20,8 @@
 // MI355X design. One block of 4 waves per (request, value head, 16 state
 // rows); each lane keeps 8 columns of one row of S in VGPRs across all
 // chunks (the layout of gdn_verify_span). Per chunk of 64 positions:
-//  1. k, q (times q_scale) and the block's v rows staged in LDS as f32;
+//  1. k, q and the block's v rows staged in LDS as f32 from registers that
+//     were loaded while the previous chunk was processed;
 //  2. K K^T and Q K^T (64 x 64 each) on the matrix cores (bf16 inputs:
 //     32x32x16 MFMA, exact products and f32 accumulation, one 32x32 tile of
 //     each per wave; f32 inputs: vector FMA), and X = K S_0^T, QS = Q S_0^T
@@ -32,9 +33,10 @@
 //     block-row update by all threads, then forward substitution inside the
 //     16 x 16 diagonal block with one lane per state row;
 //  5. outputs O = g QS + P W;
-//  6. states S_t = a_t S_{t-1} + w_t k_t^T (8 FMAs per lane and position, no
-//     dot product), each stored with nontemporal 16-byte stores when
-//     captured.
+//  6. with capture, states S_t = a_t S_{t-1} + w_t k_t^T (8 FMAs per lane
+//     and position, no dot product), each stored with nontemporal 16-byte
+//     stores; without, only the chunk-end state S_C = g S_0 + (G_C W)^T K on
+//     the matrix cores.
 // Positions past the end of the span are padded with a = 1, b = 0, k = q =
 // v = 0 (identity steps) and never streamed.
 #include <hip/hip_runtime.h>
@@ -66,11 +68,14 @@ constexpr int kOffA = kOffS0 + kRows * kSS;       // [C][kAS] K K^T, then A
 constexpr int kOffP = kOffA + kC * kAS;           // [C][kAS] Q K^T, then P = G (Q K^T), lower incl.
 constexpr int kOffX = kOffP + kC * kAS;           // [C][16] X, then Y, then W
 constexpr int kOffQS = kOffX + kC * kRows;        // [C][16] Q S_0^T
-constexpr int kOffGC = kOffQS + kC * kRows;       // [C] unused pad (keeps g_t 16-byte aligned)
+constexpr int kOffGC = kOffQS + kC * kRows;       // [C] G[n-1][t]: decay from position t to the chunk end
 constexpr int kOffG = kOffGC + kC;                // [C] g_t
 constexpr int kOffAv = kOffG + kC;                // [C] a_t
 constexpr int kOffBv = kOffAv + kC;               // [C] b_t
-constexpr int kLdsFloats = kOffBv + kC;
+constexpr int kTS = 20;                           // LDS row stride of the diagonal-block inverses
+constexpr int kOffTb = kOffBv + kC;               // [4][16][kTS] (I + A_bb)^-1 of the 16 x 16 diagonal blocks
+constexpr int kOffRb = kOffTb + 4 * 16 * kTS;     // [16][16] right-hand side of one block
+constexpr int kLdsFloats = kOffRb + 16 * kRows;
 constexpr size_t kLdsBytes = static_cast<size_t>(kLdsFloats) * sizeof(float);
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -96,31 +101,43 @@ struct ChunkArgs {
 // 32 x 32 tiles on the matrix cores, operands read from the bf16 inputs
 // (exact products, f32 accumulation); each wave computes one tile of each.
 // f32 inputs: vector FMA from the staged rows.
+// Eight staged f32 values that are bf16-exact, packed back into bf16 pairs
+// (the upper halves of their bit patterns).
+__device__ __forceinline__ bf16x8 pack_bf16(const float* p) {
+  const u32x4 x = *reinterpret_cast<const u32x4*>(p);
+  const u32x4 y = *reinterpret_cast<const u32x4*>(p + 4);
+  u32x4 r;
+  r.x = (x.x >> 16) | (x.y & 0xFFFF0000u);
+  r.y = (x.z >> 16) | (x.w & 0xFFFF0000u);
+  r.z = (y.x >> 16) | (y.y & 0xFFFF0000u);
+  r.w = (y.z >> 16) | (y.w & 0xFFFF0000u);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// K K^T and Q K^T of the staged chunk into A and P (64 x 64 each; q is
+// staged unscaled). bf16 inputs: 32 x 32 tiles on the matrix cores, operands
+// packed back to bf16 from the staged rows (exact), f32 accumulation; each
+// wave computes one tile of each. f32 inputs: vector FMA.
 template <typename TIn>
-__device__ __forceinline__ void gram(const ChunkArgs& args, float* lds, const TIn* kbase, const TIn* qbase, int n) {
+__device__ __forceinline__ void gram(float* lds) {
   float* const A = lds + kOffA;
   float* const P = lds + kOffP;
+  const float* const K = lds + kOffK;
+  const float* const Q = lds + kOffQ;
   const int tid = threadIdx.x;
   if constexpr (sizeof(TIn) == 2) {
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int ti = wave >> 1, tj = wave & 1;
-    // Rows past the span end read row 0 (in bounds); those results are never
-    // used (b = 0 there, and outputs past the end are not written).
     const int ra = 32 * ti + (lane & 31);
     const int rb = 32 * tj + (lane & 31);
-    const size_t stride = static_cast<size_t>(args.n_kheads) * kDK;
-    const size_t oa = static_cast<size_t>(ra < n ? ra : 0) * stride + 8 * (lane >> 5);
-    const size_t ob = static_cast<size_t>(rb < n ? rb : 0) * stride + 8 * (lane >> 5);
+    const int ko = 8 * (lane >> 5);
     f32x16 acc_k = {}, acc_q = {};
 #pragma unroll
     for (int kk = 0; kk < kDK; kk += 16) {
-      const u32x4 wa = *reinterpret_cast<const u32x4*>(kbase + oa + kk);
-      const u32x4 wq = *reinterpret_cast<const u32x4*>(qbase + oa + kk);
-      const u32x4 wb = *reinterpret_cast<const u32x4*>(kbase + ob + kk);
-      const bf16x8 b8 = __builtin_bit_cast(bf16x8, wb);
-      acc_k = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wa), b8, acc_k, 0, 0, 0);
-      acc_q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wq), b8, acc_q, 0, 0, 0);
+      const bf16x8 b8 = pack_bf16(K + rb * kKS + kk + ko);
+      acc_k = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack_bf16(K + ra * kKS + kk + ko), b8, acc_k, 0, 0, 0);
+      acc_q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack_bf16(Q + ra * kKS + kk + ko), b8, acc_q, 0, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -129,10 +146,7 @@ __device__ __forceinline__ void gram(const ChunkArgs& args, float* lds, const TI
       P[row * kAS + 32 * tj + (lane & 31)] = acc_q[r];
     }
   } else {
-    // 2 x 8 register tiles from the staged k and q (the staged q already
-    // carries q_scale).
-    const float* K = lds + kOffK;
-    const float* Q = lds + kOffQ;
+    // 2 x 8 register tiles.
     for (int tile = tid; tile < (kC / 2) * (kC / 8); tile += kThreads) {
       const int t0 = (tile / (kC / 8)) * 2;
       const int j0 = (tile % (kC / 8)) * 8;
@@ -165,6 +179,110 @@ __device__ __forceinline__ void gram(const ChunkArgs& args, float* lds, const TI
   }
 }
 
+// One chunk's inputs as loaded from memory (raw bits), so the loads of chunk
+// c + 1 can be issued before chunk c is processed and consumed afterwards.
+template <typename TIn> struct Raw8;
+template <> struct Raw8<uint16_t> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ void widen(float* o) const {
+    o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+    o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+  }
+};
+template <> struct Raw8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = f32x4{0.f, 0.f, 0.f, 0.f}; b = a; }
+  __device__ __forceinline__ void widen(float* o) const {
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+};
+
+constexpr int kKQItems = kC * (kDK / 8) / kThreads;   // k (and q) 8-element items per thread (4)
+
+template <typename TIn>
+struct ChunkRegs {
+  Raw8<TIn> k[kKQItems], q[kKQItems], v;
+  float a, b;
+};
+
+// Issue the loads of the chunk starting at c0 (n positions) into registers.
+template <typename TIn>
+__device__ __forceinline__ void fetch_chunk(const ChunkArgs& args, ChunkRegs<TIn>& rg, int r, int h, int g, int row0,
+                                            int c0, int n) {
+  const int T = args.n_pos;
+  const int tid = threadIdx.x;
+  const TIn* qg = static_cast<const TIn*>(args.q);
+  const TIn* kg = static_cast<const TIn*>(args.k);
+  const TIn* vg = static_cast<const TIn*>(args.v);
+#pragma unroll
+  for (int i = 0; i < kKQItems; ++i) {
+    const int e = tid + i * kThreads;
+    const int t = e / (kDK / 8);
+    const int j = (e % (kDK / 8)) * 8;
+    if (t < n) {
+      const size_t src = ((static_cast<size_t>(r) * T + c0 + t) * args.n_kheads + g) * kDK + j;
+      rg.k[i].load(kg + src);
+      rg.q[i].load(qg + src);
+    } else {
+      rg.k[i].zero();
+      rg.q[i].zero();
+    }
+  }
+  {
+    const int t = tid / (kRows / 8);
+    const int i0 = (tid % (kRows / 8)) * 8;
+    if (tid < kC * (kRows / 8) && t < n)
+      rg.v.load(vg + ((static_cast<size_t>(r) * T + c0 + t) * args.n_vheads + h) * kDK + row0 + i0);
+    else
+      rg.v.zero();
+  }
+  rg.a = 1.0f;
+  rg.b = 0.0f;
+  if (tid < n) {
+    const size_t src = (static_cast<size_t>(r) * T + c0 + tid) * args.n_vheads + h;
+    rg.a = load_elem<TIn>(static_cast<const TIn*>(args.a), src);
+    rg.b = load_elem<TIn>(static_cast<const TIn*>(args.b), src);
+  }
+}
+
+// Write a fetched chunk into the staging buffers (f32; q unscaled).
+template <typename TIn>
+__device__ __forceinline__ void stage_chunk(float* lds, const ChunkRegs<TIn>& rg) {
+  const int tid = threadIdx.x;
+  float* const Kl = lds + kOffK;
+  float* const Ql = lds + kOffQ;
+#pragma unroll
+  for (int i = 0; i < kKQItems; ++i) {
+    const int e = tid + i * kThreads;
+    const int t = e / (kDK / 8);
+    const int j = (e % (kDK / 8)) * 8;
+    float x[8];
+    rg.k[i].widen(x);
+    *reinterpret_cast<f32x4*>(Kl + t * kKS + j) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(Kl + t * kKS + j + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    rg.q[i].widen(x);
+    *reinterpret_cast<f32x4*>(Ql + t * kKS + j) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(Ql + t * kKS + j + 4) = f32x4{x[4], x[5], x[6], x[7]};
+  }
+  if (tid < kC * (kRows / 8)) {
+    float x[8];
+    rg.v.widen(x);
+    float* const lv = lds + kOffV + (tid / (kRows / 8)) * kRows + (tid % (kRows / 8)) * 8;
+    *reinterpret_cast<f32x4*>(lv) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(lv + 4) = f32x4{x[4], x[5], x[6], x[7]};
+  }
+  if (tid < kC) {
+    lds[kOffAv + tid] = rg.a;
+    lds[kOffBv + tid] = rg.b;
+  }
+}
+
 template <typename TIn, bool CAPTURE>
 __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs args) {
   extern __shared__ float lds[];
@@ -182,11 +300,6 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
   const int row_blk = (tid >> 6) * (64 / kLPR) + lane / kLPR;   // 0..15
   const size_t head_elems = static_cast<size_t>(kDK) * kDK;
   const size_t pos_stride = static_cast<size_t>(Hv) * head_elems;
-  const TIn* qg = static_cast<const TIn*>(args.q);
-  const TIn* kg = static_cast<const TIn*>(args.k);
-  const TIn* vg = static_cast<const TIn*>(args.v);
-  const TIn* ag = static_cast<const TIn*>(args.a);
-  const TIn* bg = static_cast<const TIn*>(args.b);
   float* const Kl = lds + kOffK;
   float* const Ql = lds + kOffQ;
   float* const Vl = lds + kOffV;
@@ -195,12 +308,14 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
   float* const P = lds + kOffP;
   float* const X = lds + kOffX;
   float* const QS = lds + kOffQS;
+  float* const GC = lds + kOffGC;
+  float* const Tb = lds + kOffTb;
+  float* const Rb = lds + kOffRb;
   float* const Gv = lds + kOffG;
   float* const Av = lds + kOffAv;
   float* const Bv = lds + kOffBv;
-  // Q K^T from the raw bf16 inputs lacks q_scale; the f32 path forms it from
-  // the staged (scaled) q.
-  const float p_scale = sizeof(TIn) == 2 ? args.q_scale : 1.0f;
+  // q is staged unscaled; q_scale enters P and QS.
+  const float p_scale = args.q_scale;
 
   float* const state_row = args.state + (static_cast<size_t>(r) * Hv + h) * head_elems +
                            static_cast<size_t>(row0 + row_blk) * kDK;
@@ -214,48 +329,22 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
 #pragma unroll
   for (int m = 0; m < kNCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(state_row + 4 * (li + kLPR * m));
 
+  ChunkRegs<TIn> rg;
+  fetch_chunk<TIn>(args, rg, r, h, g, row0, 0, min(kC, T));
   for (int c0 = 0; c0 < T; c0 += kC) {
     const int n = min(kC, T - c0);
     __syncthreads();   // the previous chunk's LDS reads are done
-    // 1. Stage k, q (scaled), the block's v rows and the gates; the current
-    //    state rows go to S0.
-    for (int e = tid; e < kC * (kDK / 8); e += kThreads) {
-      const int t = e / (kDK / 8);
-      const int j = (e % (kDK / 8)) * 8;
-      float kv[8] = {}, qv[8] = {};
-      if (t < n) {
-        const size_t src = ((static_cast<size_t>(r) * T + c0 + t) * args.n_kheads + g) * kDK + j;
-        load8<TIn>(kg + src, kv);
-        load8<TIn>(qg + src, qv);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        Kl[t * kKS + j + i] = kv[i];
-        Ql[t * kKS + j + i] = qv[i] * args.q_scale;
-      }
-    }
-    for (int e = tid; e < kC * (kRows / 8); e += kThreads) {
-      const int t = e / (kRows / 8);
-      const int i0 = (e % (kRows / 8)) * 8;
-      float vv[8] = {};
-      if (t < n) load8<TIn>(vg + ((static_cast<size_t>(r) * T + c0 + t) * Hv + h) * kDK + row0 + i0, vv);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Vl[t * kRows + i0 + i] = vv[i];
-    }
-    if (tid < kC) {
-      const size_t src = (static_cast<size_t>(r) * T + c0 + tid) * Hv + h;
-      Av[tid] = tid < n ? load_elem<TIn>(ag, src) : 1.0f;
-      Bv[tid] = tid < n ? load_elem<TIn>(bg, src) : 0.0f;
-    }
+    // 1. Stage the fetched chunk (k, q unscaled, the block's v rows, gates)
+    //    and the current state rows, then fetch the next chunk: its loads
+    //    complete while this one is processed.
+    stage_chunk<TIn>(lds, rg);
 #pragma unroll
     for (int m = 0; m < kNCH; ++m) *reinterpret_cast<f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m)) = s[m];
+    if (c0 + kC < T) fetch_chunk<TIn>(args, rg, r, h, g, row0, c0 + kC, min(kC, T - c0 - kC));
     __syncthreads();
     // 2. K K^T and Q K^T (matrix cores for bf16), X = K S_0^T and
-    //    QS = Q S_0^T (vector FMA, 2 x 2 register tiles per product).
-    {
-      const size_t base = ((static_cast<size_t>(r) * T + c0) * args.n_kheads + g) * kDK;
-      gram<TIn>(args, lds, kg + base, qg + base, n);
-    }
+    //    QS = Q S_0^T.
+    gram<TIn>(lds);
     {
       // X and QS on the matrix cores (16x16x4 f32 MFMA, exact f32 products):
       // wave w takes positions [16 w, 16 w + 16) for all 16 state rows. In
@@ -304,36 +393,66 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
       // Branch-free: the running product stays 1 until j < t, and entries
       // with j > t (unused) are scaled by 1 as well.
       float gp = 1.0f;   // G[t][j] for the current j
+      const bool last = t == n - 1;   // this row's products are the decays to the chunk end
 #pragma unroll
       for (int j = kC - 4; j >= 0; j -= 4) {
         const f32x4 kv = *reinterpret_cast<const f32x4*>(arow + j);
         const f32x4 qv = *reinterpret_cast<const f32x4*>(prow + j);
-        f32x4 ka, qa;
+        f32x4 ka, qa, gc;
 #pragma unroll
         for (int u = 3; u >= 0; --u) {
           const int jj = j + u;
           if (jj + 1 < kC) gp *= (jj < t) ? av[jj + 1] : 1.0f;
           ka[u] = bt * gp * kv[u];
           qa[u] = (p_scale * gp) * qv[u];
+          gc[u] = gp;
         }
         *reinterpret_cast<f32x4*>(arow + j) = ka;
         *reinterpret_cast<f32x4*>(prow + j) = qa;
+        if (last) *reinterpret_cast<f32x4*>(GC + j) = gc;
       }
       Gv[t] = av[0] * gp;   // g_t = a_0 G[t][0]
     }
     __syncthreads();
-    // 4. Y = b (V - g X) in place of X, then (I + A) W = Y by 16-position
-    //    blocks, W in place of Y.
-    for (int e = tid; e < kC * kRows; e += kThreads) {
-      const int t = e / kRows;
-      X[e] = Bv[t] * __builtin_fmaf(-Gv[t], X[e], Vl[e]);
+    // 4. Y = b (V - g X) in place of X (waves 1-3) while wave 0 inverts the
+    //    four 16 x 16 diagonal blocks of I + A (one lane per column of one
+    //    block, forward substitution in registers); then (I + A) W = Y block
+    //    by block: R = Y_b - A_b,<b W_<b, W_b = (I + A_bb)^-1 R, W in place of Y.
+    if (tid < 64) {
+      const int bi = tid >> 4;
+      const int col = tid & 15;
+      const float* ab = A + (16 * bi) * kAS + 16 * bi;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float r[16];
+#pragma unroll
+        for (int j = 0; j < 16; j += 4) {
+          const f32x4 v4 = *reinterpret_cast<const f32x4*>(ab + i * kAS + j);
+          r[j] = v4.x; r[j + 1] = v4.y; r[j + 2] = v4.z; r[j + 3] = v4.w;
+        }
+        float acc0 = (i == col) ? 1.0f : 0.0f, acc1 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < i; ++j) {
+          if (j & 1) acc1 = __builtin_fmaf(-r[j], x[j], acc1);
+          else acc0 = __builtin_fmaf(-r[j], x[j], acc0);
+        }
+        x[i] = acc0 + acc1;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Tb[(bi * 16 + i) * kTS + col] = x[i];
+    } else {
+      for (int e = tid - 64; e < kC * kRows; e += kThreads - 64) {
+        const int t = e / kRows;
+        X[e] = Bv[t] * __builtin_fmaf(-Gv[t], X[e], Vl[e]);
+      }
     }
     __syncthreads();
     for (int blk = 0; blk < kC / 16; ++blk) {
-      if (blk > 0) {
-        // Subtract the contribution of the solved positions [0, 16 blk).
-        const int t = 16 * blk + (tid >> 4);
-        const int col = tid & 15;
+      const int i = tid >> 4;          // row inside the block
+      const int col = tid & 15;
+      const int t = 16 * blk + i;
+      {
         float acc0 = X[t * kRows + col], acc1 = 0.0f;
         for (int j = 0; j < 16 * blk; j += 4) {
           const f32x4 av4 = *reinterpret_cast<const f32x4*>(A + t * kAS + j);
@@ -342,26 +461,21 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
           acc0 = __builtin_fmaf(-av4.z, X[(j + 2) * kRows + col], acc0);
           acc1 = __builtin_fmaf(-av4.w, X[(j + 3) * kRows + col], acc1);
         }
-        X[t * kRows + col] = acc0 + acc1;
-        __syncthreads();
+        Rb[i * kRows + col] = acc0 + acc1;
       }
-      if (tid < kRows) {
-        // Forward substitution inside the diagonal block, one lane per column.
-        const int col = tid;
-        const int base = 16 * blk;
-        float wv[16];
+      __syncthreads();
+      {
+        const float* trow = Tb + (blk * 16 + i) * kTS;
+        float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float acc0 = X[(base + i) * kRows + col], acc1 = 0.0f;
-#pragma unroll
-          for (int j = 0; j < i; ++j) {
-            if (j & 1) acc1 = __builtin_fmaf(-A[(base + i) * kAS + base + j], wv[j], acc1);
-            else acc0 = __builtin_fmaf(-A[(base + i) * kAS + base + j], wv[j], acc0);
-          }
-          wv[i] = acc0 + acc1;
+        for (int j = 0; j < 16; j += 4) {
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(trow + j);
+          acc0 = __builtin_fmaf(t4.x, Rb[j * kRows + col], acc0);
+          acc1 = __builtin_fmaf(t4.y, Rb[(j + 1) * kRows + col], acc1);
+          acc0 = __builtin_fmaf(t4.z, Rb[(j + 2) * kRows + col], acc0);
+          acc1 = __builtin_fmaf(t4.w, Rb[(j + 3) * kRows + col], acc1);
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) X[(base + i) * kRows + col] = wv[i];
+        X[t * kRows + col] = acc0 + acc1;
       }
       __syncthreads();
     }
@@ -372,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
       const int c4 = (tid & 3) * 4;
       if (t < n) {
         const f32x4 qs = *reinterpret_cast<const f32x4*>(QS + t * kRows + c4);
-        const float gt = Gv[t];
+        const float gt = Gv[t] * args.q_scale;
         f32x4 acc = {gt * qs.x, gt * qs.y, gt * qs.z, gt * qs.w};
         for (int j = 0; j <= t; j += 4) {
           const f32x4 p4 = *reinterpret_cast<const f32x4*>(P + t * kAS + j);
@@ -391,31 +505,31 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
         *reinterpret_cast<f32x4*>(out_h + static_cast<size_t>(c0 + t) * Hv * kDK + c4) = acc;
       }
     }
-    // 6. States: S_t = a_t S_{t-1} + w_t k_t^T (checkpoint each with capture),
-    //    8 positions at a time so their LDS reads are issued together.
-    for (int t0 = 0; t0 < n; t0 += 8) {
-      float at[8], wt[8];
-      f32x4 kk[8][kNCH];
+    if constexpr (CAPTURE) {
+      // 6. States: S_t = a_t S_{t-1} + w_t k_t^T, each checkpointed; 8
+      //    positions at a time so their LDS reads are issued together.
+      for (int t0 = 0; t0 < n; t0 += 8) {
+        float at[8], wt[8];
+        f32x4 kk[8][kNCH];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        at[u] = Av[t0 + u];
-        wt[u] = X[(t0 + u) * kRows + row_blk];
+        for (int u = 0; u < 8; ++u) {
+          at[u] = Av[t0 + u];
+          wt[u] = X[(t0 + u) * kRows + row_blk];
 #pragma unroll
-        for (int m = 0; m < kNCH; ++m)
-          kk[u][m] = *reinterpret_cast<const f32x4*>(Kl + (t0 + u) * kKS + 4 * (li + kLPR * m));
-      }
-      const int un = min(8, n - t0);
+          for (int m = 0; m < kNCH; ++m)
+            kk[u][m] = *reinterpret_cast<const f32x4*>(Kl + (t0 + u) * kKS + 4 * (li + kLPR * m));
+        }
+        const int un = min(8, n - t0);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (un == 8 || u < un) {
+        for (int u = 0; u < 8; ++u) {
+          if (un == 8 || u < un) {
 #pragma unroll
-          for (int m = 0; m < kNCH; ++m) {
-            s[m].x = __builtin_fmaf(wt[u], kk[u][m].x, at[u] * s[m].x);
-            s[m].y = __builtin_fmaf(wt[u], kk[u][m].y, at[u] * s[m].y);
-            s[m].z = __builtin_fmaf(wt[u], kk[u][m].z, at[u] * s[m].z);
-            s[m].w = __builtin_fmaf(wt[u], kk[u][m].w, at[u] * s[m].w);
-          }
-          if (CAPTURE) {
+            for (int m = 0; m < kNCH; ++m) {
+              s[m].x = __builtin_fmaf(wt[u], kk[u][m].x, at[u] * s[m].x);
+              s[m].y = __builtin_fmaf(wt[u], kk[u][m].y, at[u] * s[m].y);
+              s[m].z = __builtin_fmaf(wt[u], kk[u][m].z, at[u] * s[m].z);
+              s[m].w = __builtin_fmaf(wt[u], kk[u][m].w, at[u] * s[m].w);
+            }
             float* dst = ckpt_row0 + static_cast<size_t>(c0 + t0 + u) * pos_stride;
 #pragma unroll
             for (int m = 0; m < kNCH; ++m)
@@ -423,6 +537,38 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
           }
         }
       }
+    } else {
+      // 6. State at the chunk end only: S_C = g_{n-1} S_0 + sum_t G[n-1][t]
+      //    w_t k_t^T on the matrix cores (16x16x4 f32 MFMA; wave w takes
+      //    columns [32 w, 32 w + 32)), written over S_0 and read back into
+      //    the lanes' registers.
+      const int wave = tid >> 6;
+      const int lane = tid & 63;
+      const int i = lane & 15;
+      const int kq = lane >> 4;
+      f32x4 d0 = {}, d1 = {};
+#pragma unroll
+      for (int tb = 0; tb < kC; tb += 16) {
+        const int tq = tb + 4 * kq;
+        const f32x4 gc = *reinterpret_cast<const f32x4*>(GC + tq);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float wv = gc[u] * X[(tq + u) * kRows + i];
+          const float* krow = Kl + (tq + u) * kKS + 32 * wave + (lane & 15);
+          d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv, krow[0], d0, 0, 0, 0);
+          d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv, krow[16], d1, 0, 0, 0);
+        }
+      }
+      const float gn = Gv[n - 1];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float* e0 = S0 + (4 * kq + u) * kSS + 32 * wave + (lane & 15);
+        e0[0] = __builtin_fmaf(gn, e0[0], d0[u]);
+        e0[16] = __builtin_fmaf(gn, e0[16], d1[u]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < kNCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m));
     }
   }
   if (!CAPTURE) {
