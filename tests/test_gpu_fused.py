@@ -165,3 +165,21 @@ def test_fused_step_equals_layer_calls(hrs, tree):
                                                   w.d_k, w.d_v, parent=pr, q_scale=0.25)
                     assert_tiles(to_numpy(ck[l, r]), ock, 2, f"step ckpt l={l} r={r}")
                     assert_tiles(to_numpy(bufs.out[l, r]), oout, 1, f"step out l={l} r={r}")
+
+
+def test_layer_persistent_multi_window(hrs):
+    """8 requests (persistent producer/consumer launch) over 40 positions:
+    two windows per unit, fused staging by the producer waves; two requests
+    against the oracle, every request against its own single-request launch."""
+    import torch
+    w = layer_workload(QWEN_LAYER_CHAIN, n_req=8, n_pos=40)
+    units, wc, ck, out = run_layer(hrs, w, q_scale=0.3)
+    check_layer(w, [units[1], units[6]], wc, ck[[1, 6]], out[[1, 6]], q_scale=0.3, what="fused persistent T=40")
+    for r in range(w.n_req):
+        u = units[r]
+        x, cs, a, b, state = (to_torch(t[None]) for t in (u.x, u.conv_state, u.a, u.b, u.state))
+        ck1 = torch.empty((1, w.n_pos, w.n_vheads, w.d_v, w.d_k), device="cuda")
+        out1 = torch.empty((1, w.n_pos, w.n_vheads, w.d_v), device="cuda")
+        hrs.gdn_layer_verify_span(x, to_torch(wc), cs, a, b, ck1, out1, w.n_kheads, w.d_k, state=state, q_scale=0.3)
+        torch.cuda.synchronize()
+        assert np.array_equal(ck[r], to_numpy(ck1)[0]) and np.array_equal(out[r], to_numpy(out1)[0]), r

@@ -460,3 +460,49 @@ def test_ring_set_get_vs_oracle(hrs, dtype):
     exp_ring = oring.ring_set(ring0, packed, runs)
     assert np.array_equal(to_numpy(ring), exp_ring)
     assert np.array_equal(to_numpy(out), oring.ring_get(exp_ring, np.zeros_like(packed), runs))
+
+
+def test_gdn_persistent_multi_window_chain(hrs):
+    """8 requests of the Qwen shape (one 12-wave block per CU walking 1024
+    32-row units) over 40 positions (two LDS windows per unit): the producer
+    waves stage window 2 and the next unit while the consumers run; sampled
+    requests against the oracle, the rest against the 4-wave launch of the
+    same requests one at a time."""
+    import torch
+    w = scaled(QWEN_LAYER_CHAIN, n_req=8, n_pos=40)
+    units = [gen_unit(w, 0, r) for r in range(w.n_req)]
+    say("persistent chain R=8 T=40")
+    ck, out, _ = gpu_gdn(hrs, units)
+    check_gdn_vs_oracle([units[0], units[5]], ck[[0, 5]], out[[0, 5]], what="persistent T=40")
+    for r in range(w.n_req):
+        ck1, out1, _ = gpu_gdn(hrs, [units[r]])
+        assert np.array_equal(ck[r], ck1[0]) and np.array_equal(out[r], out1[0]), r
+
+
+def test_gdn_persistent_zero_copy_invalid_node(hrs):
+    """Zero-copy start on the persistent launch: an out-of-range index writes
+    nothing for that request and is counted; the others equal the copied start."""
+    import torch
+    w = scaled(QWEN_LAYER_CHAIN, n_req=8, n_pos=17)
+    units = [gen_unit(w, 0, r) for r in range(w.n_req)]
+    st = lambda name: to_torch(np.stack([getattr(u, name) for u in units]))
+    R, T, Hv, d = 8, 17, 32, 128
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    prev = torch.randn((R, 5, Hv, d, d), device="cuda", generator=gen) * 0.02
+    node = torch.tensor([4, 0, 2, 9, 1, 3, 4, -1], dtype=torch.int32, device="cuda")   # requests 3 and 7 invalid
+    status = torch.full((4,), -1, dtype=torch.int32, device="cuda")
+    ckpt = torch.full((R, T, Hv, d, d), float("nan"), device="cuda")
+    out = torch.full((R, T, Hv, d), float("nan"), device="cuda")
+    hrs.gdn_verify_span_from(prev, node, st("q"), st("k"), st("v"), st("a"), st("b"), ckpt, out, status=status)
+    idx = [4, 0, 2, 0, 1, 3, 4, 0]
+    state = torch.stack([prev[r, idx[r]] for r in range(R)]).contiguous()
+    ck_ref = torch.empty_like(ckpt)
+    out_ref = torch.empty_like(out)
+    hrs.gdn_verify_span(st("q"), st("k"), st("v"), st("a"), st("b"), state, ck_ref, out_ref)
+    torch.cuda.synchronize()
+    assert int(to_numpy(status)[0]) == 2
+    for r in range(R):
+        if r in (3, 7):
+            assert torch.isnan(ckpt[r]).all() and torch.isnan(out[r]).all(), r
+        else:
+            assert torch.equal(ckpt[r], ck_ref[r]) and torch.equal(out[r], out_ref[r]), r
