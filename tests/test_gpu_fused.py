@@ -183,3 +183,11 @@ def test_layer_persistent_multi_window(hrs):
         hrs.gdn_layer_verify_span(x, to_torch(wc), cs, a, b, ck1, out1, w.n_kheads, w.d_k, state=state, q_scale=0.3)
         torch.cuda.synchronize()
         assert np.array_equal(ck[r], to_numpy(ck1)[0]) and np.array_equal(out[r], to_numpy(out1)[0]), r
+
+
+def test_layer_persistent_dk64(hrs):
+    """Fused layer with d_k = d_v = 64 (q/k rows are 4-lane DPP groups) on the
+    persistent launch: 4 requests x 32 value heads x 2 row blocks."""
+    w = layer_workload(QWEN_LAYER_CHAIN, n_req=4, n_pos=20, d_k=64, d_v=64)
+    units, wc, ck, out = run_layer(hrs, w, q_scale=0.125)
+    check_layer(w, units, wc, ck, out, q_scale=0.125, what="fused persistent dk64")

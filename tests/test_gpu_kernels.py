@@ -506,3 +506,13 @@ def test_gdn_persistent_zero_copy_invalid_node(hrs):
             assert torch.isnan(ckpt[r]).all() and torch.isnan(out[r]).all(), r
         else:
             assert torch.equal(ckpt[r], ck_ref[r]) and torch.equal(out[r], out_ref[r]), r
+
+
+def test_gdn_persistent_dk64_bf16(hrs):
+    """d_k = d_v = 64 on the persistent producer/consumer launch (4 requests x
+    32 value heads x 2 row blocks = 256 units of 32 rows), bf16."""
+    w = scaled(QWEN_LAYER_CHAIN, n_req=4, n_pos=20, d_k=64, d_v=64)
+    units = [gen_unit(w, 0, r) for r in range(w.n_req)]
+    say("persistent dk64 R=4 T=20")
+    ck, out, _ = gpu_gdn(hrs, units, q_scale=0.125)
+    check_gdn_vs_oracle(units, ck, out, q_scale=0.125, what="persistent dk64")
