@@ -21,18 +21,23 @@
 //    read again until rollback (normal stores measured ~12% slower).
 //  * Work order: units are numbered row block fastest, then head, then
 //    request, and a block walks units W, W + gridDim.x, ... When there are at
-//    least as many 32-row units as compute units, the grid is one 8-wave block
-//    per CU: all CUs then advance through the positions together and each
-//    position's checkpoint region (2 MiB per request) is written as one
-//    contiguous sweep. Measured on the 16-request Qwen shape: 6.0 TB/s versus
-//    5.1 TB/s for one block per unit, and 75% of HBM peak, at the plain
-//    store-stream ceiling. Smaller problems use one 4-wave block per 16-row
-//    unit to spread over more CUs.
+//    least as many 32-row units as compute units, the grid is one block per
+//    CU with 8 row-owning waves: all CUs then advance through the positions
+//    together and each position's checkpoint region (2 MiB per request) is
+//    written as one contiguous sweep (5.1 TB/s for one block per unit on the
+//    16-request Qwen shape, 5.9 TB/s this way: 73% of HBM peak and 85% of a
+//    plain device store stream on the same GPU). Smaller problems use one
+//    4-wave block per 16-row unit to spread over more CUs.
 //  * The two row dot products (S k and S q) are butterfly sums over the 16
 //    lanes with DPP moves; the association order is fixed, so the arithmetic
 //    of a position never depends on span length, topology or launch shape.
 //  * k, q (times q_scale), v rows, a and b of a window of positions are
-//    staged once per unit into LDS as f32.
+//    staged into LDS as f32. In the capturing chain kernel 4 extra producer
+//    waves stage the next window (and the next unit's initial state rows)
+//    into a double buffer while the row-owning waves run the current one:
+//    the vector-memory counter retires loads and stores in order, so a wave
+//    that staged its own inputs would wait for all its outstanding
+//    checkpoint stores first; split by role, the storing waves load nothing.
 //  * Tree mode: the host turns each request's parent array into a stash
 //    schedule. A position with a child that is not the next position saves
 //    its state rows into an LDS slot (each lane its own 32 bytes, addressed
@@ -161,7 +166,7 @@ __device__ __forceinline__ Unit unit_of(const GdnArgs& args, int W, int rpb) {
 // Staging, plain inputs: k and q (times q_scale) of key head g and the unit's
 // v rows for positions [t0, t0 + tn), 8 elements per item, by the NTH staging
 // threads (p is the thread's index among them). q/k and v items share one
-// index space, so a thread's loads for all its items are issued together.
+// index space, so the staging takes as few rounds of loads as possible.
 template <int DK, int NTH, int RPB, int POS_FLOATS, typename TIn>
 __device__ __forceinline__ void stage_plain(const GdnArgs& args, float* buf, const Unit& u, int t0, int tn, int p) {
   const int T = args.n_pos;
