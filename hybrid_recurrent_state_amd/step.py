@@ -15,7 +15,7 @@ Buffers are allocated once by ``StepBuffers`` (device memory through torch)
 and every descriptor and pointer of the step is computed once by
 ``VerifyStep``, so launching a step is a fixed sequence of C calls.
 
-Variants with the same acceptance and results: ``ZeroCopyVerifyStep`` starts
+Variants: ``ZeroCopyVerifyStep`` starts
 each span from the previous span's accepted checkpoint in place (no rollback
 copy, conv state rebuilt from the accepted path) and ``FusedVerifyStep`` adds
 one fused kernel per layer (conv, SiLU, q/k/v split, q/k L2 norm and the
