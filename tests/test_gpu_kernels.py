@@ -516,3 +516,21 @@ def test_gdn_persistent_dk64_bf16(hrs):
     say("persistent dk64 R=4 T=20")
     ck, out, _ = gpu_gdn(hrs, units, q_scale=0.125)
     check_gdn_vs_oracle(units, ck, out, q_scale=0.125, what="persistent dk64")
+
+
+def test_gdn_span_prefix_equals_shorter_span(hrs):
+    """The first j+1 checkpoints and outputs of a 17-position span equal a
+    (j+1)-position span over the same inputs, bit for bit (the arithmetic of a
+    position does not depend on the span length or the launch shape)."""
+    w = scaled(QWEN_LAYER_CHAIN, n_req=8)
+    units = [gen_unit(w, 0, r) for r in range(w.n_req)]
+    ck, out, _ = gpu_gdn(hrs, units)
+    for j in (0, 4, 15):
+        short = [scaled_unit(u, j + 1) for u in units]
+        cks, outs, _ = gpu_gdn(hrs, short)
+        assert np.array_equal(ck[:, :j + 1], cks) and np.array_equal(out[:, :j + 1], outs), j
+
+
+def scaled_unit(u, n):
+    import dataclasses
+    return dataclasses.replace(u, q=u.q[:n], k=u.k[:n], v=u.v[:n], a=u.a[:n], b=u.b[:n], x=u.x[:n])

@@ -114,3 +114,23 @@ def test_generator_plant_is_recovered(wl):
         if wl.logits_distinct:
             for t in range(f.shape[0]):
                 assert np.unique(f[t]).size == f.shape[1]
+
+
+def test_generator_tree_constraints():
+    """Draft trees of the tree workload: root first, parents before children,
+    depth at most 8, at most 3 children per node, sibling tokens distinct."""
+    from synth import gen_tree_parent
+    w = scaled(QWEN_STACK_TREE, vocab=4096)
+    for req in range(20):
+        par = gen_tree_parent(w, req)
+        assert par[0] == -1 and all(0 <= par[i] < i for i in range(1, w.n_pos))
+        depth = np.zeros(w.n_pos, dtype=int)
+        for i in range(1, w.n_pos):
+            depth[i] = depth[par[i]] + 1
+        assert depth.max() <= w.tree_max_depth
+        kids = np.bincount(par[1:], minlength=w.n_pos)
+        assert kids.max() <= w.tree_max_children
+        ai = gen_accept(w, req, with_logits=False)
+        for p in range(w.n_pos):
+            sib = ai.tokens[1:][par[1:] == p]
+            assert len(set(sib.tolist())) == len(sib)
