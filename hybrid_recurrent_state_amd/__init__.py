@@ -49,6 +49,10 @@ class GdnDesc(ctypes.Structure):
                 ("topo", _i32), ("parent", ctypes.POINTER(_i32))]
 
 
+class ChunkedDesc(ctypes.Structure):
+    _fields_ = [("gdn", GdnDesc), ("log_gates", _i32), ("out_dtype", _i32)]
+
+
 class GdnLayerDesc(ctypes.Structure):
     _fields_ = [("gdn", GdnDesc), ("conv_width", _i32), ("silu", _i32), ("l2_eps", ctypes.c_float)]
 
@@ -94,7 +98,7 @@ _SIGNATURES = {
     "gdn_verify_span_timed": (_i32, [ctypes.POINTER(GdnDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "gdn_verify_span_from": (_i32, [ctypes.POINTER(GdnDesc), ctypes.POINTER(SpanSource), _p, _p, _p, _p, _p, _p,
                                     _p, _p, _p]),
-    "gdn_span_chunked": (_i32, [ctypes.POINTER(GdnDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "gdn_span_chunked": (_i32, [ctypes.POINTER(ChunkedDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "gdn_layer_verify_span": (_i32, [ctypes.POINTER(GdnLayerDesc), _p, _p, _p, _p, _p, _p,
                                      ctypes.POINTER(SpanSource), _p, _p, _p, _p]),
     "conv1d_verify_span_nocapture": (_i32, [ctypes.POINTER(ConvDesc), _p, _p, _p, _p, _p]),
@@ -266,13 +270,14 @@ def gdn_verify_span_from(src_ckpt, src_node, q, k, v, a, b, ckpt, out, parent=No
     _check(st, "gdn_verify_span_from")
 
 
-def gdn_span_chunked(q, k, v, a, b, state, ckpt, out, q_scale: float = 1.0, stream=None):
+def gdn_span_chunked(q, k, v, a, b, state, ckpt, out, q_scale: float = 1.0, log_gates: bool = False, stream=None):
     """Chunked (64-position) gated delta rule over a long chain span: same
     arguments as gdn_verify_span without a parent; ckpt None updates state
-    in place."""
+    in place. log_gates: `a` holds log decays. out may be f32 or bf16."""
     R, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
-    d = GdnDesc(R, T, Hk, Hv, dk, dv, _dtype_code(q), float(q_scale), HRS_CHAIN, None)
+    g = GdnDesc(R, T, Hk, Hv, dk, dv, _dtype_code(q), float(q_scale), HRS_CHAIN, None)
+    d = ChunkedDesc(g, int(bool(log_gates)), _dtype_code(out))
     st = lib.gdn_span_chunked(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(state), _ptr(ckpt),
                               _ptr(out), _stream(stream))
     _check(st, "gdn_span_chunked")

@@ -89,7 +89,7 @@ struct ChunkArgs {
   const void* b;
   float* state;
   float* ckpt;
-  float* out;
+  void* out;       // float or bf16 (OUTBF)
   int32_t n_pos;
   int32_t n_kheads;
   int32_t n_vheads;
@@ -212,7 +212,7 @@ struct ChunkRegs {
 };
 
 // Issue the loads of the chunk starting at c0 (n positions) into registers.
-template <typename TIn>
+template <typename TIn, bool LOGG>
 __device__ __forceinline__ void fetch_chunk(const ChunkArgs& args, ChunkRegs<TIn>& rg, int r, int h, int g, int row0,
                                             int c0, int n) {
   const int T = args.n_pos;
@@ -246,14 +246,14 @@ __device__ __forceinline__ void fetch_chunk(const ChunkArgs& args, ChunkRegs<TIn
   rg.b = 0.0f;
   if (tid < n) {
     const size_t src = (static_cast<size_t>(r) * T + c0 + tid) * args.n_vheads + h;
-    rg.a = load_elem<TIn>(static_cast<const TIn*>(args.a), src);
+    rg.a = load_elem<TIn>(static_cast<const TIn*>(args.a), src);   // the log decay with log gates
     rg.b = load_elem<TIn>(static_cast<const TIn*>(args.b), src);
   }
 }
 
 // Write a fetched chunk into the staging buffers (f32; q unscaled).
-template <typename TIn>
-__device__ __forceinline__ void stage_chunk(float* lds, const ChunkRegs<TIn>& rg) {
+template <typename TIn, bool LOGG>
+__device__ __forceinline__ void stage_chunk(float* lds, const ChunkRegs<TIn>& rg, int n) {
   const int tid = threadIdx.x;
   float* const Kl = lds + kOffK;
   float* const Ql = lds + kOffQ;
@@ -278,12 +278,21 @@ __device__ __forceinline__ void stage_chunk(float* lds, const ChunkRegs<TIn>& rg
     *reinterpret_cast<f32x4*>(lv + 4) = f32x4{x[4], x[5], x[6], x[7]};
   }
   if (tid < kC) {
-    lds[kOffAv + tid] = rg.a;
+    // Log-space gates: a_t = exp(g_t) (positions past the span end keep a = 1).
+    lds[kOffAv + tid] = (LOGG && tid < n) ? expf(rg.a) : rg.a;
     lds[kOffBv + tid] = rg.b;
   }
 }
 
-template <typename TIn, bool CAPTURE>
+// One output rounded to the nearest bf16 (ties to even; NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x0040u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// LOGG: `a` holds log decays; OUTBF: outputs are written as bf16.
+template <typename TIn, bool CAPTURE, bool LOGG, bool OUTBF>
 __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs args) {
   extern __shared__ float lds[];
   const int T = args.n_pos;
@@ -323,24 +332,24 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
                                          static_cast<size_t>(h) * head_elems +
                                          static_cast<size_t>(row0 + row_blk) * kDK
                                    : nullptr;
-  float* const out_h = args.out + (static_cast<size_t>(r) * T * Hv + h) * kDK + row0;
+  const size_t out_h = (static_cast<size_t>(r) * T * Hv + h) * kDK + row0;   // element offset
 
   f32x4 s[kNCH];
 #pragma unroll
   for (int m = 0; m < kNCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(state_row + 4 * (li + kLPR * m));
 
   ChunkRegs<TIn> rg;
-  fetch_chunk<TIn>(args, rg, r, h, g, row0, 0, min(kC, T));
+  fetch_chunk<TIn, LOGG>(args, rg, r, h, g, row0, 0, min(kC, T));
   for (int c0 = 0; c0 < T; c0 += kC) {
     const int n = min(kC, T - c0);
     __syncthreads();   // the previous chunk's LDS reads are done
     // 1. Stage the fetched chunk (k, q unscaled, the block's v rows, gates)
     //    and the current state rows, then fetch the next chunk: its loads
     //    complete while this one is processed.
-    stage_chunk<TIn>(lds, rg);
+    stage_chunk<TIn, LOGG>(lds, rg, n);
 #pragma unroll
     for (int m = 0; m < kNCH; ++m) *reinterpret_cast<f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m)) = s[m];
-    if (c0 + kC < T) fetch_chunk<TIn>(args, rg, r, h, g, row0, c0 + kC, min(kC, T - c0 - kC));
+    if (c0 + kC < T) fetch_chunk<TIn, LOGG>(args, rg, r, h, g, row0, c0 + kC, min(kC, T - c0 - kC));
     __syncthreads();
     // 2. K K^T and Q K^T (matrix cores for bf16), X = K S_0^T and
     //    QS = Q S_0^T.
@@ -502,7 +511,15 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
             acc.w = __builtin_fmaf(pv, w4.w, acc.w);
           }
         }
-        *reinterpret_cast<f32x4*>(out_h + static_cast<size_t>(c0 + t) * Hv * kDK + c4) = acc;
+        const size_t o = out_h + static_cast<size_t>(c0 + t) * Hv * kDK + c4;
+        if constexpr (OUTBF) {
+          u32x2 w;
+          w.x = bf16_rne(acc.x) | (bf16_rne(acc.y) << 16);
+          w.y = bf16_rne(acc.z) | (bf16_rne(acc.w) << 16);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(args.out) + o) = w;
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(args.out) + o) = acc;
+        }
       }
     }
     if constexpr (CAPTURE) {
@@ -577,13 +594,25 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
   }
 }
 
-template <typename TIn>
-hipError_t launch_chunked(const ChunkArgs& args, int blocks, bool capture, hipStream_t s) {
-  if (capture)
-    hipLaunchKernelGGL((gdn_chunked_kernel<TIn, true>), dim3(blocks), dim3(kThreads), kLdsBytes, s, args);
+template <typename TIn, bool CAPTURE, bool LOGG>
+hipError_t launch_out(const ChunkArgs& args, int blocks, bool out_bf16, hipStream_t s) {
+  if (out_bf16)
+    hipLaunchKernelGGL((gdn_chunked_kernel<TIn, CAPTURE, LOGG, true>), dim3(blocks), dim3(kThreads), kLdsBytes, s,
+                       args);
   else
-    hipLaunchKernelGGL((gdn_chunked_kernel<TIn, false>), dim3(blocks), dim3(kThreads), kLdsBytes, s, args);
+    hipLaunchKernelGGL((gdn_chunked_kernel<TIn, CAPTURE, LOGG, false>), dim3(blocks), dim3(kThreads), kLdsBytes, s,
+                       args);
   return launch_error();
+}
+
+template <typename TIn>
+hipError_t launch_chunked(const ChunkArgs& args, int blocks, bool capture, bool log_gates, bool out_bf16,
+                          hipStream_t s) {
+  if (capture)
+    return log_gates ? launch_out<TIn, true, true>(args, blocks, out_bf16, s)
+                     : launch_out<TIn, true, false>(args, blocks, out_bf16, s);
+  return log_gates ? launch_out<TIn, false, true>(args, blocks, out_bf16, s)
+                   : launch_out<TIn, false, false>(args, blocks, out_bf16, s);
 }
 
 }  // namespace
@@ -591,12 +620,13 @@ hipError_t launch_chunked(const ChunkArgs& args, int blocks, bool capture, hipSt
 
 using namespace hrs;
 
-extern "C" int gdn_span_chunked(const hrs_gdn_desc* d, const void* q, const void* k, const void* v, const void* a,
-                                const void* b, float* state, float* ckpt, float* out, void* stream) {
-  if (d == nullptr) return HRS_EINVAL;
+extern "C" int gdn_span_chunked(const hrs_chunked_desc* cd, const void* q, const void* k, const void* v,
+                                const void* a, const void* b, float* state, float* ckpt, void* out, void* stream) {
+  if (cd == nullptr) return HRS_EINVAL;
+  const hrs_gdn_desc* d = &cd->gdn;
   if (d->n_req < 1 || d->n_kheads < 1 || d->n_vheads < 1 || d->d_k < 1 || d->d_v < 1) return HRS_EINVAL;
   if (d->n_vheads % d->n_kheads != 0) return HRS_EINVAL;
-  if (!dtype_ok(d->in_dtype)) return HRS_EINVAL;
+  if (!dtype_ok(d->in_dtype) || !dtype_ok(cd->out_dtype)) return HRS_EINVAL;
   if (d->topo != HRS_CHAIN) return d->topo == HRS_TREE ? HRS_EUNSUPPORTED : HRS_EINVAL;
   if (d->n_pos < 1 || d->n_pos > HRS_MAX_CHUNKED_POS) return HRS_EINVAL;
   if (!q || !k || !v || !a || !b || !state || !out) return HRS_EINVAL;
@@ -612,9 +642,12 @@ extern "C" int gdn_span_chunked(const hrs_gdn_desc* d, const void* q, const void
   args.n_pos = d->n_pos; args.n_kheads = d->n_kheads; args.n_vheads = d->n_vheads;
   args.group = d->n_vheads / d->n_kheads; args.q_scale = d->q_scale;
   const int blocks = d->n_req * d->n_vheads * (kDK / kRows);
+  const bool logg = cd->log_gates != 0;
+  const bool obf = cd->out_dtype == HRS_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const hipError_t e = d->in_dtype == HRS_BF16 ? launch_chunked<uint16_t>(args, blocks, ckpt != nullptr, s)
-                                               : launch_chunked<float>(args, blocks, ckpt != nullptr, s);
+  const hipError_t e = d->in_dtype == HRS_BF16
+                           ? launch_chunked<uint16_t>(args, blocks, ckpt != nullptr, logg, obf, s)
+                           : launch_chunked<float>(args, blocks, ckpt != nullptr, logg, obf, s);
   return e == hipSuccess ? HRS_OK : HRS_EDEVICE;
 }

@@ -18,6 +18,10 @@
  *   ring_set_2d / ring_get_2d
  *                       batched feature-ring row copies with wraparound
  *
+ * and, beside them: gdn_verify_span_from, conv1d_verify_span_nocapture and
+ * conv_state_advance (zero-copy rollback), gdn_layer_verify_span (one layer
+ * fused into one kernel) and gdn_span_chunked (long spans in chunks).
+ *
  * Conventions shared by every entry point
  * ----------------------------------------
  *  - Memory: every device buffer is allocated and owned by the caller. The
@@ -202,6 +206,14 @@ int gdn_verify_span_timed(const hrs_gdn_desc* desc, const void* q, const void* k
 /* Longest span gdn_span_chunked accepts. */
 #define HRS_MAX_CHUNKED_POS (1 << 20)
 
+typedef struct {
+  hrs_gdn_desc gdn;     /* shapes, input dtype, q_scale; topo must be HRS_CHAIN */
+  int32_t log_gates;    /* nonzero: `a` holds log decays g_t = log a_t (<= 0),
+                           so a_t = exp(g_t); zero: `a` holds a_t itself */
+  hrs_dtype out_dtype;  /* dtype of `out`: HRS_F32, or HRS_BF16 (each output
+                           rounded to the nearest bf16, ties to even) */
+} hrs_chunked_desc;
+
 /*
  * gdn_span_chunked - the gated delta rule of gdn_verify_span over a long
  * chain span (prefill length, up to HRS_MAX_CHUNKED_POS positions), computed
@@ -217,15 +229,17 @@ int gdn_verify_span_timed(const hrs_gdn_desc* desc, const void* q, const void* k
  * gdn_verify_span. Same mathematics, different rounding order: results agree
  * with gdn_verify_span to f32 rounding, not bit for bit.
  *
- * Arguments, layouts and capture as gdn_verify_span, chain only (desc->topo
- * must be HRS_CHAIN; parent is ignored): ckpt != NULL writes every
- * position's state and leaves `state` unchanged; ckpt == NULL updates `state`
- * in place to the state after the last position. Errors: HRS_EINVAL (sizes,
- * NULL pointers, n_pos outside [1, HRS_MAX_CHUNKED_POS]), HRS_EALIGN,
- * HRS_EUNSUPPORTED (tree topology; d_k or d_v other than 128), HRS_EDEVICE.
+ * Arguments, layouts and capture as gdn_verify_span, chain only
+ * (desc->gdn.topo must be HRS_CHAIN; parent is ignored), with two variants:
+ * log-space gates and bf16 outputs (`out` [R][T][Hv][d_v] in out_dtype).
+ * ckpt != NULL writes every position's state and leaves `state` unchanged;
+ * ckpt == NULL updates `state` in place to the state after the last
+ * position. Errors: HRS_EINVAL (sizes, NULL pointers, n_pos outside
+ * [1, HRS_MAX_CHUNKED_POS], out_dtype), HRS_EALIGN, HRS_EUNSUPPORTED (tree
+ * topology; d_k or d_v other than 128), HRS_EDEVICE.
  */
-int gdn_span_chunked(const hrs_gdn_desc* desc, const void* q, const void* k, const void* v,
-                     const void* a, const void* b, float* state, float* ckpt, float* out,
+int gdn_span_chunked(const hrs_chunked_desc* desc, const void* q, const void* k, const void* v,
+                     const void* a, const void* b, float* state, float* ckpt, void* out,
                      void* stream);
 
 typedef struct {

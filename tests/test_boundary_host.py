@@ -331,14 +331,16 @@ def test_chunked_entry_rejections():
     E = hrs
 
     def call(n_req=1, n_pos=200, Hk=2, Hv=4, dk=128, dv=128, dt=hrs.HRS_BF16, topo=hrs.HRS_CHAIN, q=FAKE, state=FAKE,
-             ckpt=None, out=FAKE, desc=True):
-        d = hrs.GdnDesc(n_req, n_pos, Hk, Hv, dk, dv, dt, 1.0, topo, None)
+             ckpt=None, out=FAKE, desc=True, out_dt=hrs.HRS_F32, log_gates=0):
+        g = hrs.GdnDesc(n_req, n_pos, Hk, Hv, dk, dv, dt, 1.0, topo, None)
+        d = hrs.ChunkedDesc(g, log_gates, out_dt)
         return hrs.lib.gdn_span_chunked(ctypes.byref(d) if desc else None, q, FAKE, FAKE, FAKE, FAKE, state, ckpt,
                                         out, None)
     assert call(desc=False) == E.HRS_EINVAL
     assert call(n_req=0) == E.HRS_EINVAL
     assert call(Hv=3) == E.HRS_EINVAL
     assert call(dt=9) == E.HRS_EINVAL
+    assert call(out_dt=5) == E.HRS_EINVAL
     assert call(n_pos=0) == E.HRS_EINVAL
     assert call(n_pos=(1 << 20) + 1) == E.HRS_EINVAL
     assert call(q=None) == E.HRS_EINVAL
@@ -348,7 +350,8 @@ def test_chunked_entry_rejections():
     assert call(topo=7) == E.HRS_EINVAL
     assert call(q=MIS) == E.HRS_EALIGN
     assert call(ckpt=MIS) == E.HRS_EALIGN
+    assert call(out=MIS) == E.HRS_EALIGN
     assert call(dk=64, dv=64) == E.HRS_EUNSUPPORTED
     assert call(n_pos=(1 << 20)) in (E.HRS_EDEVICE, E.HRS_OK)
-    assert call(ckpt=FAKE) in (E.HRS_EDEVICE, E.HRS_OK)
+    assert call(ckpt=FAKE, out_dt=hrs.HRS_BF16, log_gates=1) in (E.HRS_EDEVICE, E.HRS_OK)
     assert call() in (E.HRS_EDEVICE, E.HRS_OK)

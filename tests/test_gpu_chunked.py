@@ -109,3 +109,56 @@ def test_chunked_matches_recurrent_kernel_on_short_spans(hrs):
     for r in range(R):
         assert_tiles(s2[r], last[r], 2, f"in-place vs captured final state r={r}")
     assert torch.equal(out3, out1)
+
+
+def test_chunked_log_gates(hrs):
+    """Log-space gates: `a` holds g = log a (bf16); the oracle runs the
+    recurrence on a = exp(g) computed in float64 from the same bf16 values."""
+    import torch
+    from synth import bf16_to_f32
+    w = scaled(QWEN_LAYER_CHAIN, n_req=2, n_pos=90, n_kheads=4, n_vheads=8)
+    units = [gen_unit(w, 0, r) for r in range(w.n_req)]
+    for u in units:
+        g = np.log(bf16_to_f32(u.a).astype(np.float64))
+        u.a = bf16_bits(g.astype(np.float32))          # the kernel's input: bf16 log decays
+    st = lambda name: to_torch(np.stack([getattr(u, name) for u in units]))
+    q, k, v, g, b, state = st("q"), st("k"), st("v"), st("a"), st("b"), st("state")
+    R, T, Hv, d = 2, 90, 8, 128
+    ckpt = torch.full((R, T, Hv, d, d), float("nan"), device="cuda")
+    out = torch.full((R, T, Hv, d), float("nan"), device="cuda")
+    hrs.gdn_span_chunked(q, k, v, g, b, state, ckpt, out, log_gates=True)
+    torch.cuda.synchronize()
+    ck, o = to_numpy(ckpt), to_numpy(out)
+    for r, u in enumerate(units):
+        a64 = np.exp(bf16_to_f32(u.a).astype(np.float64))
+        ock, oout = ogdn.gdn_span(u.state, u.q, u.k, u.v, a64, u.b, None, 1.0)
+        e1 = assert_tiles(ck[r], ock, 2, f"log gates ckpt r={r}")
+        e2 = assert_tiles(o[r], oout, 1, f"log gates out r={r}")
+        say(f"log gates r={r}: ckpt err {e1:.2e}, out err {e2:.2e}")
+
+
+def test_chunked_bf16_outputs(hrs):
+    """bf16 outputs are the f32 outputs of the same computation rounded to the
+    nearest bf16 (ties to even), bit for bit; against the oracle, within one
+    bf16 rounding (2^-8 of the tile maximum)."""
+    import torch
+    w = scaled(QWEN_LAYER_CHAIN, n_req=2, n_pos=100, n_kheads=4, n_vheads=8)
+    units = [gen_unit(w, 0, r) for r in range(w.n_req)]
+    st = lambda name: to_torch(np.stack([getattr(u, name) for u in units]))
+    q, k, v, a, b = st("q"), st("k"), st("v"), st("a"), st("b")
+    R, T, Hv, d = 2, 100, 8, 128
+    out32 = torch.empty((R, T, Hv, d), device="cuda")
+    out16 = torch.empty((R, T, Hv, d), device="cuda", dtype=torch.bfloat16)
+    s1, s2 = st("state"), st("state")
+    hrs.gdn_span_chunked(q, k, v, a, b, s1, None, out32, q_scale=0.5)
+    hrs.gdn_span_chunked(q, k, v, a, b, s2, None, out16, q_scale=0.5)
+    torch.cuda.synchronize()
+    o32 = to_numpy(out32)
+    o16 = to_numpy(out16)
+    o16 = o16 if o16.dtype == np.uint16 else bf16_bits(o16)
+    assert np.array_equal(o16, bf16_bits(o32))
+    assert torch.equal(s1, s2)
+    from synth import bf16_to_f32
+    for r, u in enumerate(units):
+        _, oout = ogdn.gdn_span(u.state, u.q, u.k, u.v, u.a, u.b, None, 0.5)
+        assert_tiles(bf16_to_f32(o16[r]), oout, 1, f"bf16 out r={r}", tol=2.0 ** -8)
