@@ -10,7 +10,13 @@
 // MI355X design: in capture mode for a chain, one thread takes 8 channels of
 // two consecutive positions and slides the window over five loaded rows
 // (measured 8.5 us versus 10.4 us for one position per thread on 16
-// requests x 8192 channels). For a tree every (position, 8-channel group) is
+// requests x 8192 channels). Every thread loads once and then stores, so a
+// launch is one load phase and one store phase; a variant in which each
+// thread walked several rows with the next row's loads issued before the
+// current row's stores was not faster at these sizes (27.6 MB per launch on
+// 16 requests, where the launch's fixed latency is a large part of the
+// time). Captured states are written with nontemporal stores (not read
+// again by this span); 128-thread blocks measured faster than 256. For a tree every (position, 8-channel group) is
 // an independent thread: the host turns the parent array into a table that
 // names, for each position and window slot, the x row or conv-state row to
 // read (x rows are re-read from L2 by up to W threads). Loads and stores
@@ -29,7 +35,7 @@
 namespace hrs {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 128;
 constexpr int kWidth = 4;
 constexpr int kBack = kWidth - 1;
 
@@ -53,6 +59,9 @@ template <> struct Raw8<uint16_t> {
   u32x4 v;
   __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
   __device__ __forceinline__ void store(uint16_t* p) const { *reinterpret_cast<u32x4*>(p) = v; }
+  __device__ __forceinline__ void store_nt(uint16_t* p) const {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  }
   __device__ __forceinline__ float f(int i) const {
     const uint32_t w = v[i >> 1];
     return (i & 1) ? bf16_hi(w) : bf16_lo(w);
@@ -67,6 +76,10 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ void store(float* p) const {
     *reinterpret_cast<f32x4*>(p) = v0;
     *reinterpret_cast<f32x4*>(p + 4) = v1;
+  }
+  __device__ __forceinline__ void store_nt(float* p) const {
+    __builtin_nontemporal_store(v0, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(v1, reinterpret_cast<f32x4*>(p + 4));
   }
   __device__ __forceinline__ float f(int i) const { return i < 4 ? v0[i] : v1[i - 4]; }
 };
@@ -103,6 +116,8 @@ __device__ __forceinline__ void conv_out(const float (&wt)[8][kWidth], const Raw
 // Capture mode: one thread per (position, 8-channel group).
 template <typename T, bool STORE>
 __global__ __launch_bounds__(kThreads) void conv_capture_kernel(const ConvArgs args) {
+  args_in_registers(args.x, args.w, args.conv_state, args.conv_ckpt, args.y, args.n_pos, args.channels,
+                    args.req0, args.per_request_table, args.silu);
   const int C = args.channels;
   const int c0 = (blockIdx.x * kThreads + threadIdx.x) * 8;
   if (c0 >= C) return;
@@ -132,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void conv_capture_kernel(const ConvArgs a
   if (STORE) {
     T* dst = ck + (static_cast<size_t>(r) * T_ + t) * kBack * C + c0;
 #pragma unroll
-    for (int m = 0; m < kBack; ++m) win[m + 1].store(dst + static_cast<size_t>(m) * C);
+    for (int m = 0; m < kBack; ++m) win[m + 1].store_nt(dst + static_cast<size_t>(m) * C);
   }
 }
 
@@ -141,6 +156,8 @@ __global__ __launch_bounds__(kThreads) void conv_capture_kernel(const ConvArgs a
 constexpr int kChainPos = 2;
 template <typename T, bool STORE>
 __global__ __launch_bounds__(kThreads) void conv_chain_kernel(const ConvArgs args) {
+  args_in_registers(args.x, args.w, args.conv_state, args.conv_ckpt, args.y, args.n_pos, args.channels,
+                    args.req0, args.per_request_table, args.silu);
   const int C = args.channels;
   const int c0 = (blockIdx.x * kThreads + threadIdx.x) * 8;
   if (c0 >= C) return;
@@ -172,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void conv_chain_kernel(const ConvArgs arg
       if (STORE) {
         T* dst = ck + (static_cast<size_t>(r) * T_ + t) * kBack * C + c0;
 #pragma unroll
-        for (int m = 0; m < kBack; ++m) win[m + 1].store(dst + static_cast<size_t>(m) * C);
+        for (int m = 0; m < kBack; ++m) win[m + 1].store_nt(dst + static_cast<size_t>(m) * C);
       }
     }
   }
@@ -181,6 +198,8 @@ __global__ __launch_bounds__(kThreads) void conv_chain_kernel(const ConvArgs arg
 // No capture (chain): one thread per 8-channel group walks the positions.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void conv_inplace_kernel(const ConvArgs args) {
+  args_in_registers(args.x, args.w, args.conv_state, args.conv_ckpt, args.y, args.n_pos, args.channels,
+                    args.req0, args.per_request_table, args.silu);
   const int C = args.channels;
   const int c0 = (blockIdx.x * kThreads + threadIdx.x) * 8;
   if (c0 >= C) return;

@@ -21,6 +21,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // bf16 -> f32 is exact: the bf16 pattern is the upper half of the f32.
+// Makes the compiler read the given kernel-argument values here, as one batch
+// of scalar loads, instead of after the kernel's first branch (an early-exit
+// test loads its bound first and the pointers only behind it): every later
+// batch of argument loads is one more dependent memory round trip before the
+// first data load of the launch.
+template <typename T>
+__device__ __forceinline__ void arg_in_register(const T& v) {
+  asm volatile("" : : "s"(v));
+}
+template <typename... Ts>
+__device__ __forceinline__ void args_in_registers(const Ts&... v) {
+  (arg_in_register(v), ...);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_one(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }

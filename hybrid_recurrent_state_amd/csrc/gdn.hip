@@ -20,7 +20,7 @@
 //    lines. Checkpoints are written with nontemporal stores; they are not
 //    read again until rollback (normal stores measured ~12% slower).
 //  * Work order: units are numbered row block fastest, then head, then
-//    request, and a block walks units W, W + gridDim.x, ... When there are at
+//    request, and a block walks units W, W + n_blocks, ... When there are at
 //    least as many 32-row units as compute units, the grid is one block per
 //    CU with 8 row-owning waves: all CUs then advance through the positions
 //    together and each position's checkpoint region (2 MiB per request) is
@@ -110,6 +110,7 @@ struct GdnArgs {
   int32_t group;   // Hv / Hk
   int32_t req0;    // first request of this launch
   int32_t n_units; // row units of this launch: (d_v / rows per unit) * Hv * requests
+  int32_t n_blocks; // blocks of this launch (block W walks units W, W + n_blocks, ...)
   int32_t window;  // positions staged in LDS at a time (min(n_pos, kWindow))
   float q_scale;
   // Zero-copy source of the initial state (gdn_verify_span_from): when
@@ -511,15 +512,6 @@ __global__ __launch_bounds__((NW + NP) * 64) void gdn_span_kernel(const GdnArgs 
   const size_t pos_stride = static_cast<size_t>(Hv) * head_elems;   // one position of ckpt
   const int out_stride = Hv * dv;
 
-  if (args.status != nullptr && args.req0 == 0 && blockIdx.x == 0 && tid == (NP > 0 ? NC : 0)) {
-    int32_t bad = 0;
-    for (int i = 0; i < args.n_req_total; ++i) {
-      const int32_t u = args.src_node[i];
-      bad += (u < 0 || u >= args.src_npos) ? 1 : 0;
-    }
-    *args.status = bad;
-  }
-
   // Consumer pointers of the current unit.
   auto ckpt_of = [&](const Unit& u) -> float* {
     return CAPTURE ? args.ckpt + static_cast<size_t>(u.r) * T * pos_stride + static_cast<size_t>(u.h) * head_elems +
@@ -533,7 +525,7 @@ __global__ __launch_bounds__((NW + NP) * 64) void gdn_span_kernel(const GdnArgs 
 
   if constexpr (NP == 0) {
     f32x4* const stash = reinterpret_cast<f32x4*>(lds + staging_floats(args.window, POS_FLOATS));
-    for (int W = blockIdx.x; W < args.n_units; W += gridDim.x) {
+    for (int W = blockIdx.x; W < args.n_units; W += args.n_blocks) {
       const Unit u = unit_of(args, W, RPB);
       const float* init = initial_rows<DK>(args, u);
       if (init == nullptr) continue;   // block-uniform: every thread has the same request
@@ -566,13 +558,13 @@ __global__ __launch_bounds__((NW + NP) * 64) void gdn_span_kernel(const GdnArgs 
     const int p = tid - NC;                // producer index
     const int nwin = (T + kWindow - 1) / kWindow;
     const int n_my = static_cast<int>(blockIdx.x) < args.n_units
-                         ? (args.n_units - 1 - static_cast<int>(blockIdx.x)) / static_cast<int>(gridDim.x) + 1
+                         ? (args.n_units - 1 - static_cast<int>(blockIdx.x)) / args.n_blocks + 1
                          : 0;
     const int n_items = n_my * nwin;       // (unit, window) pairs of this block, in order
 
     // Stage item i into buffer i % 2: all threads for item 0 (no checkpoint
     // store is in flight yet), the producers for every later item.
-    auto item_unit = [&](int i) { return unit_of(args, blockIdx.x + (i / nwin) * gridDim.x, RPB); };
+    auto item_unit = [&](int i) { return unit_of(args, blockIdx.x + (i / nwin) * args.n_blocks, RPB); };
     if (n_items > 0)
       produce_item<DK, (NW + NP) * 64, RPB, POS_FLOATS, TIn, FUSED, true>(args, lds, state_lds, flag_lds, item_unit(0),
                                                                           0, min(kWindow, T), tid);
@@ -583,7 +575,7 @@ __global__ __launch_bounds__((NW + NP) * 64) void gdn_span_kernel(const GdnArgs 
     for (int i = 0; i < n_items; ++i) {
       const int j = i % nwin;
       if (consumer && j == 0) {
-        const Unit u = unit_of(args, blockIdx.x + (i / nwin) * gridDim.x, RPB);
+        const Unit u = unit_of(args, blockIdx.x + (i / nwin) * args.n_blocks, RPB);
         valid = flag_lds[0] != 0;
         if (valid) {
 #pragma unroll
@@ -610,6 +602,16 @@ __global__ __launch_bounds__((NW + NP) * 64) void gdn_span_kernel(const GdnArgs 
       __syncthreads();  // window i + 1 is staged; buffer i % 2 is free
     }
   }
+  // The status word counts out-of-range source indices. It is taken last so
+  // that no branch sits between the kernel's entry and its argument loads.
+  if (args.status != nullptr && args.req0 == 0 && blockIdx.x == 0 && tid == (NP > 0 ? NC : 0)) {
+    int32_t bad = 0;
+    for (int i = 0; i < args.n_req_total; ++i) {
+      const int32_t u = args.src_node[i];
+      bad += (u < 0 || u >= args.src_npos) ? 1 : 0;
+    }
+    *args.status = bad;
+  }
 }
 
 // Launch through hipExtLaunchKernelGGL so that optional timing events are
@@ -618,6 +620,7 @@ template <int DK, int NW, int NP, typename TIn, bool TREE, bool RELOAD, bool CAP
 hipError_t launch_one(GdnArgs& args, int grid, int n_slots, hipStream_t stream, hipEvent_t start,
                       hipEvent_t stop) {
   constexpr int RPB = (64 / kLanesPerRow) * NW;
+  args.n_blocks = grid;
   const size_t lds = NP > 0 ? pipelined_bytes(DK, RPB, args.window)
                             : staging_bytes(DK, RPB, args.window, TREE) + (TREE ? n_slots * slot_bytes(DK, NW) : 0);
   hipExtLaunchKernelGGL((gdn_span_kernel<DK, NW, NP, TIn, TREE, RELOAD, CAPTURE, FUSED>), dim3(grid),

@@ -50,7 +50,7 @@ __device__ __forceinline__ void copy_chunk(const u32x4* src, u32x4* dst, int64_t
 #pragma unroll
   for (int i = 0; i < kVecPerThread; ++i) {
     const int64_t e = base + static_cast<int64_t>(i) * kThreads;
-    if (e < n_vecs) dst[e] = v[i];
+    if (e < n_vecs) __builtin_nontemporal_store(v[i], dst + e);
   }
 }
 
