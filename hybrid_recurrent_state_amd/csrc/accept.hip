@@ -12,9 +12,11 @@
 // value bits above the complemented index) and writes it to the caller's
 // workspace. Taking the maximum key realises "largest value, lowest index on
 // ties, NaN never wins" with plain integer compares, in any reduction order,
-// so the result is deterministic. Pass 2 is one wave per request: lane t
-// reduces row t's chunk keys, then the acceptance walk runs over the T <= 64
-// positions in LDS.
+// so the result is deterministic. Each pass-1 thread issues all its loads
+// before its first compare. Pass 2 is one wave per request: the lanes gather
+// the row keys (64-bit maximum per row in LDS), the draft tokens and the
+// parents together, then the acceptance walk runs over the T <= 64 positions
+// in LDS.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -27,6 +29,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunk = 8192;  // logits per pass-1 block
+static_assert(kChunk % (kThreads * 8) == 0, "whole 8-logit slices per thread");
 
 struct AcceptArgs {
   const int32_t* tokens;
@@ -70,13 +73,24 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const T* logit
   const T* base = logits + static_cast<size_t>(row) * vocab;
   const int begin = chunk * kChunk;
   const int end = min(vocab, begin + kChunk);
+  // All of the thread's loads are issued before the first use (one memory
+  // latency per block); slices past the row's end re-read the chunk's last
+  // eight logits (end - 8 >= begin since vocab is a multiple of 8) and are
+  // given key 0, which never wins.
+  constexpr int kIter = kChunk / (kThreads * 8);
+  float v[kIter][8];
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    const int e = begin + (it * kThreads + threadIdx.x) * 8;
+    load8<T>(base + min(e, end - 8), v[it]);
+  }
   uint64_t best = 0;
-  for (int e = begin + threadIdx.x * 8; e < end; e += kThreads * 8) {
-    float v[8];
-    load8<T>(base + e, v);
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    const int e = begin + (it * kThreads + threadIdx.x) * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint64_t key = make_key(v[i], static_cast<uint32_t>(e + i));
+      const uint64_t key = e < end ? make_key(v[it][i], static_cast<uint32_t>(e + i)) : 0;
       best = key > best ? key : best;
     }
   }
@@ -100,28 +114,50 @@ __global__ __launch_bounds__(64) void accept_walk_kernel(const AcceptArgs args) 
   const int rl = blockIdx.x;
   const int r = args.req0 + rl;
   const int lane = threadIdx.x;
+  __shared__ unsigned long long row_key[HRS_MAX_POS];
   __shared__ int32_t am[HRS_MAX_POS];
+  __shared__ int32_t tok[HRS_MAX_POS];
+  __shared__ int32_t par[HRS_MAX_POS];
   __shared__ int32_t path_s[HRS_MAX_POS];
   __shared__ int32_t depth[HRS_MAX_POS];
   __shared__ int32_t matched[HRS_MAX_POS];
   __shared__ int32_t len_s;
+  // Everything the walk reads is gathered first, by all lanes at once: the
+  // row's chunk keys (maximum per row in LDS), the draft tokens and the
+  // parents; the walk itself then touches LDS only.
   if (lane < T_) {
-    const uint64_t* k = args.keys + (static_cast<size_t>(r) * T_ + lane) * args.n_chunks;
-    uint64_t b = 0;
-    for (int c = 0; c < args.n_chunks; ++c) b = k[c] > b ? k[c] : b;
-    const int32_t idx = static_cast<int32_t>(~static_cast<uint32_t>(b));
+    const int32_t tk = args.tokens[static_cast<size_t>(r) * T_ + lane];
+    const int32_t pr = args.tree ? args.parent[rl * T_ + lane] : lane - 1;
+    row_key[lane] = 0;
+    tok[lane] = tk;
+    par[lane] = pr;
+  }
+  __syncthreads();
+  const int n_keys = T_ * args.n_chunks;
+  const uint64_t* k = args.keys + static_cast<size_t>(r) * n_keys;
+  // Eight keys per lane are loaded (unconditionally, from clamped indices)
+  // before the LDS maxima take them, so their latencies overlap.
+  for (int i0 = lane; i0 < n_keys; i0 += 64 * 8) {
+    uint64_t kv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kv[j] = k[min(i0 + 64 * j, n_keys - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (i0 + 64 * j < n_keys) atomicMax(&row_key[(i0 + 64 * j) / args.n_chunks], static_cast<unsigned long long>(kv[j]));
+  }
+  __syncthreads();
+  if (lane < T_) {
+    const int32_t idx = static_cast<int32_t>(~static_cast<uint32_t>(row_key[lane]));
     am[lane] = idx;
     args.argmax[static_cast<size_t>(r) * T_ + lane] = idx;
   }
   __syncthreads();
   if (lane == 0) {
-    const int32_t* tok = args.tokens + static_cast<size_t>(r) * T_;
-    const int8_t* par = args.parent + rl * T_;
     matched[0] = 1;
     depth[0] = 0;
     int32_t best = 0;
     for (int t = 1; t < T_; ++t) {
-      const int p = args.tree ? par[t] : t - 1;
+      const int p = par[t];
       depth[t] = depth[p] + 1;
       matched[t] = (matched[p] && tok[t] == am[p]) ? 1 : 0;
       if (matched[t] && depth[t] > depth[best]) best = t;
@@ -130,7 +166,7 @@ __global__ __launch_bounds__(64) void accept_walk_kernel(const AcceptArgs args) 
     int node = best;
     for (int d = len; d >= 0; --d) {
       path_s[d] = node;
-      node = args.tree ? par[node] : node - 1;
+      node = par[node];
     }
     len_s = len;
     args.accept_node[r] = best;
