@@ -182,10 +182,14 @@ __global__ __launch_bounds__(64) void accept_walk_kernel(const AcceptArgs args) 
 
 using namespace hrs;
 
+// Pass 1 runs one block per (row, 8192-logit chunk): at most 2^24 blocks.
+constexpr int64_t kMaxChunkBlocks = int64_t{1} << 24;
+
 static bool accept_desc_ok(const hrs_accept_desc* d) {
   return d && d->n_req >= 1 && d->vocab >= 8 && d->vocab % 8 == 0 && dtype_ok(d->logit_dtype) &&
          (d->topo == HRS_CHAIN || d->topo == HRS_TREE) && d->n_pos >= 1 && d->n_pos <= HRS_MAX_POS &&
-         static_cast<int64_t>(d->n_req) * d->n_pos <= 65535 * 64;
+         static_cast<int64_t>(d->n_req) * d->n_pos <= 65535 * 64 &&
+         static_cast<int64_t>(d->n_req) * d->n_pos * ((d->vocab + kChunk - 1) / kChunk) <= kMaxChunkBlocks;
 }
 
 static int accept_chunks(const hrs_accept_desc* d) { return (d->vocab + kChunk - 1) / kChunk; }

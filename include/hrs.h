@@ -399,8 +399,9 @@ size_t accept_greedy_workspace_bytes(const hrs_accept_desc* desc);
  * device arrays argmax [R][T], accept_node [R], accept_len [R],
  * path [R][T], bonus [R]. workspace: device scratch of at least
  * accept_greedy_workspace_bytes(desc) bytes, 16-byte aligned, contents
- * ignored on entry. Errors: HRS_EINVAL, HRS_EALIGN, HRS_EGEOMETRY,
- * HRS_EDEVICE.
+ * ignored on entry. Size limits: n_req * n_pos <= 65535 * 64 and
+ * n_req * n_pos * ceil(V / 8192) <= 2^24 (else HRS_EINVAL). Errors:
+ * HRS_EINVAL, HRS_EALIGN, HRS_EGEOMETRY, HRS_EDEVICE.
  */
 int accept_greedy(const hrs_accept_desc* desc, const void* logits, const int32_t* tokens,
                   int32_t* argmax, int32_t* accept_node, int32_t* accept_len,

@@ -192,6 +192,12 @@ def test_accept_rejections_and_workspace_size():
     assert accept_call(topo=E.HRS_TREE, parent=[-1, 0, 0, 1, 1, -1, 0, 1, 1, 2])[0] in (E.HRS_EDEVICE, E.HRS_OK)
     assert accept_call(path=MIS)[0] == E.HRS_EALIGN
     assert accept_call(vocab=0)[1] == 0
+    # pass-1 blocks (rows x 8192-logit chunks) are bounded by 2^24: the largest
+    # vocabulary (2^31 - 8, 2^18 chunks) fits 64 rows, not 128
+    vmax = (1 << 31) - 8
+    d64 = hrs.AcceptDesc(1, 64, vmax, E.HRS_BF16, E.HRS_CHAIN, None)
+    assert hrs.lib.accept_greedy_workspace_bytes(ctypes.byref(d64)) == 64 * (1 << 18) * 8
+    assert accept_call(n_req=2, n_pos=64, vocab=vmax) == (E.HRS_EINVAL, 0)
 
 
 def rollback_call(**kw):
