@@ -334,6 +334,19 @@ def main():
     phases = {"conv+gdn": ph[0].elapsed_time(ph[1]), "accept": ph[1].elapsed_time(ph[2]),
               "rollback": ph[2].elapsed_time(ph[3]), "ring": ph[3].elapsed_time(ph[4])}
 
+    # Per-stack timing: the L GDN spans of a step back to back with no other
+    # kernel between them (launch gaps included), event-timed, median of 3.
+    stack = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for l in range(L):
+            step.launch_gdn(l, h)
+        e1.record()
+        torch.cuda.synchronize()
+        stack.append(e0.elapsed_time(e1) / L)
+    stack_s = float(np.median(stack)) / 1e3
+
     R, T = w.n_req, w.n_pos
     value = R * T * L / (ms_per_step / 1e3)
     gdn_bytes = shape.gdn_bytes_per_layer
@@ -437,7 +450,9 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "gdn_verify_span", "bytes_per_launch": gdn_bytes,
                      "avg_launch_us": gdn_avg_s * 1e6, "median_launch_us": gdn_med_s * 1e6,
-                     "store_stream_gbs": store_gbs, "frac_of_store_stream": achieved / store_gbs},
+                     "store_stream_gbs": store_gbs, "frac_of_store_stream": achieved / store_gbs,
+                     "stack_us_per_layer": stack_s * 1e6,
+                     "stack_frac": gdn_bytes / stack_s / 1e9 / HBM_PEAK_GBS},
         "gdn_tokens_per_s_per_layer": R * T / gdn_avg_s,
         "draft_tokens_per_s_per_layer": R * (T - 1) * L / (ms_per_step / 1e3),
         "phases_ms": phases,

@@ -208,6 +208,10 @@ class VerifyStep:
         else:
             _check(lib.gdn_verify_span_timed(self.gdn_p, *gdn_a, stream, events[0], events[1]), "gdn_verify_span")
 
+    def launch_gdn(self, l: int, stream: int) -> None:
+        """The GDN span of layer l alone (its inputs as the step leaves them)."""
+        _check(lib.gdn_verify_span(self.gdn_p, *self.layer_args[l][1], stream), "gdn_verify_span")
+
     def launch_accept(self, stream: int) -> None:
         if self.accept_desc is not None:
             _check(lib.accept_greedy(ctypes.byref(self.accept_desc), *self.accept_args, stream), "accept_greedy")
