@@ -353,12 +353,35 @@ __device__ __forceinline__ void run_positions(const float* buf, f32x4* stash, f3
   const int lane = tid & 63;
   const int li = lane % LPR;
   const int row_blk = (tid >> 6) * (64 / LPR) + lane / LPR;
-  for (int tt = 0; tt < tn; ++tt) {
-    const int t = t0 + tt;
-    const float* lp = buf + tt * POS_FLOATS;
-    int tree_code = 0;
-    if constexpr (TREE) {
-      tree_code = __builtin_amdgcn_readfirstlane(__float_as_int(lp[2 * DK + RPB + 2]));
+  if constexpr (TREE) {
+    // Tree spans (single-role blocks): the staged inputs of a position are
+    // read from LDS one position ahead, into registers, so their LDS latency
+    // overlaps the previous position (4% faster on 16 requests; the chain
+    // kernel, whose producer waves share the SIMDs, measured 6% slower).
+    f32x4 kn[NCH], qn[NCH];
+    float an = 0.0f, bn = 0.0f, vn = 0.0f;
+    int cn = 0;
+    auto fetch = [&](int tt) {
+      const float* lp = buf + tt * POS_FLOATS;
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) {
+        kn[m] = *reinterpret_cast<const f32x4*>(lp + 4 * (li + LPR * m));
+        qn[m] = *reinterpret_cast<const f32x4*>(lp + DK + 4 * (li + LPR * m));
+      }
+      an = lp[2 * DK + RPB];
+      bn = lp[2 * DK + RPB + 1];
+      vn = lp[2 * DK + row_blk];
+      cn = __builtin_amdgcn_readfirstlane(__float_as_int(lp[2 * DK + RPB + 2]));
+    };
+    if (tn > 0) fetch(0);
+    for (int tt = 0; tt < tn; ++tt) {
+      const int t = t0 + tt;
+      f32x4 kk[NCH], qq[NCH];
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) { kk[m] = kn[m]; qq[m] = qn[m]; }
+      const float at = an, bt = bn, vt = vn;
+      const int tree_code = cn;
+      if (tt + 1 < tn) fetch(tt + 1);
       const int rs = static_cast<int8_t>((tree_code >> 8) & 0xFF);
       if (rs >= 0) {
 #pragma unroll
@@ -374,54 +397,90 @@ __device__ __forceinline__ void run_positions(const float* buf, f32x4* stash, f3
         // drain all outstanding checkpoint stores.
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       }
-    }
-    f32x4 kk[NCH];
+      float u = 0.0f;
 #pragma unroll
-    for (int m = 0; m < NCH; ++m) kk[m] = *reinterpret_cast<const f32x4*>(lp + 4 * (li + LPR * m));
-    float u = 0.0f;
+      for (int m = 0; m < NCH; ++m) {
+        u = __builtin_fmaf(s[m].x, kk[m].x, u);
+        u = __builtin_fmaf(s[m].y, kk[m].y, u);
+        u = __builtin_fmaf(s[m].z, kk[m].z, u);
+        u = __builtin_fmaf(s[m].w, kk[m].w, u);
+      }
+      u = group_sum<LPR>(u);
+      const float c = bt * __builtin_fmaf(-at, u, vt);
 #pragma unroll
-    for (int m = 0; m < NCH; ++m) {
-      u = __builtin_fmaf(s[m].x, kk[m].x, u);
-      u = __builtin_fmaf(s[m].y, kk[m].y, u);
-      u = __builtin_fmaf(s[m].z, kk[m].z, u);
-      u = __builtin_fmaf(s[m].w, kk[m].w, u);
-    }
-    u = group_sum<LPR>(u);
-    const float at = lp[2 * DK + RPB];
-    const float bt = lp[2 * DK + RPB + 1];
-    const float vt = lp[2 * DK + row_blk];
-    const float c = bt * __builtin_fmaf(-at, u, vt);
+      for (int m = 0; m < NCH; ++m) {
+        s[m].x = __builtin_fmaf(c, kk[m].x, at * s[m].x);
+        s[m].y = __builtin_fmaf(c, kk[m].y, at * s[m].y);
+        s[m].z = __builtin_fmaf(c, kk[m].z, at * s[m].z);
+        s[m].w = __builtin_fmaf(c, kk[m].w, at * s[m].w);
+      }
+      if (CAPTURE) {
+        float* dst = ckpt_row0 + static_cast<size_t>(t) * pos_stride;
 #pragma unroll
-    for (int m = 0; m < NCH; ++m) {
-      s[m].x = __builtin_fmaf(c, kk[m].x, at * s[m].x);
-      s[m].y = __builtin_fmaf(c, kk[m].y, at * s[m].y);
-      s[m].z = __builtin_fmaf(c, kk[m].z, at * s[m].z);
-      s[m].w = __builtin_fmaf(c, kk[m].w, at * s[m].w);
-    }
-    if (CAPTURE) {
-      float* dst = ckpt_row0 + static_cast<size_t>(t) * pos_stride;
-#pragma unroll
-      for (int m = 0; m < NCH; ++m)
-        __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(dst + 4 * (li + LPR * m)));
-    }
-    if constexpr (TREE) {
+        for (int m = 0; m < NCH; ++m)
+          __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(dst + 4 * (li + LPR * m)));
+      }
       const int sv = static_cast<int8_t>((tree_code >> 16) & 0xFF);
       if (sv >= 0) {
 #pragma unroll
         for (int m = 0; m < NCH; ++m) stash[(sv * NCH + m) * NTHREADS + tid] = s[m];
       }
-    }
-    float o = 0.0f;
+      float o = 0.0f;
 #pragma unroll
-    for (int m = 0; m < NCH; ++m) {
-      const f32x4 qq = *reinterpret_cast<const f32x4*>(lp + DK + 4 * (li + LPR * m));
-      o = __builtin_fmaf(s[m].x, qq.x, o);
-      o = __builtin_fmaf(s[m].y, qq.y, o);
-      o = __builtin_fmaf(s[m].z, qq.z, o);
-      o = __builtin_fmaf(s[m].w, qq.w, o);
+      for (int m = 0; m < NCH; ++m) {
+        o = __builtin_fmaf(s[m].x, qq[m].x, o);
+        o = __builtin_fmaf(s[m].y, qq[m].y, o);
+        o = __builtin_fmaf(s[m].z, qq[m].z, o);
+        o = __builtin_fmaf(s[m].w, qq[m].w, o);
+      }
+      o = group_sum<LPR>(o);
+      if (li == 0) out_r[static_cast<size_t>(t) * out_stride] = o;
     }
-    o = group_sum<LPR>(o);
-    if (li == 0) out_r[static_cast<size_t>(t) * out_stride] = o;
+  } else {
+    for (int tt = 0; tt < tn; ++tt) {
+      const int t = t0 + tt;
+      const float* lp = buf + tt * POS_FLOATS;
+      f32x4 kk[NCH];
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) kk[m] = *reinterpret_cast<const f32x4*>(lp + 4 * (li + LPR * m));
+      float u = 0.0f;
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) {
+        u = __builtin_fmaf(s[m].x, kk[m].x, u);
+        u = __builtin_fmaf(s[m].y, kk[m].y, u);
+        u = __builtin_fmaf(s[m].z, kk[m].z, u);
+        u = __builtin_fmaf(s[m].w, kk[m].w, u);
+      }
+      u = group_sum<LPR>(u);
+      const float at = lp[2 * DK + RPB];
+      const float bt = lp[2 * DK + RPB + 1];
+      const float vt = lp[2 * DK + row_blk];
+      const float c = bt * __builtin_fmaf(-at, u, vt);
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) {
+        s[m].x = __builtin_fmaf(c, kk[m].x, at * s[m].x);
+        s[m].y = __builtin_fmaf(c, kk[m].y, at * s[m].y);
+        s[m].z = __builtin_fmaf(c, kk[m].z, at * s[m].z);
+        s[m].w = __builtin_fmaf(c, kk[m].w, at * s[m].w);
+      }
+      if (CAPTURE) {
+        float* dst = ckpt_row0 + static_cast<size_t>(t) * pos_stride;
+#pragma unroll
+        for (int m = 0; m < NCH; ++m)
+          __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(dst + 4 * (li + LPR * m)));
+      }
+      float o = 0.0f;
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) {
+        const f32x4 qq = *reinterpret_cast<const f32x4*>(lp + DK + 4 * (li + LPR * m));
+        o = __builtin_fmaf(s[m].x, qq.x, o);
+        o = __builtin_fmaf(s[m].y, qq.y, o);
+        o = __builtin_fmaf(s[m].z, qq.z, o);
+        o = __builtin_fmaf(s[m].w, qq.w, o);
+      }
+      o = group_sum<LPR>(o);
+      if (li == 0) out_r[static_cast<size_t>(t) * out_stride] = o;
+    }
   }
 }
 
