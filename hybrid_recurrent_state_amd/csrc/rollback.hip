@@ -8,9 +8,11 @@
 // split-chain fast rollback with F32 SSM checkpoints"), Summary: restore
 // the captured F32 checkpoint instead of replaying the accepted tokens.
 //
-// MI355X design: a plain HBM-bound copy. The grid is (16 KiB chunk, layer x
-// request); each thread issues four 16-byte loads before its four stores so
-// every wave keeps 4 KiB in flight. A block whose request carries an index
+// MI355X design: a plain HBM-bound copy. The grid is (64 KiB chunk, layer x
+// request) of 1024-thread blocks; each thread issues four 16-byte
+// nontemporal loads before its four nontemporal stores, so every wave keeps
+// 4 KiB in flight (on 16 requests x 48 layers, 3.3 GB: 542 us, 6.1 TB/s,
+// against 580 us for 256-thread blocks; eight loads per thread were slower). A block whose request carries an index
 // outside [0, T) copies nothing; block (0, 0) alone writes the status word
 // (the count of such requests), so the word needs no clearing and no atomics.
 #include <hip/hip_runtime.h>
@@ -21,7 +23,7 @@
 namespace hrs {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kVecPerThread = 4;
 constexpr size_t kChunkBytes = static_cast<size_t>(kThreads) * kVecPerThread * 16;
 
