@@ -548,14 +548,15 @@ __device__ __forceinline__ void produce_item(const GdnArgs& args, float* buf, fl
 // kStashSlots live branch points). FUSED: one layer in its own order; the
 // staging computes q, k and v from the conv input (conv, SiLU, split, q/k L2
 // norm) instead of loading them.
-template <int DK, int NW, int NP, typename TIn, bool TREE, bool RELOAD, bool CAPTURE, bool FUSED>
-__global__ __launch_bounds__((NW + NP) * 64) void gdn_span_kernel(const GdnArgs args) {
+template <int DK, int NW, int NP, typename TIn, bool TREE, bool RELOAD, bool CAPTURE, bool FUSED, int NX>
+__global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const GdnArgs args) {
   constexpr int LPR = kLanesPerRow;
   constexpr int RPW = 64 / LPR;          // rows per wave
   constexpr int RPB = RPW * NW;          // rows per unit
   constexpr int NCH = DK / (4 * LPR);    // float4 chunks per lane
   static_assert(NCH >= 1 && DK % (4 * LPR) == 0, "lane mapping");
   static_assert(NP == 0 || (!TREE && CAPTURE), "only the capturing chain kernel has producer waves");
+  static_assert(NX == 0 || NP == 0, "staging helpers belong to the single-role kernel");
   constexpr int POS_FLOATS = pos_floats(DK, RPB, TREE);
   constexpr int NC = NW * 64;            // consumer threads
 
@@ -584,24 +585,29 @@ __global__ __launch_bounds__((NW + NP) * 64) void gdn_span_kernel(const GdnArgs 
 
   if constexpr (NP == 0) {
     f32x4* const stash = reinterpret_cast<f32x4*>(lds + staging_floats(args.window, POS_FLOATS));
+    // NX further waves only help stage each window (they own no rows).
+    const bool owner = NX == 0 || tid < NC;   // wave-uniform
     for (int W = blockIdx.x; W < args.n_units; W += args.n_blocks) {
       const Unit u = unit_of(args, W, RPB);
       const float* init = initial_rows<DK>(args, u);
       if (init == nullptr) continue;   // block-uniform: every thread has the same request
-      init += static_cast<size_t>(row_blk) * DK;
+      if (owner) {
+        init += static_cast<size_t>(row_blk) * DK;
 #pragma unroll
-      for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(init + 4 * (li + LPR * m));
+        for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(init + 4 * (li + LPR * m));
+      }
       float* const ckpt_row0 = ckpt_of(u);
       float* const out_r = out_of(u);
       for (int t0 = 0; t0 < T; t0 += kWindow) {
         const int tn = min(kWindow, T - t0);
         __syncthreads();  // LDS reads of the previous window (or unit) are done
-        stage_window<DK, NC, RPB, POS_FLOATS, TIn, TREE, FUSED>(args, lds, u, t0, tn, tid);
+        stage_window<DK, NC + NX * 64, RPB, POS_FLOATS, TIn, TREE, FUSED>(args, lds, u, t0, tn, tid);
         __syncthreads();
-        run_positions<DK, NW, RPB, POS_FLOATS, TREE, RELOAD, CAPTURE>(lds, stash, s, t0, tn, ckpt_row0, out_r,
-                                                                      pos_stride, out_stride);
+        if (owner)
+          run_positions<DK, NW, RPB, POS_FLOATS, TREE, RELOAD, CAPTURE>(lds, stash, s, t0, tn, ckpt_row0, out_r,
+                                                                        pos_stride, out_stride);
       }
-      if (!CAPTURE) {
+      if (!CAPTURE && owner) {
         float* state_row = args.state + (static_cast<size_t>(u.r) * Hv + u.h) * head_elems +
                            static_cast<size_t>(u.row0 + row_blk) * DK;
 #pragma unroll
@@ -675,15 +681,15 @@ __global__ __launch_bounds__((NW + NP) * 64) void gdn_span_kernel(const GdnArgs 
 
 // Launch through hipExtLaunchKernelGGL so that optional timing events are
 // recorded by the dispatch itself (no extra stream commands between kernels).
-template <int DK, int NW, int NP, typename TIn, bool TREE, bool RELOAD, bool CAPTURE, bool FUSED>
+template <int DK, int NW, int NP, typename TIn, bool TREE, bool RELOAD, bool CAPTURE, bool FUSED, int NX = 0>
 hipError_t launch_one(GdnArgs& args, int grid, int n_slots, hipStream_t stream, hipEvent_t start,
                       hipEvent_t stop) {
   constexpr int RPB = (64 / kLanesPerRow) * NW;
   args.n_blocks = grid;
   const size_t lds = NP > 0 ? pipelined_bytes(DK, RPB, args.window)
                             : staging_bytes(DK, RPB, args.window, TREE) + (TREE ? n_slots * slot_bytes(DK, NW) : 0);
-  hipExtLaunchKernelGGL((gdn_span_kernel<DK, NW, NP, TIn, TREE, RELOAD, CAPTURE, FUSED>), dim3(grid),
-                        dim3((NW + NP) * 64), lds, stream, start, stop, 0, args);
+  hipExtLaunchKernelGGL((gdn_span_kernel<DK, NW, NP, TIn, TREE, RELOAD, CAPTURE, FUSED, NX>), dim3(grid),
+                        dim3((NW + NP + NX) * 64), lds, stream, start, stop, 0, args);
   return launch_error();
 }
 
@@ -695,10 +701,15 @@ hipError_t launch_mode(GdnArgs& args, Mode mode, int grid, int n_slots, hipStrea
   // f32 conv inputs need twice the registers of bf16 ones in the fused
   // staging; that variant keeps the single-role kernel (no spills).
   constexpr int NP = (FUSED && sizeof(TIn) == 4) ? 0 : kProducerWaves;
+  // Trees in blocks of 16-row units (each block then usually holds one
+  // unit, whose window its 4 waves would stage alone) take 4 staging-only
+  // waves.
+  constexpr int NXT = NW == 4 ? 4 : 0;
   switch (mode) {
     case Mode::kTreeReload:
-      return launch_one<DK, NW, 0, TIn, true, true, true, FUSED>(args, grid, n_slots, s, e0, e1);
-    case Mode::kTree: return launch_one<DK, NW, 0, TIn, true, false, true, FUSED>(args, grid, n_slots, s, e0, e1);
+      return launch_one<DK, NW, 0, TIn, true, true, true, FUSED, NXT>(args, grid, n_slots, s, e0, e1);
+    case Mode::kTree:
+      return launch_one<DK, NW, 0, TIn, true, false, true, FUSED, NXT>(args, grid, n_slots, s, e0, e1);
     case Mode::kChain: return launch_one<DK, NW, NP, TIn, false, false, true, FUSED>(args, grid, 0, s, e0, e1);
     default:
       // The fused layer always captures (checked by the entry point).
