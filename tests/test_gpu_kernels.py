@@ -135,6 +135,37 @@ def test_gdn_random_long_trees(hrs):
         check_gdn_vs_oracle(units, ck, out, parents=par[None], what=f"random tree T={T}")
 
 
+def _mixed_trees(rng, n_req, T):
+    """Per request a random tree of T positions: uniform parents (wide, many
+    live branch points), a deep chain with side branches, or a pure chain."""
+    out = []
+    for r in range(n_req):
+        kind = r % 3
+        if kind == 0:
+            par = [-1] + [int(rng.integers(0, i)) for i in range(1, T)]
+        elif kind == 1:
+            par = [-1] + [i - 1 if rng.random() < 0.7 else int(rng.integers(0, i)) for i in range(1, T)]
+        else:
+            par = list(range(-1, T - 1))
+        out.append(par)
+    return np.asarray(out, dtype=np.int32)
+
+
+def test_gdn_tree_batch_split_over_launches(hrs):
+    """20 requests of 64-position trees: the tree geometry of at most 16
+    requests fits one launch, so the span runs as a 16-request launch (one
+    block per CU) and a 4-request launch (16-row units with staging-only
+    waves); wide trees need the checkpoint-reload variant."""
+    rng = np.random.default_rng(71)
+    R, T = 20, 64
+    w = scaled(QWEN_LAYER_CHAIN, n_req=R, n_kheads=2, n_vheads=4, n_pos=T)
+    units = [gen_unit(w, 0, r) for r in range(R)]
+    parents = _mixed_trees(rng, R, T)
+    say(f"tree batch R={R} T={T}")
+    ck, out, _ = gpu_gdn(hrs, units, parent=parents)
+    check_gdn_vs_oracle(units, ck, out, parents=parents, what="tree batch")
+
+
 def test_gdn_tree_with_chain_parent_equals_chain(hrs):
     w = scaled(QWEN_LAYER_CHAIN, n_req=2)
     units = [gen_unit(w, 0, r) for r in range(2)]
@@ -256,6 +287,22 @@ def test_conv_tree_vs_oracle(hrs):
         oy, ock = oconv.conv_span(u.x, wt, u.conv_state, parents[r])
         assert_tiles(y[r], oy, 1, "conv tree y")
         assert np.array_equal(ck[r], ock)
+
+
+def test_conv_tree_batch_split_over_launches(hrs):
+    """20 requests of 64-position trees: the window-source tables of at most
+    16 requests fit one launch."""
+    rng = np.random.default_rng(72)
+    R, T = 20, 64
+    w = scaled(QWEN_LAYER_CHAIN, n_req=R, n_pos=T, conv_channels=1024)
+    units = [gen_unit(w, 0, r) for r in range(R)]
+    wt = gen_conv_weight(w, 0)
+    parents = _mixed_trees(rng, R, T)
+    y, ck, _ = gpu_conv(hrs, units, wt, parent=parents, silu=True)
+    for r, u in enumerate(units):
+        oy, ock = oconv.conv_span(u.x, wt, u.conv_state, parents[r], silu=True)
+        assert_tiles(y[r], oy, 1, f"conv tree batch y r={r}")
+        assert np.array_equal(ck[r], ock), f"conv tree batch checkpoints r={r}"
 
 
 @pytest.mark.parametrize("T", [1, 2, 5])
