@@ -190,6 +190,55 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+class _Checks:
+    """Rejects, before anything is launched, a tensor that the kernels would
+    read or write out of bounds or as the wrong type. Calls check each
+    tensor's shape (the library takes every size from the leading tensor),
+    dtype and layout; on_gpu() then checks that all of them are on the GPU."""
+
+    def __init__(self):
+        self.seen = []
+
+    def __call__(self, name: str, t, shape=None, dtypes=None, optional: bool = False) -> None:
+        if t is None:
+            if optional:
+                return
+            raise ValueError(f"{name} is required")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if dtypes is not None and t.dtype not in dtypes:
+            raise TypeError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        self.seen.append((name, t))
+
+    def status(self, status, optional: bool = True) -> None:
+        self("status", status, None, _i32t(), optional)
+        if status is not None and status.numel() < 1:
+            raise ValueError("status needs at least one int32")
+
+    def on_gpu(self) -> None:
+        for name, t in self.seen:
+            if not t.is_cuda:
+                raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _in_dtypes(name: str, t):
+    """The input dtype of a call (f32 or bf16), checked on its leading tensor."""
+    torch = _torch()
+    if t.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"{name}: dtype {t.dtype}, expected torch.float32 or torch.bfloat16")
+    return (t.dtype,)
+
+
+def _f32():
+    return (_torch().float32,)
+
+
+def _i32t():
+    return (_torch().int32,)
+
+
 def _stream(stream) -> Optional[int]:
     torch = _torch()
     if stream is None:
@@ -242,6 +291,17 @@ def gdn_verify_span(q, k, v, a, b, state, ckpt, out, parent=None, q_scale: float
     kernel dispatch itself (gdn_verify_span_timed)."""
     R, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
+    dt = _in_dtypes("q", q)
+    chk = _Checks()
+    chk("q", q, None, dt)
+    chk("k", k, (R, T, Hk, dk), dt)
+    chk("v", v, (R, T, Hv, dv), dt)
+    chk("a", a, (R, T, Hv), dt)
+    chk("b", b, (R, T, Hv), dt)
+    chk("state", state, (R, Hv, dv, dk), _f32())
+    chk("ckpt", ckpt, (R, T, Hv, dv, dk), _f32(), optional=True)
+    chk("out", out, (R, T, Hv, dv), _f32())
+    chk.on_gpu()
     par, par_p = _parent_array(parent, R, T)
     d = GdnDesc(R, T, Hk, Hv, dk, dv, _dtype_code(q), float(q_scale),
                 HRS_TREE if parent is not None else HRS_CHAIN, par_p)
@@ -261,6 +321,20 @@ def gdn_verify_span_from(src_ckpt, src_node, q, k, v, a, b, ckpt, out, parent=No
     both on the device) instead of a state buffer."""
     R, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
+    dt = _in_dtypes("q", q)
+    chk = _Checks()
+    chk("q", q, None, dt)
+    chk("k", k, (R, T, Hk, dk), dt)
+    chk("v", v, (R, T, Hv, dv), dt)
+    chk("a", a, (R, T, Hv), dt)
+    chk("b", b, (R, T, Hv), dt)
+    chk("src_ckpt", src_ckpt, None, _f32())
+    chk("src_ckpt", src_ckpt, (R, src_ckpt.shape[1], Hv, dv, dk), _f32())
+    chk("src_node", src_node, (R,), _i32t())
+    chk("ckpt", ckpt, (R, T, Hv, dv, dk), _f32())
+    chk("out", out, (R, T, Hv, dv), _f32())
+    chk.status(status)
+    chk.on_gpu()
     par, par_p = _parent_array(parent, R, T)
     d = GdnDesc(R, T, Hk, Hv, dk, dv, _dtype_code(q), float(q_scale),
                 HRS_TREE if parent is not None else HRS_CHAIN, par_p)
@@ -276,6 +350,18 @@ def gdn_span_chunked(q, k, v, a, b, state, ckpt, out, q_scale: float = 1.0, log_
     in place. log_gates: `a` holds log decays. out may be f32 or bf16."""
     R, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
+    torch = _torch()
+    dt = _in_dtypes("q", q)
+    chk = _Checks()
+    chk("q", q, None, dt)
+    chk("k", k, (R, T, Hk, dk), dt)
+    chk("v", v, (R, T, Hv, dv), dt)
+    chk("a", a, (R, T, Hv), dt)
+    chk("b", b, (R, T, Hv), dt)
+    chk("state", state, (R, Hv, dv, dk), _f32())
+    chk("ckpt", ckpt, (R, T, Hv, dv, dk), _f32(), optional=True)
+    chk("out", out, (R, T, Hv, dv), (torch.float32, torch.bfloat16))
+    chk.on_gpu()
     g = GdnDesc(R, T, Hk, Hv, dk, dv, _dtype_code(q), float(q_scale), HRS_CHAIN, None)
     d = ChunkedDesc(g, int(bool(log_gates)), _dtype_code(out))
     st = lib.gdn_span_chunked(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(state), _ptr(ckpt),
@@ -294,6 +380,24 @@ def gdn_layer_verify_span(x, conv_w, conv_state, a, b, ckpt, out, n_kheads: int,
     R, T, C = x.shape
     Hv = a.shape[2]
     dv = (C - 2 * n_kheads * d_k) // Hv
+    if Hv < 1 or C != 2 * n_kheads * d_k + Hv * dv:
+        raise ValueError(f"x: {C} channels do not split into q, k ({n_kheads} x {d_k} each) and {Hv} v heads")
+    dt = _in_dtypes("x", x)
+    chk = _Checks()
+    chk("x", x, None, dt)
+    chk("conv_w", conv_w, (C, conv_w.shape[1] if conv_w is not None and conv_w.dim() == 2 else 4), dt)
+    chk("conv_state", conv_state, (R, conv_w.shape[1] - 1, C), dt)
+    chk("a", a, (R, T, Hv), dt)
+    chk("b", b, (R, T, Hv), dt)
+    chk("ckpt", ckpt, (R, T, Hv, dv, d_k), _f32())
+    chk("out", out, (R, T, Hv, dv), _f32())
+    chk("state", state, (R, Hv, dv, d_k), _f32(), optional=True)
+    if src_ckpt is not None:
+        chk("src_ckpt", src_ckpt, None, _f32())
+        chk("src_ckpt", src_ckpt, (R, src_ckpt.shape[1], Hv, dv, d_k), _f32())
+        chk("src_node", src_node, (R,), _i32t())
+    chk.status(status)
+    chk.on_gpu()
     par, par_p = _parent_array(parent, R, T)
     g = GdnDesc(R, T, n_kheads, Hv, d_k, dv, _dtype_code(x), float(q_scale),
                 HRS_TREE if parent is not None else HRS_CHAIN, par_p)
@@ -309,7 +413,15 @@ def gdn_layer_verify_span(x, conv_w, conv_state, a, b, ckpt, out, n_kheads: int,
 def conv1d_verify_span_nocapture(x, w, conv_state, y, parent=None, silu: bool = False, stream=None):
     """conv output y only; conv_state [R,W-1,C] is read only."""
     R, T, C = x.shape
-    W = w.shape[1]
+    dt = _in_dtypes("x", x)
+    chk = _Checks()
+    chk("x", x, None, dt)
+    chk("w", w, None, dt)
+    W = w.shape[1] if w.dim() == 2 else 0
+    chk("w", w, (C, W), dt)
+    chk("conv_state", conv_state, (R, W - 1, C), dt)
+    chk("y", y, (R, T, C), _f32())
+    chk.on_gpu()
     par, par_p = _parent_array(parent, R, T)
     d = ConvDesc(R, T, C, W, _dtype_code(x), int(bool(silu)), HRS_TREE if parent is not None else HRS_CHAIN, par_p)
     st = lib.conv1d_verify_span_nocapture(ctypes.byref(d), _ptr(x), _ptr(w), _ptr(conv_state), _ptr(y),
@@ -320,6 +432,15 @@ def conv1d_verify_span_nocapture(x, w, conv_state, y, parent=None, silu: bool = 
 def conv_state_advance(x, conv_state, path, accept_len, status=None, stream=None):
     """x [L,R,T,C]; conv_state [L,R,W-1,C]; path [R,T], accept_len [R] int32 (device)."""
     L, R, T, C = x.shape
+    dt = _in_dtypes("x", x)
+    chk = _Checks()
+    chk("x", x, None, dt)
+    chk("conv_state", conv_state, None, dt)
+    chk("conv_state", conv_state, (L, R, conv_state.shape[2], C), dt)
+    chk("path", path, (R, T), _i32t())
+    chk("accept_len", accept_len, (R,), _i32t())
+    chk.status(status)
+    chk.on_gpu()
     d = ConvAdvanceDesc(L, R, T, C, conv_state.shape[2] + 1, _dtype_code(x))
     st = lib.conv_state_advance(ctypes.byref(d), _ptr(x), _ptr(conv_state), _ptr(path), _ptr(accept_len),
                                 _ptr(status), _stream(stream))
@@ -330,7 +451,16 @@ def conv1d_verify_span(x, w, conv_state, conv_ckpt, y, parent=None, silu: bool =
     """x [R,T,C]; w [C,W]; conv_state [R,W-1,C]; conv_ckpt [R,T,W-1,C] or None
     (same dtype as x); y [R,T,C] f32. parent: None (chain) or host [R,T]/[T]."""
     R, T, C = x.shape
-    W = w.shape[1]
+    dt = _in_dtypes("x", x)
+    chk = _Checks()
+    chk("x", x, None, dt)
+    chk("w", w, None, dt)
+    W = w.shape[1] if w.dim() == 2 else 0
+    chk("w", w, (C, W), dt)
+    chk("conv_state", conv_state, (R, W - 1, C), dt)
+    chk("conv_ckpt", conv_ckpt, (R, T, W - 1, C), dt, optional=True)
+    chk("y", y, (R, T, C), _f32())
+    chk.on_gpu()
     par, par_p = _parent_array(parent, R, T)
     d = ConvDesc(R, T, C, W, _dtype_code(x), int(bool(silu)),
                  HRS_TREE if parent is not None else HRS_CHAIN, par_p)
@@ -357,6 +487,13 @@ def accept_greedy(logits, tokens, argmax, accept_node, accept_len, path, bonus, 
     argmax [R,T], accept_node [R], accept_len [R], path [R,T], bonus [R];
     workspace: device tensor of at least accept_greedy_workspace_bytes."""
     R, T, V = logits.shape
+    chk = _Checks()
+    chk("logits", logits, None, _in_dtypes("logits", logits))
+    for name, t, shape in (("tokens", tokens, (R, T)), ("argmax", argmax, (R, T)), ("accept_node", accept_node, (R,)),
+                           ("accept_len", accept_len, (R,)), ("path", path, (R, T)), ("bonus", bonus, (R,))):
+        chk(name, t, shape, _i32t())
+    chk("workspace", workspace)
+    chk.on_gpu()
     d, _keep = accept_desc(R, T, V, _dtype_code(logits), parent)
     nbytes = workspace.numel() * workspace.element_size()
     st = lib.accept_greedy(ctypes.byref(d), _ptr(logits), _ptr(tokens), _ptr(argmax), _ptr(accept_node),
@@ -370,19 +507,40 @@ def rollback_restore(ckpt, state, conv_ckpt, conv_state, accept_node, status, st
     [L,R,T,W-1,C] -> conv_state [L,R,W-1,C] (both None to skip);
     accept_node [R] int32 device; status [>=1] int32 device."""
     L, R, T, Hv, dv, dk = ckpt.shape
+    chk = _Checks()
+    chk("ckpt", ckpt, None, _f32())
+    chk("state", state, (L, R, Hv, dv, dk), _f32())
+    chk("accept_node", accept_node, (R,), _i32t())
+    chk.status(status, optional=False)
+    if (conv_ckpt is None) != (conv_state is None):
+        raise ValueError("conv_ckpt and conv_state go together")
     if conv_ckpt is not None:
+        cdt_t = _in_dtypes("conv_ckpt", conv_ckpt)
+        chk("conv_ckpt", conv_ckpt, None, cdt_t)
+        if conv_ckpt.dim() != 5 or tuple(conv_ckpt.shape[:3]) != (L, R, T):
+            raise ValueError(f"conv_ckpt: shape {tuple(conv_ckpt.shape)}, expected ({L}, {R}, {T}, W-1, C)")
         C, W1 = conv_ckpt.shape[4], conv_ckpt.shape[3]
+        chk("conv_state", conv_state, (L, R, W1, C), cdt_t)
         cdt = _dtype_code(conv_ckpt)
     else:
         C, W1, cdt = 0, 0, HRS_F32
+    chk.on_gpu()
     d = RollbackDesc(L, R, T, Hv, dk, dv, C, W1 + 1 if conv_ckpt is not None else 0, cdt)
     st = lib.rollback_restore(ctypes.byref(d), _ptr(ckpt), _ptr(state), _ptr(conv_ckpt), _ptr(conv_state),
                               _ptr(accept_node), _ptr(status), _stream(stream))
     _check(st, "rollback_restore")
 
 
-def _ring_desc(ring, n_packed_rows: int, runs: Sequence[tuple]):
+def _ring_desc(ring, packed, runs: Sequence[tuple]):
     n_rings, S, D = ring.shape
+    dt = _in_dtypes("ring", ring)
+    chk = _Checks()
+    chk("ring", ring, None, dt)
+    chk("packed", packed, None, dt)
+    if packed.dim() != 2 or packed.shape[1] != D:
+        raise ValueError(f"packed: shape {tuple(packed.shape)}, expected (rows, {D})")
+    chk.on_gpu()
+    n_packed_rows = packed.shape[0]
     arr = (RingRun * max(1, len(runs)))(*[RingRun(*map(int, r)) for r in runs])
     d = RingDesc(n_rings, S, D, _dtype_code(ring), n_packed_rows, len(runs), arr)
     return d, arr
@@ -390,10 +548,10 @@ def _ring_desc(ring, n_packed_rows: int, runs: Sequence[tuple]):
 
 def ring_set_2d(ring, packed, runs, stream=None):
     """ring [n_rings,S,D]; packed [N,D]; runs: (ring_id, start_pos, n_rows, packed_row)."""
-    d, _keep = _ring_desc(ring, packed.shape[0], runs)
+    d, _keep = _ring_desc(ring, packed, runs)
     _check(lib.ring_set_2d(ctypes.byref(d), _ptr(ring), _ptr(packed), _stream(stream)), "ring_set_2d")
 
 
 def ring_get_2d(ring, packed, runs, stream=None):
-    d, _keep = _ring_desc(ring, packed.shape[0], runs)
+    d, _keep = _ring_desc(ring, packed, runs)
     _check(lib.ring_get_2d(ctypes.byref(d), _ptr(ring), _ptr(packed), _stream(stream)), "ring_get_2d")

@@ -361,3 +361,48 @@ def test_chunked_entry_rejections():
     assert call(n_pos=(1 << 20)) in (E.HRS_EDEVICE, E.HRS_OK)
     assert call(ckpt=FAKE, out_dt=hrs.HRS_BF16, log_gates=1) in (E.HRS_EDEVICE, E.HRS_OK)
     assert call() in (E.HRS_EDEVICE, E.HRS_OK)
+
+
+def test_binding_rejects_mismatched_tensors_before_launch():
+    """The binding checks every tensor against the sizes the library takes from
+    the leading one (and dtype, layout and device) before anything launches,
+    so a wrong tensor raises instead of being read or written out of bounds."""
+    import torch
+    R, T, Hk, Hv, d = 2, 3, 1, 2, 64
+    f, h = torch.float32, torch.bfloat16
+    def span(**over):
+        t = dict(q=torch.zeros(R, T, Hk, d, dtype=h), k=torch.zeros(R, T, Hk, d, dtype=h),
+                 v=torch.zeros(R, T, Hv, d, dtype=h), a=torch.zeros(R, T, Hv, dtype=h), b=torch.zeros(R, T, Hv, dtype=h),
+                 state=torch.zeros(R, Hv, d, d, dtype=f), ckpt=torch.zeros(R, T, Hv, d, d, dtype=f),
+                 out=torch.zeros(R, T, Hv, d, dtype=f))
+        t.update(over)
+        hrs.gdn_verify_span(t["q"], t["k"], t["v"], t["a"], t["b"], t["state"], t["ckpt"], t["out"])
+    with pytest.raises(ValueError, match="v: shape"):
+        span(v=torch.zeros(R, T + 1, Hv, d, dtype=h))
+    with pytest.raises(ValueError, match="out: shape"):
+        span(out=torch.zeros(R, T, Hv, d - 1, dtype=f))
+    with pytest.raises(TypeError, match="a: dtype"):
+        span(a=torch.zeros(R, T, Hv, dtype=f))
+    with pytest.raises(TypeError, match="state: dtype"):
+        span(state=torch.zeros(R, Hv, d, d, dtype=h))
+    with pytest.raises(ValueError, match="contiguous"):
+        span(b=torch.zeros(R, Hv, T, dtype=h).transpose(1, 2))
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        span()                                   # right shapes, host memory
+    with pytest.raises(ValueError, match="state is required"):
+        span(state=None)
+    x = torch.zeros(R, T, 64, dtype=h)
+    with pytest.raises(ValueError, match="conv_state: shape"):
+        hrs.conv1d_verify_span(x, torch.zeros(64, 4, dtype=h), torch.zeros(R, 4, 64, dtype=h), None,
+                               torch.zeros(R, T, 64, dtype=f))
+    with pytest.raises(ValueError, match="tokens: shape"):
+        hrs.accept_greedy(torch.zeros(R, T, 64, dtype=h), torch.zeros(R, T + 1, dtype=torch.int32),
+                          *[torch.zeros(R, T, dtype=torch.int32)] + [torch.zeros(R, dtype=torch.int32)] * 2 +
+                          [torch.zeros(R, T, dtype=torch.int32), torch.zeros(R, dtype=torch.int32),
+                           torch.zeros(64, dtype=torch.int64)])
+    with pytest.raises(ValueError, match="go together"):
+        hrs.rollback_restore(torch.zeros(1, R, T, Hv, d, d), torch.zeros(1, R, Hv, d, d), None,
+                             torch.zeros(1, R, 3, 64, dtype=h), torch.zeros(R, dtype=torch.int32),
+                             torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="packed: shape"):
+        hrs.ring_set_2d(torch.zeros(2, 8, 16, dtype=h), torch.zeros(3, 8, dtype=h), [(0, 0, 3, 0)])
