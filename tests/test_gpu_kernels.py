@@ -166,6 +166,34 @@ def test_gdn_tree_batch_split_over_launches(hrs):
     check_gdn_vs_oracle(units, ck, out, parents=parents, what="tree batch")
 
 
+def test_gdn_random_shapes(hrs):
+    """Seeded sweep over shapes the library accepts (d_k 64/128, d_v a
+    multiple of 16 up to 256, 1-4 value heads per key head, 1-5 requests,
+    1-40 positions, chain or random tree, bf16 or f32 inputs), each against
+    the oracle: launch shapes and unit counts beyond the model's."""
+    rng = np.random.default_rng(2024)
+    for i in range(12):
+        dk = int(rng.choice([64, 128]))
+        dv = int(rng.choice([16, 32, 48, 64, 96, 128, 256]))
+        Hk = int(rng.choice([1, 2, 3]))
+        Hv = Hk * int(rng.choice([1, 2, 4]))
+        R = int(rng.integers(1, 6))
+        T = int(rng.integers(1, 41))
+        dt = BF16 if rng.random() < 0.6 else F32
+        tree = T > 2 and rng.random() < 0.5
+        w = scaled(QWEN_LAYER_CHAIN, n_req=R, n_pos=T, n_kheads=Hk, n_vheads=Hv, d_k=dk, d_v=dv, dtype=dt,
+                   conv_channels=16, seed=100 + i)
+        units = [gen_unit(w, 0, r) for r in range(R)]
+        parents = None
+        if tree:
+            parents = np.array([[-1] + [int(rng.integers(0, t)) for t in range(1, T)] for _ in range(R)],
+                               dtype=np.int32)
+        what = f"shape {i}: R={R} T={T} Hk={Hk} Hv={Hv} dk={dk} dv={dv} {dt} {'tree' if tree else 'chain'}"
+        say(what)
+        ck, out, _ = gpu_gdn(hrs, units, parent=parents)
+        check_gdn_vs_oracle(units, ck, out, parents=parents, what=what)
+
+
 def test_gdn_tree_with_chain_parent_equals_chain(hrs):
     w = scaled(QWEN_LAYER_CHAIN, n_req=2)
     units = [gen_unit(w, 0, r) for r in range(2)]
