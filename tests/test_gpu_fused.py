@@ -191,3 +191,30 @@ def test_layer_persistent_dk64(hrs):
     w = layer_workload(QWEN_LAYER_CHAIN, n_req=4, n_pos=20, d_k=64, d_v=64)
     units, wc, ck, out = run_layer(hrs, w, q_scale=0.125)
     check_layer(w, units, wc, ck, out, q_scale=0.125, what="fused persistent dk64")
+
+
+def test_layer_random_shapes(hrs):
+    """Seeded sweep over layer shapes (d_k 64/128, d_v 16-128, 1-4 value
+    heads per key head, 1-4 requests, 1-40 positions, chain or random tree,
+    bf16 or f32, SiLU on or off), each against the fused-layer oracle."""
+    rng = np.random.default_rng(4048)
+    for i in range(8):
+        dk = int(rng.choice([64, 128]))
+        dv = int(rng.choice([16, 32, 48, 64, 128]))
+        Hk = int(rng.choice([1, 2]))
+        Hv = Hk * int(rng.choice([1, 2, 4]))
+        R = int(rng.integers(1, 5))
+        T = int(rng.integers(1, 41))
+        dt = TINY_CHAIN.dtype if rng.random() < 0.4 else QWEN_LAYER_CHAIN.dtype
+        tree = T > 2 and rng.random() < 0.5
+        silu = bool(rng.random() < 0.7)
+        q_scale = float(2.0 ** -int(rng.integers(0, 4)))
+        w = layer_workload(TINY_CHAIN, n_req=R, n_pos=T, n_kheads=Hk, n_vheads=Hv, d_k=dk, d_v=dv, dtype=dt,
+                           seed=300 + i)
+        parents = None
+        if tree:
+            parents = [np.array([-1] + [int(rng.integers(0, t)) for t in range(1, T)], dtype=np.int32)
+                       for _ in range(R)]
+        what = f"layer shape {i}: R={R} T={T} Hk={Hk} Hv={Hv} dk={dk} dv={dv} {dt} silu={silu}"
+        units, wc, ck, out = run_layer(hrs, w, parents=parents, q_scale=q_scale, silu=silu)
+        check_layer(w, units, wc, ck, out, parents=parents, q_scale=q_scale, silu=silu, what=what)
