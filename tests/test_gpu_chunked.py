@@ -162,3 +162,25 @@ def test_chunked_bf16_outputs(hrs):
     for r, u in enumerate(units):
         _, oout = ogdn.gdn_span(u.state, u.q, u.k, u.v, u.a, u.b, None, 0.5)
         assert_tiles(bf16_to_f32(o16[r]), oout, 1, f"bf16 out r={r}", tol=2.0 ** -8)
+
+
+def test_chunked_random_shapes(hrs):
+    """Seeded sweep: 1-4 requests, 1-300 positions (several chunks, ragged
+    last chunk), 1-4 value heads per key head, capture on or off, bf16 or f32
+    inputs, power-of-two q scales; each against the GDN oracle."""
+    rng = np.random.default_rng(777)
+    for i in range(8):
+        Hk = int(rng.choice([1, 2]))
+        Hv = Hk * int(rng.choice([1, 2, 4]))
+        R = int(rng.integers(1, 5))
+        T = int(rng.integers(1, 301))
+        dt = F32 if rng.random() < 0.3 else BF16
+        capture = bool(rng.random() < 0.5)
+        q_scale = float(2.0 ** -int(rng.integers(0, 4)))
+        w = scaled(QWEN_LAYER_CHAIN, n_req=R, n_pos=T, n_kheads=Hk, n_vheads=Hv, dtype=dt, conv_channels=16,
+                   seed=500 + i)
+        units = [gen_unit(w, 0, r) for r in range(R)]
+        what = f"chunked shape {i}: R={R} T={T} Hk={Hk} Hv={Hv} {dt} capture={capture}"
+        say(what)
+        ck, out, state = run(hrs, units, capture, q_scale=q_scale)
+        check(units, ck, out, state, capture, q_scale=q_scale, what=what)
