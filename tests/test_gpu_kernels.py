@@ -333,6 +333,34 @@ def test_conv_tree_batch_split_over_launches(hrs):
         assert np.array_equal(ck[r], ock), f"conv tree batch checkpoints r={r}"
 
 
+def test_conv_random_shapes(hrs):
+    """Seeded sweep: channels 8-8200 (partial blocks), 1-64 positions, 1-4
+    requests, chain or random tree, SiLU on or off, bf16 or f32; outputs
+    within the tolerance and checkpoints bit-exact against the oracle."""
+    rng = np.random.default_rng(909)
+    for i in range(10):
+        C = 8 * int(rng.integers(1, 1026))
+        T = int(rng.integers(1, 65))
+        R = int(rng.integers(1, 5))
+        dt = F32 if rng.random() < 0.3 else BF16
+        silu = bool(rng.random() < 0.5)
+        tree = T > 2 and rng.random() < 0.5
+        w = scaled(QWEN_LAYER_CHAIN, n_req=R, n_pos=T, conv_channels=C, dtype=dt, n_kheads=1, n_vheads=1, d_k=64,
+                   d_v=16, seed=700 + i)
+        units = [gen_unit(w, 0, r) for r in range(R)]
+        wt = gen_conv_weight(w, 0)
+        parents = None
+        if tree:
+            parents = np.array([[-1] + [int(rng.integers(0, t)) for t in range(1, T)] for _ in range(R)],
+                               dtype=np.int32)
+        say(f"conv shape {i}: R={R} T={T} C={C} {dt} silu={silu} {'tree' if tree else 'chain'}")
+        y, ck, _ = gpu_conv(hrs, units, wt, parent=parents, silu=silu)
+        for r, u in enumerate(units):
+            oy, ock = oconv.conv_span(u.x, wt, u.conv_state, None if parents is None else parents[r], silu=silu)
+            assert_tiles(y[r], oy, 1, f"conv shape {i} y r={r}")
+            assert np.array_equal(ck[r], ock), f"conv shape {i} checkpoints r={r}"
+
+
 @pytest.mark.parametrize("T", [1, 2, 5])
 def test_conv_in_place_decode(hrs, T):
     w = scaled(QWEN_LAYER_CHAIN, n_req=2, n_pos=T, conv_channels=2048)
