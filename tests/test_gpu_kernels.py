@@ -476,9 +476,12 @@ def test_accept_special_values(hrs, dtype):
 # rollback
 
 
-def test_rollback_copies_checkpoint_and_flags_bad_index(hrs):
+@pytest.mark.parametrize("Hv,dv,dk,C", [(4, 64, 64, 64),      # state exactly one 64 KiB block
+                                          (3, 48, 64, 24),      # 36 KiB state: one partial block
+                                          (3, 112, 128, 1000)])  # 2.6 blocks, odd conv width
+def test_rollback_copies_checkpoint_and_flags_bad_index(hrs, Hv, dv, dk, C):
     torch = _torch()
-    L, R, T, Hv, dv, dk, C = 2, 3, 5, 4, 64, 64, 64
+    L, R, T = 2, 3, 5
     rng = np.random.default_rng(4)
     ckpt = rng.standard_normal((L, R, T, Hv, dv, dk)).astype(np.float32)
     state0 = rng.standard_normal((L, R, Hv, dv, dk)).astype(np.float32)
