@@ -436,6 +436,88 @@ __device__ __forceinline__ void run_positions(const float* buf, f32x4* stash, f3
       o = group_sum<LPR>(o);
       if (li == 0) out_r[static_cast<size_t>(t) * out_stride] = o;
     }
+  } else if constexpr (NW == 4) {
+    // Blocks of one 16-row unit (launches too small to give every CU more
+    // than one unit): each SIMD runs one row-owning wave, so the position
+    // loop is a dependent chain with nothing to hide its latency. It is
+    // software-pipelined: position t+1's k, a, b and v and position t's q
+    // are read from LDS during position t, and o_{t-1} = S_{t-1} q_{t-1} is
+    // summed beside u_t = S_{t-1} k_t (the same state; two independent
+    // sums whose butterflies interleave). Every sum keeps its association
+    // order, so the results are bit-identical to the loop below.
+    f32x4 kk[NCH], qp[NCH];
+    float at = 0.0f, bt = 0.0f, vt = 0.0f;
+    auto fetch_kabv = [&](int tt, f32x4 (&kd)[NCH], float& ad, float& bd, float& vd) {
+      const float* lp = buf + tt * POS_FLOATS;
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) kd[m] = *reinterpret_cast<const f32x4*>(lp + 4 * (li + LPR * m));
+      ad = lp[2 * DK + RPB];
+      bd = lp[2 * DK + RPB + 1];
+      vd = lp[2 * DK + row_blk];
+    };
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) qp[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (tn > 0) fetch_kabv(0, kk, at, bt, vt);
+    for (int tt = 0; tt < tn; ++tt) {
+      const int t = t0 + tt;
+      float u = 0.0f, o = 0.0f;
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) {
+        u = __builtin_fmaf(s[m].x, kk[m].x, u);
+        o = __builtin_fmaf(s[m].x, qp[m].x, o);
+        u = __builtin_fmaf(s[m].y, kk[m].y, u);
+        o = __builtin_fmaf(s[m].y, qp[m].y, o);
+        u = __builtin_fmaf(s[m].z, kk[m].z, u);
+        o = __builtin_fmaf(s[m].z, qp[m].z, o);
+        u = __builtin_fmaf(s[m].w, kk[m].w, u);
+        o = __builtin_fmaf(s[m].w, qp[m].w, o);
+      }
+      u = group_sum<LPR>(u);
+      o = group_sum<LPR>(o);
+      // Next position's inputs (the last position re-reads its own: always
+      // inside the staged window) and this position's q.
+      f32x4 kn[NCH], qn[NCH];
+      float an, bn, vn;
+      fetch_kabv(min(tt + 1, tn - 1), kn, an, bn, vn);
+      const float* lp = buf + tt * POS_FLOATS;
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) qn[m] = *reinterpret_cast<const f32x4*>(lp + DK + 4 * (li + LPR * m));
+      if (tt > 0 && li == 0) out_r[static_cast<size_t>(t - 1) * out_stride] = o;
+      const float c = bt * __builtin_fmaf(-at, u, vt);
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) {
+        s[m].x = __builtin_fmaf(c, kk[m].x, at * s[m].x);
+        s[m].y = __builtin_fmaf(c, kk[m].y, at * s[m].y);
+        s[m].z = __builtin_fmaf(c, kk[m].z, at * s[m].z);
+        s[m].w = __builtin_fmaf(c, kk[m].w, at * s[m].w);
+      }
+      if (CAPTURE) {
+        float* dst = ckpt_row0 + static_cast<size_t>(t) * pos_stride;
+#pragma unroll
+        for (int m = 0; m < NCH; ++m)
+          __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(dst + 4 * (li + LPR * m)));
+      }
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) {
+        kk[m] = kn[m];
+        qp[m] = qn[m];
+      }
+      at = an;
+      bt = bn;
+      vt = vn;
+    }
+    if (tn > 0) {
+      float o = 0.0f;
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) {
+        o = __builtin_fmaf(s[m].x, qp[m].x, o);
+        o = __builtin_fmaf(s[m].y, qp[m].y, o);
+        o = __builtin_fmaf(s[m].z, qp[m].z, o);
+        o = __builtin_fmaf(s[m].w, qp[m].w, o);
+      }
+      o = group_sum<LPR>(o);
+      if (li == 0) out_r[static_cast<size_t>(t0 + tn - 1) * out_stride] = o;
+    }
   } else {
     for (int tt = 0; tt < tn; ++tt) {
       const int t = t0 + tt;
