@@ -666,6 +666,20 @@ __global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const Gdn
   f32x4 s[NCH];
 
   if constexpr (NP == 0) {
+    // One batch of argument loads before the unit loop's first test (the
+    // producer/consumer kernel below gets this from the compiler unasked);
+    // otherwise the bound, the shape and the pointers arrive one dependent
+    // round trip after another before the first staging load.
+    // (One asm statement takes every value, so that all loads are issued
+    // before the single wait.)
+    asm volatile("" : : "s"(args.q), "s"(args.k), "s"(args.v), "s"(args.a), "s"(args.b), "s"(args.state),
+                 "s"(args.ckpt), "s"(args.out), "s"(args.n_pos), "s"(args.n_kheads), "s"(args.n_vheads),
+                 "s"(args.d_v), "s"(args.group), "s"(args.req0), "s"(args.n_units), "s"(args.n_blocks),
+                 "s"(args.window), "s"(args.q_scale), "s"(args.src_ckpt), "s"(args.src_node), "s"(args.src_npos),
+                 "s"(args.geom_req));
+    if constexpr (FUSED)
+      asm volatile("" : : "s"(args.x), "s"(args.conv_w), "s"(args.conv_state), "s"(args.conv_c), "s"(args.silu),
+                   "s"(args.l2_eps));
     f32x4* const stash = reinterpret_cast<f32x4*>(lds + staging_floats(args.window, POS_FLOATS));
     // NX further waves only help stage each window (they own no rows).
     const bool owner = NX == 0 || tid < NC;   // wave-uniform
