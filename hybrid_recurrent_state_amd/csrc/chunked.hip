@@ -27,8 +27,9 @@
 //     each per wave; f32 inputs: vector FMA), and X = K S_0^T, QS = Q S_0^T
 //     for the block's rows (16x16x4 f32 MFMA, one 16-position tile per wave);
 //  3. G, g, A = strictly lower (b_t G[t][j] (K K^T)[t][j]) and P = lower
-//     (G[t][j] (Q K^T)[t][j]) by running products (no division, no
-//     logarithm: zero and tiny decays are exact);
+//     (G[t][j] (Q K^T)[t][j]) by running products, four lanes per row
+//     (16 columns each, the decays above a lane's segment from the other
+//     lanes; no division, no logarithm: zero and tiny decays are exact);
 //  4. Y = b (V - g X), then (I + A) W = Y by blocks of 16 positions: a
 //     block-row update by all threads, then forward substitution inside the
 //     16 x 16 diagonal block with one lane per state row;
@@ -386,41 +387,59 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
     }
     __syncthreads();
     // 3. Row t: A[t][j] = b_t G[t][j] (K K^T)[t][j] for j < t, P[t][j] =
-    //    G[t][j] (q_t . k_j) for j <= t, and g_t, by running products from
-    //    the diagonal down (the decays are read into registers first).
-    if (tid < kC) {
-      const int t = tid;
-      float av[kC];
+    //    G[t][j] (q_t . k_j) for j <= t, and g_t, where G[t][j] = a_{j+1}
+    //    ... a_t (1 for j >= t). Four lanes share a row, each 16 columns
+    //    [16 s, 16 s + 16): a lane multiplies the decays of its own segment
+    //    into running products from the segment's top down (no division, no
+    //    logarithm: zero and tiny decays are exact), and the product of the
+    //    decays above its segment comes from the other three lanes.
+    {
+      const int t = tid >> 2;
+      const int sg = tid & 3;
+      const int j0 = 16 * sg;
+      float av[16];   // a_{j0} .. a_{j0 + 15}
 #pragma unroll
-      for (int j = 0; j < kC; j += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(Av + j);
+      for (int j = 0; j < 16; j += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(Av + j0 + j);
         av[j] = x.x; av[j + 1] = x.y; av[j + 2] = x.z; av[j + 3] = x.w;
+      }
+      // Product of this segment's decays with index <= t (the factor that
+      // every column of the segments below needs).
+      float own = 1.0f;
+#pragma unroll
+      for (int i = 15; i >= 0; --i) own *= (j0 + i <= t) ? av[i] : 1.0f;
+      // Product of the segments above (lanes sg + 1 .. 3 of this row),
+      // highest first.
+      const int base = tid & ~3;
+      float above = 1.0f;
+#pragma unroll
+      for (int k = 3; k >= 1; --k) {
+        const float o = __shfl(own, base + k);
+        if (k > sg) above *= o;
       }
       const float bt = Bv[t];
       float* const arow = A + t * kAS;
       float* const prow = P + t * kAS;
-      // Branch-free: the running product stays 1 until j < t, and entries
-      // with j > t (unused) are scaled by 1 as well.
-      float gp = 1.0f;   // G[t][j] for the current j
       const bool last = t == n - 1;   // this row's products are the decays to the chunk end
+      float gp = above;               // G[t][j] for the current j
 #pragma unroll
-      for (int j = kC - 4; j >= 0; j -= 4) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(arow + j);
-        const f32x4 qv = *reinterpret_cast<const f32x4*>(prow + j);
+      for (int j = 12; j >= 0; j -= 4) {
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(arow + j0 + j);
+        const f32x4 qv = *reinterpret_cast<const f32x4*>(prow + j0 + j);
         f32x4 ka, qa, gc;
 #pragma unroll
         for (int u = 3; u >= 0; --u) {
-          const int jj = j + u;
-          if (jj + 1 < kC) gp *= (jj < t) ? av[jj + 1] : 1.0f;
+          const int jj = j0 + j + u;   // column
+          if (j + u < 15) gp *= (jj < t) ? av[j + u + 1] : 1.0f;
           ka[u] = bt * gp * kv[u];
           qa[u] = (p_scale * gp) * qv[u];
           gc[u] = gp;
         }
-        *reinterpret_cast<f32x4*>(arow + j) = ka;
-        *reinterpret_cast<f32x4*>(prow + j) = qa;
-        if (last) *reinterpret_cast<f32x4*>(GC + j) = gc;
+        *reinterpret_cast<f32x4*>(arow + j0 + j) = ka;
+        *reinterpret_cast<f32x4*>(prow + j0 + j) = qa;
+        if (last) *reinterpret_cast<f32x4*>(GC + j0 + j) = gc;
       }
-      Gv[t] = av[0] * gp;   // g_t = a_0 G[t][0]
+      if (sg == 0) Gv[t] = av[0] * gp;   // g_t = a_0 G[t][0]
     }
     __syncthreads();
     // 4. Y = b (V - g X) in place of X (waves 1-3) while wave 0 inverts the
