@@ -221,6 +221,41 @@ def chunked_prefill_row(reps: int = 10, T: int = 1024, R: int = 1):
                                       "speedup": res["recurrent_r16"] / res["chunked_r16"]}}
 
 
+def row_rates(step, shape, h, L: int, reps: int = 5):
+    """Achieved HBM rate of the step's other rows, each timed alone after the
+    timed regions: the L conv spans back to back (per layer), acceptance,
+    rollback of every layer, ring set + get. Event pairs around each piece,
+    median of `reps`; bytes are the algorithmic bytes of the piece."""
+    import torch
+
+    def timed(fn, per: int) -> float:
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) / per)
+        return float(np.median(out)) / 1e3
+
+    def entry(sec: float, nbytes: int, unit: str) -> dict:
+        gbs = nbytes / sec / 1e9
+        return {"unit_of_work": unit, "us": sec * 1e6, "bytes": nbytes, "achieved_gbs": gbs,
+                "frac": gbs / HBM_PEAK_GBS}
+
+    rows = {"conv1d_verify_span": entry(timed(lambda: [step.launch_conv(l, h) for l in range(L)], L),
+                                        shape.conv_bytes_per_layer, "one layer (launches back to back)")}
+    if shape.vocab:
+        rows["accept_greedy"] = entry(timed(lambda: step.launch_accept(h), 1), shape.accept_bytes, "one call")
+    rows["rollback_restore"] = entry(timed(lambda: step.launch_rollback(h), 1), shape.rollback_bytes,
+                                     "one call (every layer)")
+    if shape.ring_slots:
+        rows["ring_set_2d+ring_get_2d"] = entry(timed(lambda: step.launch_ring(h), 1), shape.ring_bytes,
+                                                "one set and one get")
+    return rows
+
+
 def store_stream_gbs(mib: int = 2048, reps: int = 10) -> float:
     """Reference ceiling: a plain device store stream (torch's fill of one
     buffer), timed with events over `reps` fills."""
@@ -347,6 +382,8 @@ def main():
         stack.append(e0.elapsed_time(e1) / L)
     stack_s = float(np.median(stack)) / 1e3
 
+    rows = row_rates(step, shape, h, L)
+
     R, T = w.n_req, w.n_pos
     value = R * T * L / (ms_per_step / 1e3)
     gdn_bytes = shape.gdn_bytes_per_layer
@@ -456,6 +493,7 @@ def main():
         "gdn_tokens_per_s_per_layer": R * T / gdn_avg_s,
         "draft_tokens_per_s_per_layer": R * (T - 1) * L / (ms_per_step / 1e3),
         "phases_ms": phases,
+        "rows": rows,
         "next_rows": next_rows,
         "cpu_baseline": cpu,
     }

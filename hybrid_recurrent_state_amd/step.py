@@ -208,6 +208,10 @@ class VerifyStep:
         else:
             _check(lib.gdn_verify_span_timed(self.gdn_p, *gdn_a, stream, events[0], events[1]), "gdn_verify_span")
 
+    def launch_conv(self, l: int, stream: int) -> None:
+        """The conv span of layer l alone."""
+        _check(lib.conv1d_verify_span(self.conv_p, *self.layer_args[l][0], stream), "conv1d_verify_span")
+
     def launch_gdn(self, l: int, stream: int) -> None:
         """The GDN span of layer l alone (its inputs as the step leaves them)."""
         _check(lib.gdn_verify_span(self.gdn_p, *self.layer_args[l][1], stream), "gdn_verify_span")
