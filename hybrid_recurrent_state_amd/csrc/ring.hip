@@ -6,10 +6,13 @@
 // stream synchronisation per token.
 //
 // MI355X design: the host splits wrapping runs into non-wrapping segments and
-// passes them (with their row prefix sums) in the kernel arguments, so one
-// launch copies every row of every run. Grid = (4 KiB column chunk, row);
-// a block finds its segment by binary search over the prefix sums (uniform,
-// scalar) and copies 16 bytes per lane.
+// passes them in the kernel arguments, so one launch copies every row of
+// every run. Grid = (4 KiB column chunk, segment, row within the segment):
+// a block reads its segment's fields at an index it knows at entry, so the
+// copy waits for one round of argument loads (a binary search over the
+// segments' row prefix sums took one dependent round per step; 16 requests
+// of 17 rows: 24 segments); blocks past their segment's length return at
+// once. 16 bytes per lane.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -36,19 +39,17 @@ struct RingArgs {
   int32_t seg_ring[kMaxSeg];
   int32_t seg_slot[kMaxSeg];
   int32_t seg_row[kMaxSeg];     // first packed row of the segment
-  int32_t seg_first[kMaxSeg + 1];  // prefix sum of segment lengths
+  int32_t seg_n[kMaxSeg];       // rows of the segment
 };
 
 __global__ __launch_bounds__(kThreads) void ring_copy_kernel(const RingArgs args) {
-  const int row = blockIdx.y;
-  int lo = 0, hi = args.n_seg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (args.seg_first[mid] <= row) lo = mid; else hi = mid - 1;
-  }
-  const int i = row - args.seg_first[lo];
-  const int64_t slot = static_cast<int64_t>(args.seg_ring[lo]) * args.n_slots + args.seg_slot[lo] + i;
-  const int64_t prow = static_cast<int64_t>(args.seg_row[lo]) + i;
+  const int sg = blockIdx.y;    // < n_seg (the grid's y extent)
+  const int i = blockIdx.z;     // row within the segment
+  args_in_registers(args.dst_ring, args.src_ring, args.dst_packed, args.src_packed, args.row_vecs, args.n_slots,
+                    args.seg_ring[sg], args.seg_slot[sg], args.seg_row[sg], args.seg_n[sg]);
+  if (i >= args.seg_n[sg]) return;
+  const int64_t slot = static_cast<int64_t>(args.seg_ring[sg]) * args.n_slots + args.seg_slot[sg] + i;
+  const int64_t prow = static_cast<int64_t>(args.seg_row[sg]) + i;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (e >= args.row_vecs) return;
   if (args.dst_ring) {
@@ -103,6 +104,14 @@ int ring_copy(const hrs_ring_desc* d, bool set, void* ring_w, const void* ring_r
   if (!ring || (!packed && d->n_packed_rows > 0)) return HRS_EINVAL;
   if (!aligned16(ring) || !aligned16(packed)) return HRS_EALIGN;
   if (segs.empty()) return HRS_OK;
+  // A segment is one grid z extent: split any longer than the z limit.
+  constexpr int32_t kMaxRows = 65535;
+  std::vector<Seg> parts;
+  parts.reserve(segs.size());
+  for (const Seg& g : segs)
+    for (int32_t o = 0; o < g.n; o += kMaxRows)
+      parts.push_back({g.ring, g.slot + o, std::min(kMaxRows, g.n - o), g.row + o});
+  segs.swap(parts);
 
   RingArgs args;
   args.dst_ring = set ? static_cast<u32x4*>(ring_w) : nullptr;
@@ -118,19 +127,18 @@ int ring_copy(const hrs_ring_desc* d, bool set, void* ring_w, const void* ring_r
   size_t i = 0;
   while (i < segs.size()) {
     int n = 0;
-    int rows = 0;
-    while (i < segs.size() && n < kMaxSeg && rows + segs[i].n <= 65535) {
+    int longest = 0;   // grid z extent: the longest segment of this launch (<= n_slots)
+    while (i < segs.size() && n < kMaxSeg) {
       args.seg_ring[n] = segs[i].ring;
       args.seg_slot[n] = segs[i].slot;
       args.seg_row[n] = segs[i].row;
-      args.seg_first[n] = rows;
-      rows += segs[i].n;
+      args.seg_n[n] = segs[i].n;
+      longest = std::max(longest, static_cast<int>(segs[i].n));
       ++n;
       ++i;
     }
-    args.seg_first[n] = rows;
     args.n_seg = n;
-    hipLaunchKernelGGL(ring_copy_kernel, dim3(gx, rows), block, 0, s, args);
+    hipLaunchKernelGGL(ring_copy_kernel, dim3(gx, n, longest), block, 0, s, args);
     if (launch_error() != hipSuccess) return HRS_EDEVICE;
   }
   return HRS_OK;

@@ -568,6 +568,28 @@ def test_ring_set_get_vs_oracle(hrs, dtype):
     assert np.array_equal(to_numpy(out), oring.ring_get(exp_ring, np.zeros_like(packed), runs))
 
 
+def test_ring_run_longer_than_one_launch_extent(hrs):
+    """A run of 68,000 rows (more than the 65,535 rows one grid dimension of a
+    launch holds) into a 70,000-slot ring, beside a wrapping run: set and get
+    against the oracle."""
+    rng = np.random.default_rng(9)
+    n_rings, S, D = 2, 70000, 8
+    ring0 = bf16_bits(rng.standard_normal((n_rings, S, D)).astype(np.float32))
+    packed = bf16_bits(rng.standard_normal((68050, D)).astype(np.float32))
+    runs = [(0, 1000, 68000, 0), (1, 69990, 50, 68000)]   # run 1 wraps
+    say("ring 2 x 70000 slots, runs of 68000 and 50 rows")
+    ring = to_torch(ring0)
+    pk = to_torch(packed)
+    _torch().cuda.synchronize()
+    hrs.ring_set_2d(ring, pk, runs)
+    out = to_torch(np.zeros_like(packed))
+    hrs.ring_get_2d(ring, out, runs)
+    _torch().cuda.synchronize()
+    exp_ring = oring.ring_set(ring0, packed, runs)
+    assert np.array_equal(to_numpy(ring), exp_ring)
+    assert np.array_equal(to_numpy(out), oring.ring_get(exp_ring, np.zeros_like(packed), runs))
+
+
 def test_gdn_persistent_multi_window_chain(hrs):
     """8 requests of the Qwen shape (one 12-wave block per CU walking 1024
     32-row units) over 40 positions (two LDS windows per unit): the producer
