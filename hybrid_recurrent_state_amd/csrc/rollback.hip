@@ -49,10 +49,15 @@ __device__ __forceinline__ void copy_chunk(const u32x4* src, u32x4* dst, int64_t
     const int64_t e = base + static_cast<int64_t>(i) * kThreads;
     if (e < n_vecs) v[i] = __builtin_nontemporal_load(src + e);
   }
+  // Stores through a buffer resource over the destination with the
+  // streaming and device-scope cache bits (nt sc1): 16 requests x 48 layers
+  // 525-531 vs 542-545 us with plain nontemporal stores (same GPU, three
+  // alternating runs).
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(dst, 0, static_cast<int>(n_vecs * 16), 0x00020000);
 #pragma unroll
   for (int i = 0; i < kVecPerThread; ++i) {
     const int64_t e = base + static_cast<int64_t>(i) * kThreads;
-    if (e < n_vecs) __builtin_nontemporal_store(v[i], dst + e);
+    if (e < n_vecs) __builtin_amdgcn_raw_buffer_store_b128(v[i], rsrc, static_cast<int>(e * 16), 0, 2 | 16);
   }
 }
 
@@ -108,6 +113,9 @@ extern "C" int rollback_restore(const hrs_rollback_desc* d, const float* ckpt, f
       conv ? static_cast<int64_t>(d->conv_width - 1) * d->conv_channels * static_cast<int64_t>(dtype_size(d->conv_dtype))
            : 0;
   if (state_bytes % 16 != 0 || conv_bytes % 16 != 0) return HRS_EINVAL;
+  // The copy addresses one state (or conv state) through a buffer resource
+  // whose size is a signed 32-bit byte count.
+  if (state_bytes > INT32_MAX || conv_bytes > INT32_MAX) return HRS_EINVAL;
 
   RollbackArgs args;
   args.ckpt = reinterpret_cast<const u32x4*>(ckpt);

@@ -440,7 +440,8 @@ typedef struct {
  *           status     one int32, device: written by the launch with the
  *                      number of requests whose accept_node is outside
  *                      [0, T); those requests are left untouched.
- * Errors: HRS_EINVAL, HRS_EALIGN, HRS_EDEVICE.
+ * Errors: HRS_EINVAL (also L * R > 65535, or one (layer, request) state or
+ * conv state of 2 GiB or more), HRS_EALIGN, HRS_EDEVICE.
  */
 int rollback_restore(const hrs_rollback_desc* desc, const float* ckpt, float* state,
                      const void* conv_ckpt, void* conv_state,

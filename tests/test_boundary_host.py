@@ -222,6 +222,9 @@ def test_rollback_rejections():
     assert rollback_call(cs=None) == E.HRS_EINVAL          # conv buffers come in pairs
     assert rollback_call(state=MIS) == E.HRS_EALIGN
     assert rollback_call(conv_channels=3, conv_dtype=hrs.HRS_BF16) == E.HRS_EINVAL  # 3 rows x 3 x 2 B not 16-B
+    # one (layer, request) state of 2 GiB or more: 64 heads x 4096 x 2048 x 4 B = 2 GiB
+    assert rollback_call(n_vheads=64, d_v=4096, d_k=2048) == E.HRS_EINVAL
+    assert rollback_call(conv_channels=(1 << 28), conv_dtype=hrs.HRS_F32) == E.HRS_EINVAL   # 3 x 2^28 x 4 B
     assert rollback_call() in (E.HRS_EDEVICE, E.HRS_OK)
     assert rollback_call(cck=None, cs=None, conv_channels=0) in (E.HRS_EDEVICE, E.HRS_OK)
 
