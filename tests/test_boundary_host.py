@@ -248,6 +248,8 @@ def test_ring_rejections():
         assert ring_call(setter, width=3) == E.HRS_EINVAL                   # row not 16-byte multiple
         assert ring_call(setter, ring=MIS) == E.HRS_EALIGN
         assert ring_call(setter, runs=()) == E.HRS_OK                       # nothing to copy
+        # a run longer than one grid dimension (split on the host before the launch)
+        assert ring_call(setter, runs=((0, 5, 70000, 0),), n_slots=80000, n_packed=70000) in (E.HRS_EDEVICE, E.HRS_OK)
     # set: two runs writing the same slots (wrap overlap) are rejected
     assert ring_call(True, runs=((0, 14, 3, 0), (0, 0, 2, 3))) == E.HRS_EINVAL
     assert ring_call(True, runs=((0, 14, 3, 0), (1, 0, 2, 3))) in (E.HRS_EDEVICE, E.HRS_OK)
