@@ -247,13 +247,18 @@ def _stream(stream) -> Optional[int]:
 
 
 def _parent_array(parent, n_req: int, n_pos: int):
-    """Host int32 [n_req * n_pos] array (a single [n_pos] row is repeated)."""
+    """Host int32 [n_req * n_pos] array (a single [n_pos] row is repeated).
+
+    The library reads exactly n_req * n_pos entries, so any other size is
+    rejected here instead of being over-read or silently truncated."""
     if parent is None:
         return None, None
-    arr = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
-    if arr.ndim == 1 and n_req > 1 and arr.size == n_pos:
+    arr = np.ascontiguousarray(np.asarray(parent, dtype=np.int32)).reshape(-1)
+    if arr.size == n_pos and n_req > 1:
         arr = np.ascontiguousarray(np.tile(arr, n_req))
-    arr = arr.reshape(-1)
+    if arr.size != n_req * n_pos:
+        raise ValueError(f"parent: {arr.size} entries, expected {n_pos} (one row for every request) "
+                         f"or {n_req * n_pos} ({n_req} requests x {n_pos} positions)")
     return arr, arr.ctypes.data_as(ctypes.POINTER(_i32))
 
 
@@ -301,8 +306,8 @@ def gdn_verify_span(q, k, v, a, b, state, ckpt, out, parent=None, q_scale: float
     chk("state", state, (R, Hv, dv, dk), _f32())
     chk("ckpt", ckpt, (R, T, Hv, dv, dk), _f32(), optional=True)
     chk("out", out, (R, T, Hv, dv), _f32())
-    chk.on_gpu()
     par, par_p = _parent_array(parent, R, T)
+    chk.on_gpu()
     d = GdnDesc(R, T, Hk, Hv, dk, dv, _dtype_code(q), float(q_scale),
                 HRS_TREE if parent is not None else HRS_CHAIN, par_p)
     args = (ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(state), _ptr(ckpt), _ptr(out),
@@ -334,8 +339,8 @@ def gdn_verify_span_from(src_ckpt, src_node, q, k, v, a, b, ckpt, out, parent=No
     chk("ckpt", ckpt, (R, T, Hv, dv, dk), _f32())
     chk("out", out, (R, T, Hv, dv), _f32())
     chk.status(status)
-    chk.on_gpu()
     par, par_p = _parent_array(parent, R, T)
+    chk.on_gpu()
     d = GdnDesc(R, T, Hk, Hv, dk, dv, _dtype_code(q), float(q_scale),
                 HRS_TREE if parent is not None else HRS_CHAIN, par_p)
     src = SpanSource(_ptr(src_ckpt), _ptr(src_node), src_ckpt.shape[1])
@@ -397,8 +402,8 @@ def gdn_layer_verify_span(x, conv_w, conv_state, a, b, ckpt, out, n_kheads: int,
         chk("src_ckpt", src_ckpt, (R, src_ckpt.shape[1], Hv, dv, d_k), _f32())
         chk("src_node", src_node, (R,), _i32t())
     chk.status(status)
-    chk.on_gpu()
     par, par_p = _parent_array(parent, R, T)
+    chk.on_gpu()
     g = GdnDesc(R, T, n_kheads, Hv, d_k, dv, _dtype_code(x), float(q_scale),
                 HRS_TREE if parent is not None else HRS_CHAIN, par_p)
     d = GdnLayerDesc(g, conv_w.shape[1], int(bool(silu)), float(l2_eps))
@@ -421,8 +426,8 @@ def conv1d_verify_span_nocapture(x, w, conv_state, y, parent=None, silu: bool = 
     chk("w", w, (C, W), dt)
     chk("conv_state", conv_state, (R, W - 1, C), dt)
     chk("y", y, (R, T, C), _f32())
-    chk.on_gpu()
     par, par_p = _parent_array(parent, R, T)
+    chk.on_gpu()
     d = ConvDesc(R, T, C, W, _dtype_code(x), int(bool(silu)), HRS_TREE if parent is not None else HRS_CHAIN, par_p)
     st = lib.conv1d_verify_span_nocapture(ctypes.byref(d), _ptr(x), _ptr(w), _ptr(conv_state), _ptr(y),
                                           _stream(stream))
@@ -460,8 +465,8 @@ def conv1d_verify_span(x, w, conv_state, conv_ckpt, y, parent=None, silu: bool =
     chk("conv_state", conv_state, (R, W - 1, C), dt)
     chk("conv_ckpt", conv_ckpt, (R, T, W - 1, C), dt, optional=True)
     chk("y", y, (R, T, C), _f32())
-    chk.on_gpu()
     par, par_p = _parent_array(parent, R, T)
+    chk.on_gpu()
     d = ConvDesc(R, T, C, W, _dtype_code(x), int(bool(silu)),
                  HRS_TREE if parent is not None else HRS_CHAIN, par_p)
     st = lib.conv1d_verify_span(ctypes.byref(d), _ptr(x), _ptr(w), _ptr(conv_state), _ptr(conv_ckpt),
@@ -493,8 +498,8 @@ def accept_greedy(logits, tokens, argmax, accept_node, accept_len, path, bonus, 
                            ("accept_len", accept_len, (R,)), ("path", path, (R, T)), ("bonus", bonus, (R,))):
         chk(name, t, shape, _i32t())
     chk("workspace", workspace)
-    chk.on_gpu()
     d, _keep = accept_desc(R, T, V, _dtype_code(logits), parent)
+    chk.on_gpu()
     nbytes = workspace.numel() * workspace.element_size()
     st = lib.accept_greedy(ctypes.byref(d), _ptr(logits), _ptr(tokens), _ptr(argmax), _ptr(accept_node),
                            _ptr(accept_len), _ptr(path), _ptr(bonus), _ptr(workspace), nbytes,

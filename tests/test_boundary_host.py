@@ -3,8 +3,14 @@ include/hrs.h declares, and rejects malformed calls before any launch.
 
 No compute runs here. Device pointers are fake aligned addresses that the
 host code never dereferences; a call that got past its checks would try to
-launch and return HRS_EDEVICE (no GPU in this environment), so seeing the
-specific rejection code proves the check ran first.
+launch and return HRS_EDEVICE (no GPU is visible), so seeing the specific
+rejection code proves the check ran first, and a well-formed call must end
+in HRS_EDEVICE: a launch can never count as a pass.
+
+The module runs only where no GPU is visible. On a machine with a GPU those
+well-formed calls would launch kernels on the fake addresses, so the whole
+module is skipped there (the GPU tests cover the same entry points with real
+buffers).
 """
 import ctypes
 import os
@@ -14,6 +20,24 @@ import numpy as np
 import pytest
 
 from tests.conftest import ROOT
+
+
+def _gpu_visible() -> bool:
+    """True when a GPU could be reached. Checks the kernel driver's device
+    node first and then torch's device count, neither of which initialises
+    the HIP runtime."""
+    if os.path.exists("/dev/kfd"):
+        return True
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:  # noqa: BLE001 - no torch: no device through it either
+        return False
+
+
+if _gpu_visible():
+    pytest.skip("host-only boundary checks: a GPU is visible, and a call that passes its checks "
+                "would launch on fake device addresses", allow_module_level=True)
 
 
 def _ensure_built():
@@ -125,8 +149,8 @@ def test_gdn_rejections():
     assert gdn_call(ckpt=MIS) == E.HRS_EALIGN
     assert gdn_call(d_k=96) == E.HRS_EUNSUPPORTED
     assert gdn_call(d_v=24) == E.HRS_EUNSUPPORTED
-    # a well-formed call gets past every check; without a GPU the launch fails
-    assert gdn_call() in (E.HRS_EDEVICE, E.HRS_OK)
+    # a well-formed call gets past every check; with no GPU visible the launch fails
+    assert gdn_call() == E.HRS_EDEVICE
 
 
 def conv_call(**kw):
@@ -156,7 +180,7 @@ def test_conv_rejections():
     assert conv_call(n_pos=70) == E.HRS_EGEOMETRY
     assert conv_call(y=MIS) == E.HRS_EALIGN
     assert conv_call(width=3) == E.HRS_EUNSUPPORTED
-    assert conv_call() in (E.HRS_EDEVICE, E.HRS_OK)
+    assert conv_call() == E.HRS_EDEVICE
 
 
 def accept_call(ws_bytes=None, **kw):
@@ -182,14 +206,14 @@ def test_accept_rejections_and_workspace_size():
     E = hrs
     st, need = accept_call()
     assert need == 2 * 5 * 1 * 8          # one 8192-entry chunk per row, 8-byte keys
-    assert st in (E.HRS_EDEVICE, E.HRS_OK)
+    assert st == E.HRS_EDEVICE
     assert accept_call(vocab=151936)[1] == 2 * 5 * 19 * 8
     assert accept_call(vocab=1001)[0] == E.HRS_EINVAL
     assert accept_call(ws_bytes=need - 1)[0] == E.HRS_EINVAL
     assert accept_call(tokens=None)[0] == E.HRS_EINVAL
     assert accept_call(n_pos=0)[0] == E.HRS_EGEOMETRY
     assert accept_call(topo=E.HRS_TREE, parent=[-1, 0, 0, 1, 1, -1, 0, 1, 1, 5])[0] == E.HRS_EGEOMETRY
-    assert accept_call(topo=E.HRS_TREE, parent=[-1, 0, 0, 1, 1, -1, 0, 1, 1, 2])[0] in (E.HRS_EDEVICE, E.HRS_OK)
+    assert accept_call(topo=E.HRS_TREE, parent=[-1, 0, 0, 1, 1, -1, 0, 1, 1, 2])[0] == E.HRS_EDEVICE
     assert accept_call(path=MIS)[0] == E.HRS_EALIGN
     assert accept_call(vocab=0)[1] == 0
     # pass-1 blocks (rows x 8192-logit chunks) are bounded by 2^24: the largest
@@ -225,8 +249,8 @@ def test_rollback_rejections():
     # one (layer, request) state of 2 GiB or more: 64 heads x 4096 x 2048 x 4 B = 2 GiB
     assert rollback_call(n_vheads=64, d_v=4096, d_k=2048) == E.HRS_EINVAL
     assert rollback_call(conv_channels=(1 << 28), conv_dtype=hrs.HRS_F32) == E.HRS_EINVAL   # 3 x 2^28 x 4 B
-    assert rollback_call() in (E.HRS_EDEVICE, E.HRS_OK)
-    assert rollback_call(cck=None, cs=None, conv_channels=0) in (E.HRS_EDEVICE, E.HRS_OK)
+    assert rollback_call() == E.HRS_EDEVICE
+    assert rollback_call(cck=None, cs=None, conv_channels=0) == E.HRS_EDEVICE
 
 
 def ring_call(setter=True, runs=((0, 14, 5, 0),), n_rings=2, n_slots=16, width=64, dtype=None, n_packed=8,
@@ -240,7 +264,7 @@ def ring_call(setter=True, runs=((0, 14, 5, 0),), n_rings=2, n_slots=16, width=6
 def test_ring_rejections():
     E = hrs
     for setter in (True, False):
-        assert ring_call(setter) in (E.HRS_EDEVICE, E.HRS_OK)
+        assert ring_call(setter) == E.HRS_EDEVICE
         assert ring_call(setter, runs=((2, 0, 1, 0),)) == E.HRS_EINVAL      # ring id
         assert ring_call(setter, runs=((0, 16, 1, 0),)) == E.HRS_EINVAL     # start
         assert ring_call(setter, runs=((0, 0, 17, 0),)) == E.HRS_EINVAL     # longer than the ring
@@ -249,13 +273,13 @@ def test_ring_rejections():
         assert ring_call(setter, ring=MIS) == E.HRS_EALIGN
         assert ring_call(setter, runs=()) == E.HRS_OK                       # nothing to copy
         # a run longer than one grid dimension (split on the host before the launch)
-        assert ring_call(setter, runs=((0, 5, 70000, 0),), n_slots=80000, n_packed=70000) in (E.HRS_EDEVICE, E.HRS_OK)
+        assert ring_call(setter, runs=((0, 5, 70000, 0),), n_slots=80000, n_packed=70000) == E.HRS_EDEVICE
     # set: two runs writing the same slots (wrap overlap) are rejected
     assert ring_call(True, runs=((0, 14, 3, 0), (0, 0, 2, 3))) == E.HRS_EINVAL
-    assert ring_call(True, runs=((0, 14, 3, 0), (1, 0, 2, 3))) in (E.HRS_EDEVICE, E.HRS_OK)
+    assert ring_call(True, runs=((0, 14, 3, 0), (1, 0, 2, 3))) == E.HRS_EDEVICE
     # get: two runs writing the same packed rows are rejected, same slots are fine
     assert ring_call(False, runs=((0, 14, 3, 0), (1, 0, 2, 2))) == E.HRS_EINVAL
-    assert ring_call(False, runs=((0, 14, 3, 0), (0, 14, 3, 3))) in (E.HRS_EDEVICE, E.HRS_OK)
+    assert ring_call(False, runs=((0, 14, 3, 0), (0, 14, 3, 3))) == E.HRS_EDEVICE
 
 
 def test_zero_copy_entry_rejections():
@@ -274,10 +298,10 @@ def test_zero_copy_entry_rejections():
     assert call(n_pos=0) == E.HRS_EINVAL
     assert call(n_pos=65) == E.HRS_EINVAL
     assert call(src_ckpt=FAKE + ck_bytes // 2) == E.HRS_EINVAL   # new checkpoints overlap the source
-    assert call(src_ckpt=FAKE + ck_bytes) in (E.HRS_EDEVICE, E.HRS_OK)   # adjacent, no overlap
+    assert call(src_ckpt=FAKE + ck_bytes) == E.HRS_EDEVICE   # adjacent, no overlap
     assert call(node=MIS) == E.HRS_EALIGN
     assert call(status=MIS) == E.HRS_EALIGN
-    assert call() in (E.HRS_EDEVICE, E.HRS_OK)
+    assert call() == E.HRS_EDEVICE
 
 
 def test_conv_nocapture_and_advance_rejections():
@@ -286,7 +310,7 @@ def test_conv_nocapture_and_advance_rejections():
     assert hrs.lib.conv1d_verify_span_nocapture(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) == E.HRS_EGEOMETRY
     par = np.array([-1, 0, 0, 1], dtype=np.int32)
     d = hrs.ConvDesc(1, 4, 64, 4, hrs.HRS_BF16, 0, hrs.HRS_TREE, par.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
-    assert hrs.lib.conv1d_verify_span_nocapture(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) in (E.HRS_EDEVICE, E.HRS_OK)
+    assert hrs.lib.conv1d_verify_span_nocapture(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) == E.HRS_EDEVICE
     assert hrs.lib.conv1d_verify_span_nocapture(ctypes.byref(d), FAKE, FAKE, None, FAKE, None) == E.HRS_EINVAL
 
     def adv(L=2, R=3, T=5, C=64, W=4, dt=hrs.HRS_BF16, x=FAKE, cs=FAKE, path=FAKE, ln=FAKE, st=None):
@@ -298,7 +322,7 @@ def test_conv_nocapture_and_advance_rejections():
     assert adv(path=None) == E.HRS_EINVAL
     assert adv(cs=MIS) == E.HRS_EALIGN
     assert adv(W=3) == E.HRS_EUNSUPPORTED
-    assert adv() in (E.HRS_EDEVICE, E.HRS_OK)
+    assert adv() == E.HRS_EDEVICE
 
 
 def test_layer_entry_rejections():
@@ -321,7 +345,7 @@ def test_layer_entry_rejections():
     assert call(state=None) == E.HRS_EINVAL                 # no initial state
     both = hrs.SpanSource(FAKE + (1 << 32), FAKE, 4)
     assert call(src=both) == E.HRS_EINVAL                    # two initial states
-    assert call(state=None, src=both) in (E.HRS_EDEVICE, E.HRS_OK)
+    assert call(state=None, src=both) == E.HRS_EDEVICE
     assert call(ckpt=None) == E.HRS_EINVAL                   # capture required
     assert call(x=None) == E.HRS_EINVAL
     assert call(w=None) == E.HRS_EINVAL
@@ -334,8 +358,8 @@ def test_layer_entry_rejections():
     assert call(a=MIS) == E.HRS_EALIGN
     assert call(d_k=96) == E.HRS_EUNSUPPORTED
     assert call(topo=hrs.HRS_TREE, parent=[-1, 0, 0, 5, -1, 0, 1, 1]) == E.HRS_EGEOMETRY
-    assert call(topo=hrs.HRS_TREE, parent=[-1, 0, 0, 1, -1, 0, 1, 1]) in (E.HRS_EDEVICE, E.HRS_OK)
-    assert call() in (E.HRS_EDEVICE, E.HRS_OK)
+    assert call(topo=hrs.HRS_TREE, parent=[-1, 0, 0, 1, -1, 0, 1, 1]) == E.HRS_EDEVICE
+    assert call() == E.HRS_EDEVICE
 
 
 def test_chunked_entry_rejections():
@@ -363,9 +387,9 @@ def test_chunked_entry_rejections():
     assert call(ckpt=MIS) == E.HRS_EALIGN
     assert call(out=MIS) == E.HRS_EALIGN
     assert call(dk=64, dv=64) == E.HRS_EUNSUPPORTED
-    assert call(n_pos=(1 << 20)) in (E.HRS_EDEVICE, E.HRS_OK)
-    assert call(ckpt=FAKE, out_dt=hrs.HRS_BF16, log_gates=1) in (E.HRS_EDEVICE, E.HRS_OK)
-    assert call() in (E.HRS_EDEVICE, E.HRS_OK)
+    assert call(n_pos=(1 << 20)) == E.HRS_EDEVICE
+    assert call(ckpt=FAKE, out_dt=hrs.HRS_BF16, log_gates=1) == E.HRS_EDEVICE
+    assert call() == E.HRS_EDEVICE
 
 
 def test_binding_rejects_mismatched_tensors_before_launch():
@@ -411,3 +435,28 @@ def test_binding_rejects_mismatched_tensors_before_launch():
                              torch.zeros(4, dtype=torch.int32))
     with pytest.raises(ValueError, match="packed: shape"):
         hrs.ring_set_2d(torch.zeros(2, 8, 16, dtype=h), torch.zeros(3, 8, dtype=h), [(0, 0, 3, 0)])
+
+
+def test_binding_rejects_parent_arrays_of_the_wrong_size():
+    """The library reads n_req * n_pos parent entries: the binding accepts one
+    row per request or one row repeated for all, and rejects every other size
+    (a short list would be over-read on the host, a long one truncated)."""
+    import torch
+    R, T, Hk, Hv, d = 2, 4, 1, 2, 64
+    f, h = torch.float32, torch.bfloat16
+    z = lambda *s, dt=h: torch.zeros(*s, dtype=dt)
+    span_in = (z(R, T, Hk, d), z(R, T, Hk, d), z(R, T, Hv, d), z(R, T, Hv), z(R, T, Hv), z(R, Hv, d, d, dt=f),
+               z(R, T, Hv, d, d, dt=f), z(R, T, Hv, d, dt=f))
+    good_row = [-1, 0, 0, 1]
+    for bad in (good_row[:3], good_row + [2], good_row * R + [0], (good_row * R)[:-1]):
+        with pytest.raises(ValueError, match="parent: "):
+            hrs.gdn_verify_span(*span_in, parent=bad)
+        with pytest.raises(ValueError, match="parent: "):
+            hrs.accept_greedy_workspace_bytes(R, T, 1024, parent=bad)
+        with pytest.raises(ValueError, match="parent: "):
+            hrs.conv1d_verify_span(z(R, T, 64), z(64, 4), z(R, 3, 64), None, z(R, T, 64, dt=f), parent=bad)
+    # the right sizes get past the parent check (and stop at the host tensors)
+    for ok in (good_row, good_row * R, np.array([good_row] * R)):
+        with pytest.raises(ValueError, match="must be a GPU tensor"):
+            hrs.gdn_verify_span(*span_in, parent=ok)
+        assert hrs.accept_greedy_workspace_bytes(R, T, 1024, parent=ok) == R * T * 8
