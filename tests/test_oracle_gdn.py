@@ -147,6 +147,20 @@ def _f32_frac(x):
     return Fraction(float(np.float32(x)))
 
 
+def _round_f32_exact(x: Fraction) -> np.float32:
+    """Round an exact rational to the nearest float32, ties to the even
+    significand, deciding between the two neighbours with exact arithmetic
+    (no intermediate float64 rounding)."""
+    f = np.float32(float(x))
+    best = None
+    for c in (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))):
+        d = abs(Fraction(float(c)) - x)
+        key = (d, int(np.asarray(c).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return np.float32(best[1])
+
+
 @pytest.mark.parametrize("d,T", [(2, 1), (2, 3), (3, 2), (3, 3)])
 def test_exact_rational_brute_force(d, T):
     """Exact rationals with the literal product formula S (I - b k k^T) on
@@ -273,3 +287,40 @@ def test_nonexpansive_with_unit_keys():
         cur = np.linalg.norm(ck2[t].astype(np.float64) - ck1[t])
         assert cur <= prev * (1 + 1e-5)
         prev = cur
+
+
+@pytest.mark.parametrize("d,T,seed", [(2, 3, 0), (3, 3, 1), (3, 2, 2)])
+def test_exact_rational_full_mantissa(d, T, seed):
+    """Exact rationals on random float32 inputs with full 24-bit significands,
+    so that the new state is almost never a float32 value: the checkpoint must
+    be the exact state rounded to float32 (nearest, ties to even), the output
+    must be computed from that rounded checkpoint, and the next position must
+    start from it. The inputs are checked to be ones where taking the output
+    from the unrounded state would change some output bits, so a slip there
+    cannot pass."""
+    rng = np.random.default_rng(100 + seed)
+    f32 = lambda *shape: rng.uniform(-1.0, 1.0, shape).astype(np.float32)
+    q, k, v, s = f32(T, 1, d), f32(T, 1, d), f32(T, 1, d), f32(1, d, d)
+    a = rng.uniform(0.1, 0.99, (T, 1)).astype(np.float32)
+    b = rng.uniform(0.1, 0.99, (T, 1)).astype(np.float32)
+    ckpt, out = og.gdn_span(s, q, k, v, a, b)
+    S = [[_f32_frac(s[0, i, j]) for j in range(d)] for i in range(d)]
+    differs = 0
+    for t in range(T):
+        kk = [_f32_frac(k[t, 0, j]) for j in range(d)]
+        vv = [_f32_frac(v[t, 0, j]) for j in range(d)]
+        qq = [_f32_frac(q[t, 0, j]) for j in range(d)]
+        at, bt = _f32_frac(a[t, 0]), _f32_frac(b[t, 0])
+        M = [[(1 if i == j else 0) - bt * kk[i] * kk[j] for j in range(d)] for i in range(d)]
+        exact = [[at * sum(S[i][m] * M[m][j] for m in range(d)) + bt * vv[i] * kk[j] for j in range(d)]
+                 for i in range(d)]
+        rounded = [[_round_f32_exact(exact[i][j]) for j in range(d)] for i in range(d)]
+        S = [[Fraction(float(rounded[i][j])) for j in range(d)] for i in range(d)]
+        for i in range(d):
+            o_exact = _round_f32_exact(sum(S[i][j] * qq[j] for j in range(d)))
+            o_unrounded = _round_f32_exact(sum(exact[i][j] * qq[j] for j in range(d)))
+            differs += int(o_exact != o_unrounded)
+            assert out[t, 0, i] == o_exact, (t, i)
+            for j in range(d):
+                assert ckpt[t, 0, i, j] == rounded[i][j], (t, i, j)
+    assert differs > 0, "inputs must make the output depend on the checkpoint rounding"
