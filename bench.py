@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true", help="skip the measured NEXT-row variants")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other configured workloads (measured after the headline)")
+    ap.add_argument("--workload-cpu-seconds", type=float, default=4.0,
+                    help="budget of the oracle CPU baseline of each other workload")
     ap.add_argument("--graph", action="store_true",
                     help="launch each step as one captured HIP graph (the same kernels)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -63,19 +67,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per gdn_verify_span launch from the committed counter passes
-    (profiles/hbm_traffic.json), or None when they were taken on another
-    workload or on different kernel sources."""
+def measured_traffic(workload: str, kernel: str = "gdn_verify_span"):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter passes (profiles/hbm_traffic.json), or None when none were taken
+    there or the kernel sources have changed since."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f)
+            data = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != kernel_source_hash():
-        return None
-    return rec.get("traffic_bytes_per_launch")
+    for rec in data.get("records", []):
+        if (rec.get("workload") == workload and rec.get("entry_point") == kernel
+                and rec.get("kernel_source_sha256") == kernel_source_hash()):
+            return rec.get("traffic_bytes_per_launch")
+    return None
 
 
 def _oracle_units(w, units, seconds: float):
@@ -124,19 +130,22 @@ def cpu_baseline(w, seconds: float):
     core (at most 16), each for about seconds / workers."""
     units = [(l, r) for r in range(w.n_req) for l in range(w.n_layers)]
     done, tokens, t_work = _oracle_units(w, units, seconds)
+    avail = len(os.sched_getaffinity(0))
     out = {"value": tokens / t_work, "unit": "verify tokens/s per layer", "cores": 1, "kind": "oracle",
+           "available_cores": avail, "os_cpu_count": os.cpu_count(),
            "sample": f"{done} (layer, request) units of {w.name}: conv span, GDN span, acceptance "
                      f"(argmax once per request), replay rollback; {t_work:.1f} s of CPU work, 1 thread"}
     try:
         import multiprocessing as mp
-        n = max(1, min(16, len(os.sched_getaffinity(0))))
+        n = max(1, min(16, avail, len(units)))
         per = max(1.0, seconds / n)
         chunks = [(w.name, units[i::n], per) for i in range(n)]
         with mp.get_context("spawn").Pool(n) as pool:
             res = pool.map(_pool_worker, chunks)
         rate = sum(tok / t for (_, tok, t) in res if t > 0)
-        out["pool"] = {"value": rate, "cores": n,
-                       "sample": f"{sum(d for d, _, _ in res)} units over {n} worker processes, "
+        out["pool"] = {"value": rate, "cores": n, "available_cores": avail,
+                       "sample": f"{sum(d for d, _, _ in res)} units over {n} worker processes "
+                                 f"({avail} cores available to this process, at most 16 workers), "
                                  f"~{per:.1f} s of work each; rate = sum of per-worker rates"}
     except Exception as e:  # noqa: BLE001 - the pooled figure is optional context
         out["pool"] = {"error": str(e)}
@@ -275,6 +284,129 @@ def store_stream_gbs(mib: int = 2048, reps: int = 10) -> float:
     return gbs
 
 
+def time_steps(step, stream, K: int, warmup: int, graph: bool = False) -> float:
+    """ms per step of K consecutive steps (launch + the single host sync),
+    after `warmup` untimed ones; graph=True replays captured graphs (the
+    step's capture_graph is called first)."""
+    import torch
+    if graph:
+        step.capture_graph()
+    for _ in range(warmup):
+        step.replay() if graph else step.run(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        if graph:
+            step.replay()
+        else:
+            step.launch(stream)
+            step.finish()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / K
+
+
+
+def gdn_launch_stats(step, stream, L: int, K: int) -> dict:
+    """Timed region 2 and the untimed splits of one workload's step.
+
+    * K more steps in which every gdn_verify_span dispatch records a
+      start/stop event pair itself (gdn_verify_span_timed): the events bracket
+      exactly the kernel, but they open short gaps between kernels, so this
+      region is not used for the step time. Average and median per launch.
+    * Phase split: one step with events between its phases.
+    * Per stack: the step's L GDN spans back to back with no other kernel
+      between them (launch gaps included), event-timed, median of 3."""
+    import torch
+    import hybrid_recurrent_state_amd as hrs
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+          for _ in range(K)]
+    ev_h = [[(hrs.event_handle(s), hrs.event_handle(e)) for (s, e) in row] for row in ev]
+    torch.cuda.synchronize()
+    log(f"timing {K} steps with per-launch GDN events")
+    t2 = time.perf_counter()
+    for i in range(K):
+        step.launch(stream, gdn_events=ev_h[i])
+        step.finish()
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    gdn_ms = np.array([[s.elapsed_time(e) for (s, e) in row] for row in ev])
+
+    ph = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    h = stream.cuda_stream
+    ph[0].record()
+    for l in range(L):
+        step.launch_layer(l, h)
+    ph[1].record()
+    step.launch_accept(h)
+    ph[2].record()
+    step.launch_rollback(h)
+    ph[3].record()
+    step.launch_ring(h)
+    ph[4].record()
+    torch.cuda.synchronize()
+    phases = {"conv+gdn": ph[0].elapsed_time(ph[1]), "accept": ph[1].elapsed_time(ph[2]),
+              "rollback": ph[2].elapsed_time(ph[3]), "ring": ph[3].elapsed_time(ph[4])}
+
+    stack = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for l in range(L):
+            step.launch_gdn(l, h)
+        e1.record()
+        torch.cuda.synchronize()
+        stack.append(e0.elapsed_time(e1) / L)
+    return {"avg_s": float(gdn_ms.mean()) / 1e3, "median_s": float(np.median(gdn_ms)) / 1e3,
+            "min_s": float(gdn_ms.min()) / 1e3, "stack_s": float(np.median(stack)) / 1e3, "phases": phases,
+            "t_events": (t2, t3)}
+
+
+def measure_workload(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
+    """One configured workload beside the headline: its own buffers, W warmup
+    steps, K timed steps (event-free), then gdn_launch_stats, then the oracle
+    on a bounded sample of the same workload (unless cpu_seconds is 0).
+    Frees its buffers before returning."""
+    import torch
+    from synth import WORKLOADS
+    from synth.device import fill_step, step_shape
+    from hybrid_recurrent_state_amd.step import StepBuffers, VerifyStep
+    w = WORKLOADS[name]
+    shape = step_shape(w)
+    log(f"workload {name}: R={w.n_req} L={w.n_layers} T={w.n_pos}")
+    bufs = StepBuffers(shape)
+    loaded = fill_step(bufs, w)
+    step = VerifyStep(bufs, parent=loaded.parent, runs=loaded.runs)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        step.run(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step.launch(stream)
+        step.finish()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    L, R, T = w.n_layers, w.n_req, w.n_pos
+    gs = gdn_launch_stats(step, stream, L, steps)
+    nbytes = shape.gdn_bytes_per_layer
+    rec = {"workload": name, "n_req": R, "n_layers": L, "n_pos": T, "topology": "tree" if w.tree else "chain",
+           "ms_per_step": ms, "value": R * T * L / (ms / 1e3), "unit": "verify tokens/s per layer",
+           "gdn_tokens_per_s_per_layer": R * T / gs["avg_s"],
+           "gdn_bytes_per_launch": nbytes, "avg_launch_us": gs["avg_s"] * 1e6,
+           "median_launch_us": gs["median_s"] * 1e6, "min_launch_us": gs["min_s"] * 1e6,
+           "frac": nbytes / gs["avg_s"] / 1e9 / HBM_PEAK_GBS,
+           "stack_us_per_layer": gs["stack_s"] * 1e6, "stack_frac": nbytes / gs["stack_s"] / 1e9 / HBM_PEAK_GBS,
+           "traffic": measured_traffic(name), "phases_ms": gs["phases"]}
+    log(f"  step {ms:.3f} ms, gdn launch avg {rec['avg_launch_us']:.2f} us (frac {rec['frac']:.3f}), "
+        f"stack {rec['stack_us_per_layer']:.2f} us (frac {rec['stack_frac']:.3f})")
+    del step, bufs
+    torch.cuda.empty_cache()
+    if cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(w, cpu_seconds)
+    return rec
+
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -332,55 +464,12 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
 
-    # Timed region 2 (roofline of the dominant kernel): K more steps in which
-    # every gdn_verify_span dispatch records a start/stop event pair itself
-    # (gdn_verify_span_timed). The events bracket exactly the kernel, but they
-    # open short gaps between kernels, so this region is not used for the
-    # step time.
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
-          for _ in range(K)]
-    ev_h = [[(hrs.event_handle(s), hrs.event_handle(e)) for (s, e) in row] for row in ev]
-    torch.cuda.synchronize()
-    log(f"timing {K} steps with per-launch GDN events")
-    t2 = time.perf_counter()
-    for i in range(K):
-        step.launch(stream, gdn_events=ev_h[i])
-        step.finish()
-    torch.cuda.synchronize()
-    t3 = time.perf_counter()
-    gdn_ms = np.array([[s.elapsed_time(e) for (s, e) in row] for row in ev])
-    gdn_avg_s = float(gdn_ms.mean()) / 1e3
-    gdn_med_s = float(np.median(gdn_ms)) / 1e3
-
-    # Phase split (separate, untimed pass with events between phases).
-    ph = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    # Timed region 2 (roofline of the dominant kernel), phase split and
+    # per-stack timing: see gdn_launch_stats.
+    gs = gdn_launch_stats(step, stream, L, K)
+    gdn_avg_s, gdn_med_s, stack_s, phases = gs["avg_s"], gs["median_s"], gs["stack_s"], gs["phases"]
+    t2, t3 = gs["t_events"]
     h = stream.cuda_stream
-    ph[0].record()
-    for l in range(L):
-        step.launch_layer(l, h)
-    ph[1].record()
-    step.launch_accept(h)
-    ph[2].record()
-    step.launch_rollback(h)
-    ph[3].record()
-    step.launch_ring(h)
-    ph[4].record()
-    torch.cuda.synchronize()
-    phases = {"conv+gdn": ph[0].elapsed_time(ph[1]), "accept": ph[1].elapsed_time(ph[2]),
-              "rollback": ph[2].elapsed_time(ph[3]), "ring": ph[3].elapsed_time(ph[4])}
-
-    # Per-stack timing: the L GDN spans of a step back to back with no other
-    # kernel between them (launch gaps included), event-timed, median of 3.
-    stack = []
-    for _ in range(3):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for l in range(L):
-            step.launch_gdn(l, h)
-        e1.record()
-        torch.cuda.synchronize()
-        stack.append(e0.elapsed_time(e1) / L)
-    stack_s = float(np.median(stack)) / 1e3
 
     rows = row_rates(step, shape, h, L)
 
@@ -399,54 +488,45 @@ def main():
         next_rows = {}
         # f3: the same step captured once and launched as one HIP graph.
         if not args.graph:
-            step.capture_graph()
-            for _ in range(args.warmup):
-                step.replay()
-            torch.cuda.synchronize()
-            g0 = time.perf_counter()
-            for _ in range(K):
-                step.replay()
-            torch.cuda.synchronize()
-            ms_g = (time.perf_counter() - g0) * 1e3 / K
+            ms_g = time_steps(step, stream, K, args.warmup, graph=True)
             next_rows["f3_hip_graph_step"] = {"ms_per_step": ms_g, "value": R * T * L / (ms_g / 1e3),
                                               "vs_stream_launch": ms_per_step / ms_g}
             log(f"f3 graph step {ms_g:.3f} ms")
         # f2: zero-copy rollback + compact conv state (same kernels for the spans,
         # nothing copied to roll back; a second checkpoint buffer alternates).
         if w.vocab:
-            from hybrid_recurrent_state_amd.step import ZeroCopyVerifyStep
+            from hybrid_recurrent_state_amd.step import FusedVerifyStep, ZeroCopyVerifyStep
             zc = ZeroCopyVerifyStep(bufs, parent=loaded.parent, runs=loaded.runs)
-            for _ in range(args.warmup):
-                zc.run(stream)
-            torch.cuda.synchronize()
-            z0 = time.perf_counter()
-            for _ in range(K):
-                zc.launch(stream)
-                zc.finish()
-            torch.cuda.synchronize()
-            ms_z = (time.perf_counter() - z0) * 1e3 / K
+            ms_z = time_steps(zc, stream, K, args.warmup)
             next_rows["f2_zero_copy_rollback_step"] = {"ms_per_step": ms_z, "value": R * T * L / (ms_z / 1e3),
                                                        "vs_copy_rollback": ms_per_step / ms_z}
             log(f"f2 zero-copy step {ms_z:.3f} ms")
             del zc
+            # f3 on the zero-copy step: two graphs, one per checkpoint-buffer parity.
+            zc = ZeroCopyVerifyStep(bufs, parent=loaded.parent, runs=loaded.runs)
+            zc.run(stream)
+            ms_zg = time_steps(zc, stream, K, args.warmup, graph=True)
+            next_rows["f3_hip_graph_zero_copy_step"] = {"ms_per_step": ms_zg, "value": R * T * L / (ms_zg / 1e3),
+                                                        "vs_stream_launch": ms_z / ms_zg}
+            log(f"f3 graph zero-copy step {ms_zg:.3f} ms")
+            del zc
             # f1: the same zero-copy step with every layer fused into one
             # kernel (conv, SiLU, split, q/k L2 norm, gated delta rule).
             if shape.conv_channels == 2 * w.n_kheads * w.d_k + w.n_vheads * w.d_v:
-                from hybrid_recurrent_state_amd.step import FusedVerifyStep
                 fs = FusedVerifyStep(bufs, parent=loaded.parent, runs=loaded.runs)
-                for _ in range(args.warmup):
-                    fs.run(stream)
-                torch.cuda.synchronize()
-                f0 = time.perf_counter()
-                for _ in range(K):
-                    fs.launch(stream)
-                    fs.finish()
-                torch.cuda.synchronize()
-                ms_f = (time.perf_counter() - f0) * 1e3 / K
+                ms_f = time_steps(fs, stream, K, args.warmup)
                 next_rows["f1_fused_layer_step"] = {
                     "ms_per_step": ms_f, "value": R * T * L / (ms_f / 1e3), "vs_zero_copy_step": ms_z / ms_f,
-                    "layer_bytes_per_launch": shape.layer_bytes_per_layer}
+                    "layer_bytes_per_launch": shape.layer_bytes_per_layer,
+                    "traffic": measured_traffic(name, "gdn_layer_verify_span")}
                 log(f"f1 fused-layer step {ms_f:.3f} ms")
+                del fs
+                fs = FusedVerifyStep(bufs, parent=loaded.parent, runs=loaded.runs)
+                fs.run(stream)
+                ms_fg = time_steps(fs, stream, K, args.warmup, graph=True)
+                next_rows["f3_hip_graph_fused_step"] = {"ms_per_step": ms_fg, "value": R * T * L / (ms_fg / 1e3),
+                                                        "vs_stream_launch": ms_f / ms_fg}
+                log(f"f3 graph fused step {ms_fg:.3f} ms")
                 del fs
             bufs.ckpt2 = None
             torch.cuda.empty_cache()
@@ -460,10 +540,34 @@ def main():
             next_rows["f4_chunked_prefill_span"] = {"error": str(e)}
         torch.cuda.empty_cache()
 
+    headline = {"workload": name, "n_req": R, "n_layers": L, "n_pos": T, "topology": "tree" if w.tree else "chain",
+                "ms_per_step": ms_per_step, "value": value, "unit": "verify tokens/s per layer",
+                "gdn_tokens_per_s_per_layer": R * T / gdn_avg_s, "gdn_bytes_per_launch": gdn_bytes,
+                "avg_launch_us": gdn_avg_s * 1e6, "median_launch_us": gdn_med_s * 1e6,
+                "min_launch_us": gs["min_s"] * 1e6, "frac": achieved / HBM_PEAK_GBS,
+                "stack_us_per_layer": stack_s * 1e6, "stack_frac": gdn_bytes / stack_s / 1e9 / HBM_PEAK_GBS,
+                "traffic": traffic, "phases_ms": phases}
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
         cpu = cpu_baseline(w, args.cpu_seconds)
+        headline["cpu_baseline"] = cpu
+
+    # Every other configured workload, each in its own buffers after the
+    # headline's are freed (the oracle on a shorter sample of each).
+    workloads = {f"configs{WORKLOAD_ORDER.index(name)}": headline}
+    if not args.no_workloads:
+        del step, bufs
+        torch.cuda.empty_cache()
+        for idx, other in enumerate(WORKLOAD_ORDER):
+            if other == name:
+                continue
+            try:
+                workloads[f"configs{idx}"] = measure_workload(
+                    other, K, args.warmup, 0.0 if args.no_cpu_baseline else args.workload_cpu_seconds)
+            except Exception as e:  # noqa: BLE001 - report, do not lose the main line
+                workloads[f"configs{idx}"] = {"workload": other, "error": str(e)}
+        workloads = dict(sorted(workloads.items()))
 
     line = {
         "metric": "GDN verify tokens/s per layer + achieved HBM GB/s (fraction of peak), K=16",
@@ -495,6 +599,7 @@ def main():
         "phases_ms": phases,
         "rows": rows,
         "next_rows": next_rows,
+        "workloads": workloads,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

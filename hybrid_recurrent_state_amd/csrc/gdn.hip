@@ -869,6 +869,30 @@ hipError_t launch_any(const hrs_gdn_desc* d, GdnArgs& args, int n, int n_cu, int
                                  : launch_dk<64, float, FUSED>(args, n, n_cu, waves, mode, n_slots, s, e0, e1);
 }
 
+// The two device attributes a launch shape depends on, queried once per
+// device and thread (every layer of a step makes one call; the attribute
+// queries cost more than the rest of the host work of a call).
+struct DeviceLimits {
+  int n_cu;      // compute units (0: unknown, one block per 16-row unit)
+  int max_lds;   // LDS bytes a block may use
+};
+
+DeviceLimits device_limits() {
+  thread_local int cached_dev = -1;
+  thread_local DeviceLimits cached{0, 64 * 1024};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DeviceLimits{0, 64 * 1024};
+  if (dev != cached_dev) {
+    DeviceLimits lim{0, 64 * 1024};
+    if (hipDeviceGetAttribute(&lim.n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) lim.n_cu = 0;
+    if (hipDeviceGetAttribute(&lim.max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      lim.max_lds = 64 * 1024;
+    cached = lim;
+    cached_dev = dev;
+  }
+  return cached;
+}
+
 // Inputs of the fused layer: the conv input and weights replace q, k and v.
 struct FusedInputs {
   const void* x;
@@ -949,12 +973,8 @@ static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, co
   const int per_launch = tree ? std::max(1, (kGeomBytes / geom_per_pos) / d->n_pos) : 4096;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  int dev = 0, n_cu = 0, max_lds = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    n_cu = 0;  // falls back to one block per 16-row unit
-  if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-    max_lds = 64 * 1024;
+  const DeviceLimits lim = device_limits();
+  const int n_cu = lim.n_cu, max_lds = lim.max_lds;
   args.window = std::min(kWindow, static_cast<int>(d->n_pos));
   for (int r0 = 0; r0 < d->n_req; r0 += per_launch) {
     const int n = std::min(per_launch, d->n_req - r0);

@@ -370,7 +370,40 @@ class ZeroCopyVerifyStep(VerifyStep):
                                     b.accept_node.data_ptr(), b.status.data_ptr(), h), "rollback_restore")
 
     def capture_graph(self) -> None:
-        raise NotImplementedError("the zero-copy step alternates buffers; launch it eagerly")
+        """Record two HIP graphs, one per checkpoint-buffer parity: graph c
+        writes buffer c and starts every span from buffer 1 - c at the
+        accepted position the previous step left in ``accept_node``. Replays
+        alternate between them, as eager steps alternate buffers. The first
+        step of a speculation starts from ``state`` and is launched eagerly
+        (``replay`` does that by itself when no step has run yet)."""
+        import torch
+        first, cur = self.first, self.cur
+        self.graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        try:
+            self.first = False
+            for c in (0, 1):
+                self.cur = c
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    VerifyStep.launch(self, side)
+                    self._gather()
+                self.graphs.append(g)
+        finally:
+            self.first, self.cur = first, cur
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+
+    def replay(self):
+        """One step by replaying the graph of the current buffer parity (the
+        first step of a speculation eagerly), then the step's single host
+        sync."""
+        if self.first:
+            return self.run()
+        self.graphs[self.cur].replay()
+        self.cur ^= 1
+        return self._host()
 
 
 class FusedVerifyStep(ZeroCopyVerifyStep):

@@ -36,8 +36,10 @@
  *    except HRS_EDEVICE, which reports that the launch itself failed.
  *    Every argument check runs on the host before any HIP call, so the
  *    checks also work on a machine without a GPU.
- *  - Thread safety: the library holds no mutable global state (only a
- *    per-thread record of the last HIP error, see hrs_last_hip_error).
+ *  - Thread safety: the library holds no mutable global state shared
+ *    between threads; each thread keeps a record of its last HIP error (see
+ *    hrs_last_hip_error) and a cache of the device attributes its launches
+ *    need (compute units, LDS per block), keyed by the current device.
  *  - Determinism: results are bit-identical from run to run, and the
  *    arithmetic of one position does not depend on the span length or on the
  *    tree topology.
@@ -496,8 +498,7 @@ const char* hrs_strerror(int status);
 int hrs_abi_version(void);
 
 /* hipError_t of the last launch an entry point made on the calling thread
- * (0 = success): the detail behind HRS_EDEVICE. Per-thread; this record is
- * the library's only mutable state. */
+ * (0 = success): the detail behind HRS_EDEVICE. Per-thread. */
 int hrs_last_hip_error(void);
 
 /* hipGetErrorString() of hrs_last_hip_error(); never NULL. */

@@ -102,3 +102,39 @@ def test_full_size_step(idx):
         got = to_numpy(bufs.packed_out)
         assert np.array_equal(got, oring.ring_get(exp, np.zeros_like(loaded.packed), loaded.runs))
         say("ring ok")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_full_size_zero_copy_and_fused_steps(fused):
+    """The NEXT-row steps bench.py times, at the 16-request x 48-layer size:
+    the zero-copy step (spans start in place from the previous step's accepted
+    checkpoint, conv state rebuilt from the accepted path) and the same step
+    with every layer fused into one kernel. Two consecutive steps (the first
+    from the initial state, the second zero-copy); every request's acceptance
+    and sampled (layer, request) units of both steps against the oracle, the
+    second from the oracle's replay of the first step's accepted path."""
+    import torch
+    from hybrid_recurrent_state_amd.step import FusedVerifyStep, StepBuffers, ZeroCopyVerifyStep
+    from synth.device import fill_step, step_shape
+    from tests.step_oracle import TrackedUnit, unit_slices
+    torch.cuda.empty_cache()
+    w = WORKLOADS[WORKLOAD_ORDER[3]]
+    assert w.conv_channels == 2 * w.n_kheads * w.d_k + w.n_vheads * w.d_v
+    say(f"workload {w.name} ({'fused' if fused else 'zero-copy'} step): allocating and filling")
+    bufs = StepBuffers(step_shape(w))
+    loaded = fill_step(bufs, w)
+    cls = FusedVerifyStep if fused else ZeroCopyVerifyStep
+    step = cls(bufs, parent=loaded.parent, runs=loaded.runs)
+    units = [TrackedUnit(w, loaded, l, r, fused=fused) for (l, r) in [(0, 3), (47, 12), (30, 8)]]
+    for i in range(2):
+        say(f"step {i}")
+        acc_len, bonus = step.run()
+        torch.cuda.synchronize()
+        for r in range(w.n_req):
+            res = oacc.accept(oacc.argmax_rows(loaded.accept[r].logits), loaded.accept[r].tokens)
+            assert acc_len[r] == res.accept_len and bonus[r] == res.bonus, (i, r)
+        for tu in units:
+            tu.check(i, *unit_slices(bufs, step.current_ckpt(), tu.l, tu.r, with_y=not fused),
+                     what="full-size " + ("fused" if fused else "zero-copy"))
+    del step, bufs
+    torch.cuda.empty_cache()

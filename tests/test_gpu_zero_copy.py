@@ -2,35 +2,45 @@
 steps, the zero-copy step (spans start from the previous span's checkpoint at
 the accepted position; conv state rebuilt from the accepted path) must produce
 bit for bit what the checkpoint-copy step produces, and the materialised state
-must equal the copied one. Invalid indices leave outputs untouched and are
-counted in the status word."""
+must equal the copied one. Sampled (layer, request) units of every step are
+also checked against the oracle, whose state between steps is the replay of
+the accepted path from the previous step's state (openinfer PR #626, What
+Changed: conservative commit; lucebox PR #506, Summary: restore without
+replay). Graph replays of the zero-copy and fused steps are checked the same
+way. Invalid indices leave outputs untouched and are counted in the status
+word."""
 import numpy as np
 import pytest
 
 from oracle import rollback as orb
 from synth import QWEN_STACK_CHAIN, QWEN_STACK_TREE, QWEN_LAYER_CHAIN, bf16_bits, gen_unit, scaled
 from tests.gpu_util import say, to_numpy, to_torch
+from tests.step_oracle import TrackedUnit, unit_slices
 
 pytestmark = pytest.mark.gpu
 
 
-def make(w, zero_copy):
-    from hybrid_recurrent_state_amd.step import StepBuffers, VerifyStep, ZeroCopyVerifyStep
+def make(w, zero_copy, fused=False):
+    from hybrid_recurrent_state_amd.step import FusedVerifyStep, StepBuffers, VerifyStep, ZeroCopyVerifyStep
     from synth.device import fill_step, step_shape
     bufs = StepBuffers(step_shape(w))
     loaded = fill_step(bufs, w)
-    cls = ZeroCopyVerifyStep if zero_copy else VerifyStep
-    return bufs, cls(bufs, parent=loaded.parent, runs=loaded.runs)
+    cls = FusedVerifyStep if fused else (ZeroCopyVerifyStep if zero_copy else VerifyStep)
+    return bufs, cls(bufs, parent=loaded.parent, runs=loaded.runs), loaded
 
 
-@pytest.mark.parametrize("w", [
-    scaled(QWEN_STACK_CHAIN, n_layers=3, n_req=3, vocab=4096, ring_slots=64, ring_width=256),
-    scaled(QWEN_STACK_TREE, n_layers=2, n_req=2, vocab=4096),
-])
-def test_zero_copy_steps_equal_copy_steps(w):
+ZC_WORKLOADS = [
+    (scaled(QWEN_STACK_CHAIN, n_layers=3, n_req=3, vocab=4096, ring_slots=64, ring_width=256), [(0, 1), (2, 2)]),
+    (scaled(QWEN_STACK_TREE, n_layers=2, n_req=2, vocab=4096), [(1, 1)]),
+]
+
+
+@pytest.mark.parametrize("w,samples", ZC_WORKLOADS)
+def test_zero_copy_steps_equal_copy_steps(w, samples):
     import torch
-    std_bufs, std = make(w, False)
-    zc_bufs, zc = make(w, True)
+    std_bufs, std, _ = make(w, False)
+    zc_bufs, zc, loaded = make(w, True)
+    units = [TrackedUnit(w, loaded, l, r) for (l, r) in samples]
     for i in range(3):
         acc_s, bon_s = std.run()
         acc_z, bon_z = zc.run()
@@ -40,11 +50,47 @@ def test_zero_copy_steps_equal_copy_steps(w):
         assert np.array_equal(to_numpy(std_bufs.ckpt), to_numpy(zc.current_ckpt())), (i, "ckpt")
         if w.ring_slots:
             assert np.array_equal(to_numpy(std_bufs.packed_out), to_numpy(zc_bufs.packed_out)), i
+        for tu in units:
+            assert int(acc_z[tu.r]) == tu.acc.accept_len
+            tu.check(i, *unit_slices(zc_bufs, zc.current_ckpt(), tu.l, tu.r), what="zero-copy")
         say(f"step {i}: accepted {list(map(int, acc_z))}")
     zc.materialize()
     torch.cuda.synchronize()
     assert np.array_equal(to_numpy(std_bufs.state), to_numpy(zc_bufs.state))
     assert to_numpy(zc_bufs.status)[0] == 0
+    for tu in units:
+        tu.check_state(to_numpy(zc_bufs.state[tu.l, tu.r]), what="zero-copy")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("w,samples", ZC_WORKLOADS)
+def test_zero_copy_graph_replays(w, samples, fused):
+    """Two captured graphs (one per checkpoint-buffer parity) replayed
+    alternately, with unrelated eager work and host syncs between replays:
+    every replay equals the eagerly launched step bit for bit, and sampled
+    units equal the oracle."""
+    import torch
+    if fused:
+        w = scaled(w, conv_channels=2 * w.n_kheads * w.d_k + w.n_vheads * w.d_v)
+    e_bufs, eager, _ = make(w, True, fused)
+    g_bufs, graphed, loaded = make(w, True, fused)
+    graphed.capture_graph()
+    units = [TrackedUnit(w, loaded, l, r, fused=fused) for (l, r) in samples]
+    scratch = torch.randn(1 << 20, device="cuda")
+    for i in range(4):
+        acc_e, bon_e = eager.run()
+        acc_g, bon_g = graphed.replay()      # step 0 eagerly (from state), then graph parities 0, 1, 0
+        assert np.array_equal(acc_e, acc_g) and np.array_equal(bon_e, bon_g), i
+        names = ("argmax", "accept_node", "path", "out", "conv_state") + (() if fused else ("y",))
+        for name in names:
+            assert np.array_equal(to_numpy(getattr(e_bufs, name)), to_numpy(getattr(g_bufs, name))), (i, name)
+        assert np.array_equal(to_numpy(eager.current_ckpt()), to_numpy(graphed.current_ckpt())), (i, "ckpt")
+        for tu in units:
+            tu.check(i, *unit_slices(g_bufs, graphed.current_ckpt(), tu.l, tu.r, with_y=not fused),
+                     what=("fused" if fused else "zero-copy") + " graph")
+        scratch.mul_(1.0001).add_(0.5)
+        torch.cuda.synchronize()
+        say(f"replay {i}: accepted {list(map(int, acc_g))}")
 
 
 def test_span_from_invalid_node_writes_nothing():
