@@ -8,15 +8,24 @@
 //
 // MI355X design: the argmax rows are long (151,936 entries) and few (T per
 // request), so pass 1 splits every row into 8192-entry chunks, one block
-// each, streaming 16-byte loads; each block reduces a 64-bit key (ordered
-// value bits above the complemented index) and writes it to the caller's
-// workspace. Taking the maximum key realises "largest value, lowest index on
-// ties, NaN never wins" with plain integer compares, in any reduction order,
-// so the result is deterministic. Each pass-1 thread issues all its loads
-// before its first compare. Pass 2 is one wave per request: the lanes gather
-// the row keys (64-bit maximum per row in LDS), the draft tokens and the
-// parents together, then the acceptance walk runs over the T <= 64 positions
-// in LDS.
+// each, streaming 16-byte loads (each thread issues its four loads before its
+// first compare). A chunk is reduced in two passes over the registers: the
+// largest value by a chain of IEEE maximum operations over quieted values
+// (NaN never wins; three operands fold into one instruction), then the
+// lowest index holding that value (float equality, so -0 and +0 tie and the
+// lower index wins). Only the per-thread result becomes a 64-bit key (ordered
+// value bits above the complemented index); the block's maximum key goes to
+// the caller's workspace. Taking the maximum key realises "largest value,
+// lowest index on ties, NaN never wins" in any reduction order, so the result
+// is deterministic. (A 64-bit key per element cost ~14 vector instructions
+// per logit and made pass 1 compute-bound; this form costs ~5.) Pass 2 is one
+// wave per request: the lanes gather the row keys (64-bit maximum per row in
+// LDS), the draft tokens and the parents together, then the acceptance walk
+// runs over the T <= 64 positions in LDS. The kernel boundary orders the two
+// passes. (Finishing each request in pass 1 instead, in the block that counts
+// itself last in a per-request arrival counter, was slower: with 323 blocks
+// per request counting on one address the device-scope atomics serialise,
+// 72 us against 27 us for 16 requests x 17 rows of 151,936 logits.)
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -65,6 +74,37 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+constexpr int kIter = kChunk / (kThreads * 8);   // 16-byte slices per thread
+
+// The key of this thread's slices. Values are quieted first: in IEEE mode a
+// signalling NaN operand makes the hardware maximum return NaN (a bf16 NaN
+// whose top mantissa bit is clear widens to one), while a quiet NaN operand
+// is skipped. Slices it >= n_valid (past the row's end) take no part.
+__device__ __forceinline__ uint64_t thread_key(float (&v)[kIter][8], const int (&e)[kIter], int n_valid) {
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[it][i] = __builtin_canonicalizef(v[it][i]);
+    if (it < n_valid) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, v[it][i]);
+    }
+  }
+  uint32_t idx = 0xFFFFFFFFu;
+#pragma unroll
+  for (int it = kIter - 1; it >= 0; --it) {
+    if (it < n_valid) {
+#pragma unroll
+      for (int i = 7; i >= 0; --i) idx = v[it][i] == m ? static_cast<uint32_t>(e[it] + i) : idx;
+    }
+  }
+  if (idx != 0xFFFFFFFFu) return make_key(m, idx);
+  // No element equals m: every valid element is NaN (the key of the lowest
+  // index, below every number), or the thread has no valid slice.
+  return n_valid > 0 ? make_key(__builtin_nanf(""), static_cast<uint32_t>(e[0])) : 0;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const T* logits, uint64_t* keys, int32_t vocab,
                                                                   int32_t n_chunks) {
@@ -73,27 +113,21 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const T* logit
   const T* base = logits + static_cast<size_t>(row) * vocab;
   const int begin = chunk * kChunk;
   const int end = min(vocab, begin + kChunk);
-  // All of the thread's loads are issued before the first use (one memory
-  // latency per block); slices past the row's end re-read the chunk's last
-  // eight logits (end - 8 >= begin since vocab is a multiple of 8) and are
-  // given key 0, which never wins.
-  constexpr int kIter = kChunk / (kThreads * 8);
+  // All of the thread's loads are issued before the first use; slices past
+  // the row's end re-read the chunk's last eight logits (end - 8 >= begin
+  // since vocab is a multiple of 8) and are left out. Slice it starts at
+  // begin + (it * kThreads + tid) * 8, so the valid slices are a prefix.
   float v[kIter][8];
+  int e[kIter];
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
-    const int e = begin + (it * kThreads + threadIdx.x) * 8;
-    load8<T>(base + min(e, end - 8), v[it]);
+    e[it] = begin + (it * kThreads + threadIdx.x) * 8;
+    load8<T>(base + min(e[it], end - 8), v[it]);
   }
-  uint64_t best = 0;
+  int n_valid = 0;
 #pragma unroll
-  for (int it = 0; it < kIter; ++it) {
-    const int e = begin + (it * kThreads + threadIdx.x) * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint64_t key = e < end ? make_key(v[it][i], static_cast<uint32_t>(e + i)) : 0;
-      best = key > best ? key : best;
-    }
-  }
+  for (int it = 0; it < kIter; ++it) n_valid += e[it] < end ? 1 : 0;
+  uint64_t best = thread_key(v, e, n_valid);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
     const uint64_t o = shfl_xor_u64(best, m);

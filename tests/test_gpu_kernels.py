@@ -472,6 +472,80 @@ def test_accept_special_values(hrs, dtype):
     assert list(oacc.argmax_rows(logits)) == expect
 
 
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_accept_signalling_nan_patterns(hrs, dtype):
+    """NaN bit patterns whose quiet bit is clear (a bf16 NaN widens to such a
+    float32) never win either, before or after the true maximum, in the same
+    or another chunk; a row of them alone gives 0."""
+    V = 8192 + 1024
+    if dtype == F32:
+        pats = np.array([0x7F800001, 0xFF800001, 0x7FBFFFFF, 0x7FC00000], dtype=np.uint32)
+        rows = np.full((5, V), -3.0, dtype=np.float32)
+        bits = rows.view(np.uint32)
+    else:
+        pats = np.array([0x7F81, 0xFF81, 0x7FBF, 0xFFFF], dtype=np.uint16)
+        rows = bf16_bits(np.full((5, V), -3.0, dtype=np.float32))
+        bits = rows
+    bits[0, 5] = pats[0]; rows_max = {0: 4000}
+    bits[1, 8200] = pats[1]; rows_max[1] = 17
+    bits[2, :] = pats[2]                                # every entry NaN -> 0
+    bits[3, 0] = pats[0]; bits[3, 1] = pats[2]; rows_max[3] = 8191
+    bits[4, ::3] = pats[3]; rows_max[4] = V - 1
+    for r, i in rows_max.items():
+        if dtype == F32:
+            rows[r, i] = 1.5
+        else:
+            rows[r, i] = bf16_bits(np.float32(1.5))
+    tok = np.zeros((1, 5), dtype=np.int32)
+    got = gpu_accept(hrs, rows[None], tok)
+    expect = [4000, 17, 0, 8191, V - 1]
+    assert list(oacc.argmax_rows(rows)) == expect
+    assert list(got[0][0]) == expect
+
+
+def test_accept_workspace_reused_across_calls(hrs):
+    """Workspace contents are ignored on entry: one buffer serves consecutive
+    calls of different sizes, with garbage written into it between them, and
+    every result equals the oracle's."""
+    torch = _torch()
+    big = scaled(QWEN_STACK_CHAIN, n_req=5, vocab=24576)
+    small = scaled(QWEN_STACK_TREE, n_req=2, vocab=8200)
+    nbytes = max(hrs.accept_greedy_workspace_bytes(5, big.n_pos, big.vocab, hrs.HRS_BF16),
+                 hrs.accept_greedy_workspace_bytes(2, small.n_pos, small.vocab, hrs.HRS_BF16))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    for w in (big, small, big):
+        ws.fill_(0xA5)
+        acc = [gen_accept(w, r) for r in range(w.n_req)]
+        lg = np.stack([a.logits for a in acc])
+        tok = np.stack([a.tokens for a in acc])
+        par = np.stack([a.parent for a in acc]) if w.tree else None
+        R, T = tok.shape
+        outs = [torch.full(sh, -7, dtype=torch.int32, device="cuda") for sh in [(R, T), (R,), (R,), (R, T), (R,)]]
+        hrs.accept_greedy(to_torch(lg), to_torch(tok), *outs, ws, parent=par)
+        torch.cuda.synchronize()
+        check_accept([to_numpy(o) for o in outs], lg, tok, par)
+        assert [int(x) for x in to_numpy(outs[1])] == [a.planted_node for a in acc]
+
+
+def test_accept_tree_batch_over_two_launches(hrs):
+    """64-position trees for 50 requests: the parent table of one walk launch
+    holds 48 of them, so the walk runs as two launches over the requests'
+    keys and outputs."""
+    rng = np.random.default_rng(33)
+    R, T, V = 50, 64, 1024
+    par = np.stack([np.concatenate([[-1], [rng.integers(max(0, i - 3), i) for i in range(1, T)]])
+                    for _ in range(R)]).astype(np.int32)
+    lg = rng.standard_normal((R, T, V)).astype(np.float32)
+    oam = oacc.argmax_rows(lg)
+    tok = np.zeros((R, T), dtype=np.int32)
+    for r in range(R):
+        for t in range(1, T):
+            # the draft matches its parent's argmax on most positions
+            tok[r, t] = oam[r, par[r, t]] if rng.random() < 0.8 else (oam[r, par[r, t]] + 1) % V
+    got = gpu_accept(hrs, lg, tok, parent=par)
+    check_accept(got, lg, tok, par)
+
+
 # ---------------------------------------------------------------------------
 # rollback
 
