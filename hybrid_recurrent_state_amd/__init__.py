@@ -107,6 +107,7 @@ _SIGNATURES = {
     "accept_greedy_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AcceptDesc)]),
     "accept_greedy": (_i32, [ctypes.POINTER(AcceptDesc), _p, _p, _p, _p, _p, _p, _p, _p,
                              ctypes.c_size_t, _p]),
+    "accept_greedy_noalloc": (_i32, [ctypes.POINTER(AcceptDesc), _p, _p, _p, _p, _p, _p, _p, _p]),
     "rollback_restore": (_i32, [ctypes.POINTER(RollbackDesc), _p, _p, _p, _p, _p, _p, _p]),
     "ring_set_2d": (_i32, [ctypes.POINTER(RingDesc), _p, _p, _p]),
     "ring_get_2d": (_i32, [ctypes.POINTER(RingDesc), _p, _p, _p]),
@@ -505,6 +506,26 @@ def accept_greedy(logits, tokens, argmax, accept_node, accept_len, path, bonus, 
                            _ptr(accept_len), _ptr(path), _ptr(bonus), _ptr(workspace), nbytes,
                            _stream(stream))
     _check(st, "accept_greedy")
+
+
+ACCEPT_NOALLOC_MAX_BYTES = 1 << 20
+
+
+def accept_greedy_noalloc(logits, tokens, argmax, accept_node, accept_len, path, bonus, parent=None, stream=None):
+    """accept_greedy without a workspace: the library keeps the keys in a
+    fixed device array of ACCEPT_NOALLOC_MAX_BYTES per GPU (no allocation in
+    the call). Overlapping calls on one GPU share that array and race."""
+    R, T, V = logits.shape
+    chk = _Checks()
+    chk("logits", logits, None, _in_dtypes("logits", logits))
+    for name, t, shape in (("tokens", tokens, (R, T)), ("argmax", argmax, (R, T)), ("accept_node", accept_node, (R,)),
+                           ("accept_len", accept_len, (R,)), ("path", path, (R, T)), ("bonus", bonus, (R,))):
+        chk(name, t, shape, _i32t())
+    d, _keep = accept_desc(R, T, V, _dtype_code(logits), parent)
+    chk.on_gpu()
+    st = lib.accept_greedy_noalloc(ctypes.byref(d), _ptr(logits), _ptr(tokens), _ptr(argmax), _ptr(accept_node),
+                                   _ptr(accept_len), _ptr(path), _ptr(bonus), _stream(stream))
+    _check(st, "accept_greedy_noalloc")
 
 
 def rollback_restore(ckpt, state, conv_ckpt, conv_state, accept_node, status, stream=None):

@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "device.h"
 #include "internal.h"
@@ -233,26 +234,30 @@ extern "C" size_t accept_greedy_workspace_bytes(const hrs_accept_desc* d) {
   return static_cast<size_t>(d->n_req) * d->n_pos * accept_chunks(d) * sizeof(uint64_t);
 }
 
-extern "C" int accept_greedy(const hrs_accept_desc* d, const void* logits, const int32_t* tokens, int32_t* argmax,
-                             int32_t* accept_node, int32_t* accept_len, int32_t* path, int32_t* bonus,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+// Checks shared by both entry points; HRS_OK or the status to return.
+static int accept_check(const hrs_accept_desc* d, const void* logits, const int32_t* tokens, const int32_t* argmax,
+                        const int32_t* accept_node, const int32_t* accept_len, const int32_t* path,
+                        const int32_t* bonus) {
   if (d == nullptr) return HRS_EINVAL;
   if (d->topo == HRS_TREE || d->topo == HRS_CHAIN) {
     const int geo = check_topology(d->topo, d->parent, d->n_req < 1 ? 0 : d->n_req, d->n_pos);
     if (geo != HRS_OK) return geo;
   }
   if (!accept_desc_ok(d)) return HRS_EINVAL;
-  if (!logits || !tokens || !argmax || !accept_node || !accept_len || !path || !bonus || !workspace)
-    return HRS_EINVAL;
-  if (workspace_bytes < accept_greedy_workspace_bytes(d)) return HRS_EINVAL;
+  if (!logits || !tokens || !argmax || !accept_node || !accept_len || !path || !bonus) return HRS_EINVAL;
   if (!aligned16(logits) || !aligned16(tokens) || !aligned16(argmax) || !aligned16(accept_node) ||
-      !aligned16(accept_len) || !aligned16(path) || !aligned16(bonus) || !aligned16(workspace))
+      !aligned16(accept_len) || !aligned16(path) || !aligned16(bonus))
     return HRS_EALIGN;
+  return HRS_OK;
+}
 
+// Both passes of a checked call, with the pass-1 keys at `keys` (device
+// memory of accept_greedy_workspace_bytes(d) bytes).
+static int accept_launch(const hrs_accept_desc* d, const void* logits, const int32_t* tokens, int32_t* argmax,
+                         int32_t* accept_node, int32_t* accept_len, int32_t* path, int32_t* bonus, uint64_t* keys,
+                         hipStream_t s) {
   const int n_chunks = accept_chunks(d);
   const int rows = d->n_req * d->n_pos;
-  uint64_t* keys = static_cast<uint64_t*>(workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const dim3 grid1(rows * n_chunks);
   if (d->logit_dtype == HRS_BF16)
@@ -279,4 +284,67 @@ extern "C" int accept_greedy(const hrs_accept_desc* d, const void* logits, const
     if (launch_error() != hipSuccess) return HRS_EDEVICE;
   }
   return HRS_OK;
+}
+
+extern "C" int accept_greedy(const hrs_accept_desc* d, const void* logits, const int32_t* tokens, int32_t* argmax,
+                             int32_t* accept_node, int32_t* accept_len, int32_t* path, int32_t* bonus,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = accept_check(d, logits, tokens, argmax, accept_node, accept_len, path, bonus);
+  if (st != HRS_OK) return st;
+  if (workspace == nullptr || workspace_bytes < accept_greedy_workspace_bytes(d)) return HRS_EINVAL;
+  if (!aligned16(workspace)) return HRS_EALIGN;
+  return accept_launch(d, logits, tokens, argmax, accept_node, accept_len, path, bonus,
+                       static_cast<uint64_t*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// accept_greedy_noalloc: the pass-1 keys in a fixed device array instead of a
+// caller's workspace, for callers that cannot allocate.
+
+static_assert(HRS_ACCEPT_NOALLOC_MAX_BYTES % 256 == 0, "whole 256-byte lines");
+
+// One copy per GPU the library runs on, held until the process ends. In host
+// code this name is only a stand-in for the symbol: the device address of
+// each GPU's copy comes from hipGetSymbolAddress on that GPU.
+static __device__ __align__(256) unsigned char scratch[HRS_ACCEPT_NOALLOC_MAX_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_address[kMaxDevices];   // device address of `scratch` on each device, once looked up
+}  // namespace
+
+// The device address of `scratch` on the current device, looked up on the
+// first call on that device (with it current) and kept.
+static int scratch_address(void** out) {
+  int dev = 0;
+  const hipError_t e0 = hipGetDevice(&dev);
+  if (e0 != hipSuccess) {
+    set_last_hip_error(static_cast<int>(e0));
+    return HRS_EDEVICE;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return HRS_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_address[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    set_last_hip_error(static_cast<int>(e));
+    if (e != hipSuccess || p == nullptr) return HRS_EDEVICE;
+    g_scratch_address[dev] = p;
+  }
+  *out = g_scratch_address[dev];
+  return HRS_OK;
+}
+
+extern "C" int accept_greedy_noalloc(const hrs_accept_desc* d, const void* logits, const int32_t* tokens,
+                                     int32_t* argmax, int32_t* accept_node, int32_t* accept_len, int32_t* path,
+                                     int32_t* bonus, void* stream) {
+  const int st = accept_check(d, logits, tokens, argmax, accept_node, accept_len, path, bonus);
+  if (st != HRS_OK) return st;
+  if (accept_greedy_workspace_bytes(d) > HRS_ACCEPT_NOALLOC_MAX_BYTES) return HRS_EINVAL;
+  void* keys = nullptr;
+  const int sa = scratch_address(&keys);
+  if (sa != HRS_OK) return sa;
+  return accept_launch(d, logits, tokens, argmax, accept_node, accept_len, path, bonus, static_cast<uint64_t*>(keys),
+                       static_cast<hipStream_t>(stream));
 }

@@ -410,6 +410,30 @@ int accept_greedy(const hrs_accept_desc* desc, const void* logits, const int32_t
                   int32_t* path, int32_t* bonus, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/* Largest workspace accept_greedy_noalloc can use: 1 MiB, the pass-1 keys of
+ * up to 131,072 (row, 8192-logit chunk) pairs (e.g. 272 rows of 151,936
+ * logits need 41,344 bytes). */
+#define HRS_ACCEPT_NOALLOC_MAX_BYTES (1u << 20)
+
+/*
+ * accept_greedy_noalloc - accept_greedy for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the pass-1 keys live in a fixed device array of
+ * HRS_ACCEPT_NOALLOC_MAX_BYTES inside the library instead of a caller's
+ * workspace. The call itself allocates nothing. The array exists once per GPU
+ * and stays for the life of the process; its device address is looked up on
+ * the first call on each GPU (with that GPU current). Nothing in it needs to
+ * start at zero: every key a call reads is written by the same call.
+ * Calls that overlap in time on one GPU (different streams, or host threads
+ * sharing a GPU) share the array and race; serialise them.
+ * Arguments, results and errors as accept_greedy without the workspace,
+ * plus HRS_EINVAL when accept_greedy_workspace_bytes(desc) exceeds
+ * HRS_ACCEPT_NOALLOC_MAX_BYTES.
+ */
+int accept_greedy_noalloc(const hrs_accept_desc* desc, const void* logits, const int32_t* tokens,
+                          int32_t* argmax, int32_t* accept_node, int32_t* accept_len, int32_t* path,
+                          int32_t* bonus, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* On-device rollback                                                       */
 /* ------------------------------------------------------------------------ */

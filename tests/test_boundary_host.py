@@ -224,6 +224,34 @@ def test_accept_rejections_and_workspace_size():
     assert accept_call(n_req=2, n_pos=64, vocab=vmax) == (E.HRS_EINVAL, 0)
 
 
+def test_accept_noalloc_rejections():
+    """The entry point without a workspace: the same checks as accept_greedy,
+    and a size beyond its fixed device array rejected with HRS_EINVAL."""
+    E = hrs
+
+    def call(n_req=2, n_pos=5, vocab=1024, logits=FAKE, path=FAKE, parent=None):
+        keep = None
+        par = None
+        if parent is not None:
+            keep = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
+            par = keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        topo = hrs.HRS_TREE if parent is not None else hrs.HRS_CHAIN
+        d = hrs.AcceptDesc(n_req, n_pos, vocab, hrs.HRS_BF16, topo, par)
+        return hrs.lib.accept_greedy_noalloc(ctypes.byref(d), logits, FAKE, FAKE, FAKE, FAKE, path, FAKE, None)
+    assert hrs.lib.accept_greedy_noalloc(None, *([FAKE] * 7), None) == E.HRS_EINVAL
+    assert call(vocab=1001) == E.HRS_EINVAL
+    assert call(logits=None) == E.HRS_EINVAL
+    assert call(path=MIS) == E.HRS_EALIGN
+    assert call(n_pos=0) == E.HRS_EGEOMETRY
+    assert call(parent=[-1, 0, 0, 1, 7, -1, 0, 1, 1, 2]) == E.HRS_EGEOMETRY
+    # 128 x 64 rows x 19 chunks x 8 B of keys exceed the 1 MiB array; 64 x 64 rows fit
+    assert call(n_req=128, n_pos=64, vocab=151936) == E.HRS_EINVAL
+    assert hrs.ACCEPT_NOALLOC_MAX_BYTES == 1 << 20
+    # a well-formed call gets past every check; with no GPU visible the launch fails
+    assert call(n_req=64, n_pos=64, vocab=151936) == E.HRS_EDEVICE
+    assert call() == E.HRS_EDEVICE
+
+
 def rollback_call(**kw):
     d = dict(n_layers=2, n_req=3, n_pos=5, n_vheads=4, d_k=64, d_v=64, conv_channels=64, conv_width=4,
              conv_dtype=hrs.HRS_BF16)
