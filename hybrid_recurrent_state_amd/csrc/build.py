@@ -31,6 +31,11 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument"]
 HIP_FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-ffp-contract=off", "-mcode-object-version=5",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-file additions. gdn.hip: the span kernel's eight leading scalar arguments
+# (input pointers and packed shape) are preloaded into SGPRs by the hardware
+# at wave launch (kernel-argument preloading; the compiler emits a prologue
+# that loads them for firmware without it).
+FILE_FLAGS = {"gdn.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"]}
 
 
 def hipcc() -> str:
@@ -60,7 +65,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        jobs.append([cc] + COMMON + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([cc] + COMMON + HIP_FLAGS + FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         jobs.append([cc] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj])

@@ -95,6 +95,8 @@ constexpr size_t pipelined_bytes(int dk, int rows, int window) {
 // LDS bytes of one tree stash slot: every lane's dk / 16 floats of its row.
 constexpr size_t slot_bytes(int dk, int waves) { return static_cast<size_t>(waves) * 64 * (dk / 16) * sizeof(float); }
 
+// Kernel arguments of one launch. Every per-request pointer is offset to the
+// launch's first request (req0), so the kernel indexes requests from 0.
 struct GdnArgs {
   const void* q;
   const void* k;
@@ -120,6 +122,7 @@ struct GdnArgs {
   const int32_t* src_node;
   int32_t src_npos;
   int32_t n_req_total;
+  const int32_t* src_node_all;  // src_node of the whole call (not offset), for the status count
   int32_t* status;  // optional: number of requests whose src_node is out of range
   // Fused layer (gdn_layer_verify_span): conv input, weights and state; q, k
   // and v are computed from them instead of read.
@@ -137,6 +140,44 @@ struct GdnArgs {
   int8_t geom[kGeomBytes];
 };
 
+// What the first loads of a launch need: the input pointers and the shape.
+// They travel as leading scalar kernel arguments, which the hardware places
+// in SGPRs before the first instruction (kernel-argument preloading, enabled
+// for this file at build time), so the first data loads wait for no argument
+// load; the rest of GdnArgs is loaded alongside them. Pointers as in GdnArgs
+// (offset to the launch's first request).
+struct Hot {
+  const void* in0;     // q, or the conv input x (fused layer)
+  const void* in1;     // k, or the conv weights
+  const void* in2;     // v, or the conv state
+  const void* a;
+  const void* b;
+  const float* state;  // initial state; nullptr when the span starts from a source checkpoint
+  int n_pos;
+  int n_kheads;
+  int n_vheads;
+  int d_v;
+  int group;           // Hv / Hk
+};
+
+// The shape packed into two argument words: word A = n_pos | (d_v / 16) << 7 |
+// n_vheads << 12 (n_pos <= 64, d_v <= 256, n_vheads < 2^20), word B = n_kheads.
+inline uint32_t shape_word_a(int n_pos, int d_v, int n_vheads) {
+  return static_cast<uint32_t>(n_pos) | (static_cast<uint32_t>(d_v / 16) << 7) | (static_cast<uint32_t>(n_vheads) << 12);
+}
+
+__device__ __forceinline__ Hot make_hot(const void* in0, const void* in1, const void* in2, const void* a,
+                                        const void* b, const float* state, uint32_t wa, uint32_t wb) {
+  Hot h;
+  h.in0 = in0; h.in1 = in1; h.in2 = in2; h.a = a; h.b = b; h.state = state;
+  h.n_pos = static_cast<int>(wa & 0x7Fu);
+  h.d_v = static_cast<int>((wa >> 7) & 0x1Fu) * 16;
+  h.n_vheads = static_cast<int>(wa >> 12);
+  h.n_kheads = static_cast<int>(wb);
+  h.group = h.n_vheads / h.n_kheads;
+  return h;
+}
+
 // Sixteen consecutive elements as f32 (the source must be 16-byte aligned).
 template <typename TIn>
 __device__ __forceinline__ void load16(const TIn* p, float* o) {
@@ -144,24 +185,25 @@ __device__ __forceinline__ void load16(const TIn* p, float* o) {
   load8<TIn>(p + 8, o + 8);
 }
 
-// One row unit: rows [row0, row0 + RPB) of value head h of request r.
+// One row unit: rows [row0, row0 + RPB) of value head h of request r (the
+// index within this launch, which every launch pointer is offset to).
 struct Unit {
-  int r;     // request
-  int rl;    // request within this launch
+  int r;     // request within this launch
+  int rl;    // the same (geometry tables are per launch too)
   int h;     // value head
   int g;     // key head
   int row0;  // first row
 };
 
 // Units are numbered row block fastest, then value head, then request.
-__device__ __forceinline__ Unit unit_of(const GdnArgs& args, int W, int rpb) {
-  const int nrb = args.d_v / rpb;
+__device__ __forceinline__ Unit unit_of(const Hot& hs, int W, int rpb) {
+  const int nrb = hs.d_v / rpb;
   Unit u;
   u.row0 = (W % nrb) * rpb;
-  u.h = (W / nrb) % args.n_vheads;
-  u.rl = W / (nrb * args.n_vheads);
-  u.r = args.req0 + u.rl;
-  u.g = u.h / args.group;
+  u.h = (W / nrb) % hs.n_vheads;
+  u.rl = W / (nrb * hs.n_vheads);
+  u.r = u.rl;
+  u.g = u.h / hs.group;
   return u;
 }
 
@@ -170,11 +212,12 @@ __device__ __forceinline__ Unit unit_of(const GdnArgs& args, int W, int rpb) {
 // threads (p is the thread's index among them). q/k and v items share one
 // index space, so the staging takes as few rounds of loads as possible.
 template <int DK, int NTH, int RPB, int POS_FLOATS, typename TIn>
-__device__ __forceinline__ void stage_plain(const GdnArgs& args, float* buf, const Unit& u, int t0, int tn, int p) {
-  const int T = args.n_pos;
-  const TIn* qg = static_cast<const TIn*>(args.q);
-  const TIn* kg = static_cast<const TIn*>(args.k);
-  const TIn* vg = static_cast<const TIn*>(args.v);
+__device__ __forceinline__ void stage_plain(const GdnArgs& args, const Hot& hs, float* buf, const Unit& u, int t0,
+                                            int tn, int p) {
+  const int T = hs.n_pos;
+  const TIn* qg = static_cast<const TIn*>(hs.in0);
+  const TIn* kg = static_cast<const TIn*>(hs.in1);
+  const TIn* vg = static_cast<const TIn*>(hs.in2);
   constexpr int V8 = DK / 8;
   constexpr int R8 = RPB / 8;
   const int n_qk = tn * V8;
@@ -183,7 +226,7 @@ __device__ __forceinline__ void stage_plain(const GdnArgs& args, float* buf, con
     if (e < n_qk) {
       const int tt = e / V8;
       const int j = (e % V8) * 8;
-      const size_t src = ((static_cast<size_t>(u.r) * T + t0 + tt) * args.n_kheads + u.g) * DK + j;
+      const size_t src = ((static_cast<size_t>(u.r) * T + t0 + tt) * hs.n_kheads + u.g) * DK + j;
       float kv[8], qv[8];
       load8<TIn>(kg + src, kv);
       load8<TIn>(qg + src, qv);
@@ -199,7 +242,7 @@ __device__ __forceinline__ void stage_plain(const GdnArgs& args, float* buf, con
       const int tt = ev / R8;
       const int i0 = (ev % R8) * 8;
       const size_t src =
-          ((static_cast<size_t>(u.r) * T + t0 + tt) * args.n_vheads + u.h) * args.d_v + u.row0 + i0;
+          ((static_cast<size_t>(u.r) * T + t0 + tt) * hs.n_vheads + u.h) * hs.d_v + u.row0 + i0;
       float vv[8];
       load8<TIn>(vg + src, vv);
       float* lv = buf + tt * POS_FLOATS + 2 * DK + i0;
@@ -219,18 +262,19 @@ __device__ __forceinline__ void stage_plain(const GdnArgs& args, float* buf, con
 // t-3..t-1 (conv-state row t+m when negative); for a tree the host table
 // names them. Weight w[c][3] multiplies the current input.
 template <int DK, int NTH, int RPB, int POS_FLOATS, typename TIn, bool TREE>
-__device__ __forceinline__ void stage_fused(const GdnArgs& args, float* buf, const Unit& u, int t0, int tn, int p) {
+__device__ __forceinline__ void stage_fused(const GdnArgs& args, const Hot& hs, float* buf, const Unit& u, int t0,
+                                            int tn, int p) {
   constexpr int CPI = 16;            // channels per item
   constexpr int QL = DK / CPI;       // items of one q or k row (4 or 8: a DPP group)
   constexpr int VI = RPB / CPI;      // items of the unit's v rows at one position
   static_assert(QL == 4 || QL == 8, "q/k row items form a DPP group");
   static_assert(NTH % QL == 0, "staging threads cover whole q/k rows");
-  const int T = args.n_pos;
+  const int T = hs.n_pos;
   const int C = args.conv_c;
-  const int Hk = args.n_kheads;
-  const TIn* x = static_cast<const TIn*>(args.x);
-  const TIn* cs = static_cast<const TIn*>(args.conv_state);
-  const TIn* wc = static_cast<const TIn*>(args.conv_w);
+  const int Hk = hs.n_kheads;
+  const TIn* x = static_cast<const TIn*>(hs.in0);
+  const TIn* wc = static_cast<const TIn*>(hs.in1);
+  const TIn* cs = static_cast<const TIn*>(hs.in2);
   const int n_qk = tn * 2 * QL;
   const int total = n_qk + tn * VI;
   for (int e = p; e < total; e += NTH) {
@@ -247,7 +291,7 @@ __device__ __forceinline__ void stage_fused(const GdnArgs& args, float* buf, con
       const int i = e - n_qk;
       tt = i / VI;
       part = 2;
-      ch = 2 * Hk * DK + u.h * args.d_v + u.row0 + (i % VI) * CPI;
+      ch = 2 * Hk * DK + u.h * hs.d_v + u.row0 + (i % VI) * CPI;
       dst = buf + tt * POS_FLOATS + 2 * DK + (i % VI) * CPI;
     }
     const int t = t0 + tt;
@@ -297,12 +341,13 @@ __device__ __forceinline__ void stage_fused(const GdnArgs& args, float* buf, con
 // position loop would be a vector load whose wait also drains every
 // outstanding checkpoint store.
 template <int DK, int NTH, int RPB, int POS_FLOATS, typename TIn, bool TREE>
-__device__ __forceinline__ void stage_gates(const GdnArgs& args, float* buf, const Unit& u, int t0, int tn, int p) {
-  const int T = args.n_pos;
-  const TIn* ag = static_cast<const TIn*>(args.a);
-  const TIn* bg = static_cast<const TIn*>(args.b);
+__device__ __forceinline__ void stage_gates(const GdnArgs& args, const Hot& hs, float* buf, const Unit& u, int t0,
+                                            int tn, int p) {
+  const int T = hs.n_pos;
+  const TIn* ag = static_cast<const TIn*>(hs.a);
+  const TIn* bg = static_cast<const TIn*>(hs.b);
   for (int e = p; e < tn; e += NTH) {
-    const size_t src = (static_cast<size_t>(u.r) * T + t0 + e) * args.n_vheads + u.h;
+    const size_t src = (static_cast<size_t>(u.r) * T + t0 + e) * hs.n_vheads + u.h;
     buf[e * POS_FLOATS + 2 * DK + RPB] = load_elem<TIn>(ag, src);
     buf[e * POS_FLOATS + 2 * DK + RPB + 1] = load_elem<TIn>(bg, src);
     if constexpr (TREE) {
@@ -317,27 +362,28 @@ __device__ __forceinline__ void stage_gates(const GdnArgs& args, float* buf, con
 }
 
 template <int DK, int NTH, int RPB, int POS_FLOATS, typename TIn, bool TREE, bool FUSED>
-__device__ __forceinline__ void stage_window(const GdnArgs& args, float* buf, const Unit& u, int t0, int tn, int p) {
+__device__ __forceinline__ void stage_window(const GdnArgs& args, const Hot& hs, float* buf, const Unit& u, int t0,
+                                             int tn, int p) {
   if constexpr (FUSED)
-    stage_fused<DK, NTH, RPB, POS_FLOATS, TIn, TREE>(args, buf, u, t0, tn, p);
+    stage_fused<DK, NTH, RPB, POS_FLOATS, TIn, TREE>(args, hs, buf, u, t0, tn, p);
   else
-    stage_plain<DK, NTH, RPB, POS_FLOATS, TIn>(args, buf, u, t0, tn, p);
-  stage_gates<DK, NTH, RPB, POS_FLOATS, TIn, TREE>(args, buf, u, t0, tn, p);
+    stage_plain<DK, NTH, RPB, POS_FLOATS, TIn>(args, hs, buf, u, t0, tn, p);
+  stage_gates<DK, NTH, RPB, POS_FLOATS, TIn, TREE>(args, hs, buf, u, t0, tn, p);
 }
 
 // The unit's initial state rows: `state`, or for a zero-copy span the
 // previous span's checkpoint at the request's accepted position. nullptr when
 // that index is out of range (the request then writes nothing).
 template <int DK>
-__device__ __forceinline__ const float* initial_rows(const GdnArgs& args, const Unit& u) {
-  const size_t head_elems = static_cast<size_t>(args.d_v) * DK;
-  if (args.src_ckpt != nullptr) {
+__device__ __forceinline__ const float* initial_rows(const GdnArgs& args, const Hot& hs, const Unit& u) {
+  const size_t head_elems = static_cast<size_t>(hs.d_v) * DK;
+  if (hs.state == nullptr) {
     const int node = args.src_node[u.r];
     if (node < 0 || node >= args.src_npos) return nullptr;
-    return args.src_ckpt + ((static_cast<size_t>(u.r) * args.src_npos + node) * args.n_vheads + u.h) * head_elems +
+    return args.src_ckpt + ((static_cast<size_t>(u.r) * args.src_npos + node) * hs.n_vheads + u.h) * head_elems +
            static_cast<size_t>(u.row0) * DK;
   }
-  return args.state + (static_cast<size_t>(u.r) * args.n_vheads + u.h) * head_elems +
+  return hs.state + (static_cast<size_t>(u.r) * hs.n_vheads + u.h) * head_elems +
          static_cast<size_t>(u.row0) * DK;
 }
 
@@ -599,17 +645,17 @@ __device__ __forceinline__ void run_positions(const float* buf, f32x4* stash, f3
 // loads are issued before the input loads and all are written afterwards, so
 // the thread waits for memory once; otherwise each part waits in turn.
 template <int DK, int NTH, int RPB, int POS_FLOATS, typename TIn, bool FUSED, bool ONE_WAIT>
-__device__ __forceinline__ void produce_item(const GdnArgs& args, float* buf, float* state_lds, int* flag_lds,
-                                             const Unit& u, int t0, int tn, int p) {
+__device__ __forceinline__ void produce_item(const GdnArgs& args, const Hot& hs, float* buf, float* state_lds,
+                                             int* flag_lds, const Unit& u, int t0, int tn, int p) {
   constexpr int N4 = RPB * DK / 4;   // float4 chunks of a unit's state rows
   constexpr int SPT = (N4 + NTH - 1) / NTH;
   static_assert(kWindow <= NTH, "one gate pair per staging thread");
-  const int T = args.n_pos;
-  const float* init = t0 == 0 ? initial_rows<DK>(args, u) : nullptr;
+  const int T = hs.n_pos;
+  const float* init = t0 == 0 ? initial_rows<DK>(args, hs, u) : nullptr;
   if constexpr (ONE_WAIT) {
-    const TIn* ag = static_cast<const TIn*>(args.a);
-    const TIn* bg = static_cast<const TIn*>(args.b);
-    const size_t gsrc = (static_cast<size_t>(u.r) * T + t0 + min(p, tn - 1)) * args.n_vheads + u.h;
+    const TIn* ag = static_cast<const TIn*>(hs.a);
+    const TIn* bg = static_cast<const TIn*>(hs.b);
+    const size_t gsrc = (static_cast<size_t>(u.r) * T + t0 + min(p, tn - 1)) * hs.n_vheads + u.h;
     const float ga = load_elem<TIn>(ag, gsrc);
     const float gb = load_elem<TIn>(bg, gsrc);
     f32x4 sv[SPT];
@@ -618,9 +664,9 @@ __device__ __forceinline__ void produce_item(const GdnArgs& args, float* buf, fl
       for (int k = 0; k < SPT; ++k) sv[k] = reinterpret_cast<const f32x4*>(init)[min(p + k * NTH, N4 - 1)];
     }
     if constexpr (FUSED)
-      stage_fused<DK, NTH, RPB, POS_FLOATS, TIn, false>(args, buf, u, t0, tn, p);
+      stage_fused<DK, NTH, RPB, POS_FLOATS, TIn, false>(args, hs, buf, u, t0, tn, p);
     else
-      stage_plain<DK, NTH, RPB, POS_FLOATS, TIn>(args, buf, u, t0, tn, p);
+      stage_plain<DK, NTH, RPB, POS_FLOATS, TIn>(args, hs, buf, u, t0, tn, p);
     if (p < tn) {
       buf[p * POS_FLOATS + 2 * DK + RPB] = ga;
       buf[p * POS_FLOATS + 2 * DK + RPB + 1] = gb;
@@ -639,7 +685,7 @@ __device__ __forceinline__ void produce_item(const GdnArgs& args, float* buf, fl
       for (int k = 0; k < SPT; ++k)
         if (p + k * NTH < N4) reinterpret_cast<f32x4*>(state_lds)[p + k * NTH] = sv[k];
     }
-    stage_window<DK, NTH, RPB, POS_FLOATS, TIn, false, FUSED>(args, buf, u, t0, tn, p);
+    stage_window<DK, NTH, RPB, POS_FLOATS, TIn, false, FUSED>(args, hs, buf, u, t0, tn, p);
   }
   if (t0 == 0 && p == 0) flag_lds[0] = init != nullptr;
 }
@@ -658,7 +704,10 @@ __device__ __forceinline__ void produce_item(const GdnArgs& args, float* buf, fl
 // staging computes q, k and v from the conv input (conv, SiLU, split, q/k L2
 // norm) instead of loading them.
 template <int DK, int NW, int NP, typename TIn, bool TREE, bool RELOAD, bool CAPTURE, bool FUSED, int NX>
-__global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const GdnArgs args) {
+__global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const void* in0, const void* in1, const void* in2,
+                                                                       const void* ga, const void* gb,
+                                                                       const float* init_state, uint32_t shape_a,
+                                                                       uint32_t shape_b, const GdnArgs args) {
   constexpr int LPR = kLanesPerRow;
   constexpr int RPW = 64 / LPR;          // rows per wave
   constexpr int RPB = RPW * NW;          // rows per unit
@@ -670,9 +719,10 @@ __global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const Gdn
   constexpr int NC = NW * 64;            // consumer threads
 
   extern __shared__ float lds[];
-  const int T = args.n_pos;
-  const int Hv = args.n_vheads;
-  const int dv = args.d_v;
+  const Hot hs = make_hot(in0, in1, in2, ga, gb, init_state, shape_a, shape_b);
+  const int T = hs.n_pos;
+  const int Hv = hs.n_vheads;
+  const int dv = hs.d_v;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int li = lane % LPR;
@@ -699,20 +749,16 @@ __global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const Gdn
     // round trip after another before the first staging load.
     // (One asm statement takes every value, so that all loads are issued
     // before the single wait.)
-    asm volatile("" : : "s"(args.q), "s"(args.k), "s"(args.v), "s"(args.a), "s"(args.b), "s"(args.state),
-                 "s"(args.ckpt), "s"(args.out), "s"(args.n_pos), "s"(args.n_kheads), "s"(args.n_vheads),
-                 "s"(args.d_v), "s"(args.group), "s"(args.req0), "s"(args.n_units), "s"(args.n_blocks),
+    asm volatile("" : : "s"(args.state), "s"(args.ckpt), "s"(args.out), "s"(args.n_units), "s"(args.n_blocks),
                  "s"(args.window), "s"(args.q_scale), "s"(args.src_ckpt), "s"(args.src_node), "s"(args.src_npos),
                  "s"(args.geom_req));
-    if constexpr (FUSED)
-      asm volatile("" : : "s"(args.x), "s"(args.conv_w), "s"(args.conv_state), "s"(args.conv_c), "s"(args.silu),
-                   "s"(args.l2_eps));
-    f32x4* const stash = reinterpret_cast<f32x4*>(lds + staging_floats(args.window, POS_FLOATS));
+    if constexpr (FUSED) asm volatile("" : : "s"(args.conv_c), "s"(args.silu), "s"(args.l2_eps));
+    f32x4* const stash = reinterpret_cast<f32x4*>(lds + staging_floats(min(T, kWindow), POS_FLOATS));
     // NX further waves only help stage each window (they own no rows).
     const bool owner = NX == 0 || tid < NC;   // wave-uniform
     for (int W = blockIdx.x; W < args.n_units; W += args.n_blocks) {
-      const Unit u = unit_of(args, W, RPB);
-      const float* init = initial_rows<DK>(args, u);
+      const Unit u = unit_of(hs, W, RPB);
+      const float* init = initial_rows<DK>(args, hs, u);
       if (init == nullptr) continue;   // block-uniform: every thread has the same request
       if (owner) {
         init += static_cast<size_t>(row_blk) * DK;
@@ -724,7 +770,7 @@ __global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const Gdn
       for (int t0 = 0; t0 < T; t0 += kWindow) {
         const int tn = min(kWindow, T - t0);
         __syncthreads();  // LDS reads of the previous window (or unit) are done
-        stage_window<DK, NC + NX * 64, RPB, POS_FLOATS, TIn, TREE, FUSED>(args, lds, u, t0, tn, tid);
+        stage_window<DK, NC + NX * 64, RPB, POS_FLOATS, TIn, TREE, FUSED>(args, hs, lds, u, t0, tn, tid);
         __syncthreads();
         if (owner)
           run_positions<DK, NW, RPB, POS_FLOATS, TREE, RELOAD, CAPTURE>(lds, stash, s, t0, tn, ckpt_row0, out_r,
@@ -739,31 +785,34 @@ __global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const Gdn
     }
   } else {
     constexpr int NTH = NP * 64;           // producer threads
-    const int SB = staging_floats(args.window, POS_FLOATS);
+    // The window (args.window) is min(T, kWindow); computed here from the
+    // preloaded shape so that the LDS layout needs no argument load.
+    const int SB = staging_floats(min(T, kWindow), POS_FLOATS);
     float* const state_lds = lds + 2 * SB;
     int* const flag_lds = reinterpret_cast<int*>(state_lds + RPB * DK);
     const bool consumer = tid < NC;        // wave-uniform
     const int p = tid - NC;                // producer index
     const int nwin = (T + kWindow - 1) / kWindow;
-    const int n_my = static_cast<int>(blockIdx.x) < args.n_units
-                         ? (args.n_units - 1 - static_cast<int>(blockIdx.x)) / args.n_blocks + 1
-                         : 0;
-    const int n_items = n_my * nwin;       // (unit, window) pairs of this block, in order
 
     // Stage item i into buffer i % 2: all threads for item 0 (no checkpoint
-    // store is in flight yet), the producers for every later item.
-    auto item_unit = [&](int i) { return unit_of(args, blockIdx.x + (i / nwin) * args.n_blocks, RPB); };
-    if (n_items > 0)
-      produce_item<DK, (NW + NP) * 64, RPB, POS_FLOATS, TIn, FUSED, true>(args, lds, state_lds, flag_lds, item_unit(0),
-                                                                          0, min(kWindow, T), tid);
+    // store is in flight yet), the producers for every later item. Every
+    // block of a launch holds at least one unit (the grid never has more
+    // blocks than units), so item 0 is staged straight from the preloaded
+    // arguments, before anything waits for the rest of the argument block.
+    produce_item<DK, (NW + NP) * 64, RPB, POS_FLOATS, TIn, FUSED, true>(args, hs, lds, state_lds, flag_lds,
+                                                                        unit_of(hs, blockIdx.x, RPB), 0,
+                                                                        min(kWindow, T), tid);
     __syncthreads();
+    auto item_unit = [&](int i) { return unit_of(hs, blockIdx.x + (i / nwin) * args.n_blocks, RPB); };
+    const int n_my = (args.n_units - 1 - static_cast<int>(blockIdx.x)) / args.n_blocks + 1;
+    const int n_items = n_my * nwin;       // (unit, window) pairs of this block, in order
     bool valid = false;
     float* ckpt_row0 = nullptr;
     float* out_r = nullptr;
     for (int i = 0; i < n_items; ++i) {
       const int j = i % nwin;
       if (consumer && j == 0) {
-        const Unit u = unit_of(args, blockIdx.x + (i / nwin) * args.n_blocks, RPB);
+        const Unit u = unit_of(hs, blockIdx.x + (i / nwin) * args.n_blocks, RPB);
         valid = flag_lds[0] != 0;
         if (valid) {
 #pragma unroll
@@ -784,8 +833,9 @@ __global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const Gdn
         const int t0 = ((i + 1) % nwin) * kWindow;
         // The fused staging issues all its loads before its first wait; the
         // plain staging measured faster with its loads spread over the item.
-        produce_item<DK, NTH, RPB, POS_FLOATS, TIn, FUSED, FUSED>(args, lds + ((i + 1) & 1) * SB, state_lds, flag_lds,
-                                                                 item_unit(i + 1), t0, min(kWindow, T - t0), p);
+        produce_item<DK, NTH, RPB, POS_FLOATS, TIn, FUSED, FUSED>(args, hs, lds + ((i + 1) & 1) * SB, state_lds,
+                                                                 flag_lds, item_unit(i + 1), t0, min(kWindow, T - t0),
+                                                                 p);
       }
       __syncthreads();  // window i + 1 is staged; buffer i % 2 is free
     }
@@ -795,7 +845,7 @@ __global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const Gdn
   if (args.status != nullptr && args.req0 == 0 && blockIdx.x == 0 && tid == (NP > 0 ? NC : 0)) {
     int32_t bad = 0;
     for (int i = 0; i < args.n_req_total; ++i) {
-      const int32_t u = args.src_node[i];
+      const int32_t u = args.src_node_all[i];
       bad += (u < 0 || u >= args.src_npos) ? 1 : 0;
     }
     *args.status = bad;
@@ -811,8 +861,15 @@ hipError_t launch_one(GdnArgs& args, int grid, int n_slots, hipStream_t stream, 
   args.n_blocks = grid;
   const size_t lds = NP > 0 ? pipelined_bytes(DK, RPB, args.window)
                             : staging_bytes(DK, RPB, args.window, TREE) + (TREE ? n_slots * slot_bytes(DK, NW) : 0);
+  const void* in0 = FUSED ? args.x : args.q;
+  const void* in1 = FUSED ? args.conv_w : args.k;
+  const void* in2 = FUSED ? args.conv_state : args.v;
+  const float* init_state = args.src_ckpt != nullptr ? nullptr : args.state;
+  const uint32_t wa = shape_word_a(args.n_pos, args.d_v, args.n_vheads);
+  const uint32_t wb = static_cast<uint32_t>(args.n_kheads);
   hipExtLaunchKernelGGL((gdn_span_kernel<DK, NW, NP, TIn, TREE, RELOAD, CAPTURE, FUSED, NX>), dim3(grid),
-                        dim3((NW + NP + NX) * 64), lds, stream, start, stop, 0, args);
+                        dim3((NW + NP + NX) * 64), lds, stream, start, stop, 0, in0, in1, in2, args.a, args.b,
+                        init_state, wa, wb, args);
   return launch_error();
 }
 
@@ -956,6 +1013,7 @@ static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, co
   args.src_node = src ? src->node : nullptr;
   args.src_npos = src ? src->n_pos : 0;
   args.n_req_total = d->n_req;
+  args.src_node_all = args.src_node;
   args.status = src ? status : nullptr;
   args.x = fused ? fused->x : nullptr;
   args.conv_w = fused ? fused->conv_w : nullptr;
@@ -976,9 +1034,39 @@ static int gdn_span_impl(const hrs_gdn_desc* d, const void* q, const void* k, co
   const DeviceLimits lim = device_limits();
   const int n_cu = lim.n_cu, max_lds = lim.max_lds;
   args.window = std::min(kWindow, static_cast<int>(d->n_pos));
+  // Per-request strides of every per-request buffer; each launch gets its
+  // pointers offset to its first request.
+  const size_t es = dtype_size(d->in_dtype);
+  const size_t T_ = static_cast<size_t>(d->n_pos);
+  const size_t head = static_cast<size_t>(d->d_v) * d->d_k;
+  const size_t st_q = T_ * d->n_kheads * d->d_k * es, st_v = T_ * d->n_vheads * d->d_v * es;
+  const size_t st_g = T_ * d->n_vheads * es, st_state = static_cast<size_t>(d->n_vheads) * head;
+  const size_t st_x = T_ * static_cast<size_t>(args.conv_c) * es, st_cs = 3 * static_cast<size_t>(args.conv_c) * es;
+  const GdnArgs base = {q, k, v, a, b, state, ckpt, out};
+  const void* base_x = args.x;
+  const void* base_cs = args.conv_state;
+  const float* base_src = args.src_ckpt;
+  const int32_t* base_node = args.src_node;
+  auto at = [](const void* p, size_t bytes) -> const void* {
+    return p == nullptr ? nullptr : static_cast<const char*>(p) + bytes;
+  };
+  auto atf = [](float* p, size_t elems) -> float* { return p == nullptr ? nullptr : p + elems; };
   for (int r0 = 0; r0 < d->n_req; r0 += per_launch) {
     const int n = std::min(per_launch, d->n_req - r0);
+    const size_t r = static_cast<size_t>(r0);
     args.req0 = r0;
+    args.q = at(base.q, r * st_q);
+    args.k = at(base.k, r * st_q);
+    args.v = at(base.v, r * st_v);
+    args.a = at(base.a, r * st_g);
+    args.b = at(base.b, r * st_g);
+    args.state = atf(base.state, r * st_state);
+    args.ckpt = atf(base.ckpt, r * T_ * st_state);
+    args.out = atf(base.out, r * T_ * d->n_vheads * d->d_v);
+    args.x = at(base_x, r * st_x);
+    args.conv_state = at(base_cs, r * st_cs);
+    args.src_ckpt = base_src == nullptr ? nullptr : base_src + r * static_cast<size_t>(args.src_npos) * st_state;
+    args.src_node = base_node == nullptr ? nullptr : base_node + r;
     // The first launch records the start event, the last one the stop event.
     hipEvent_t e0 = r0 == 0 ? static_cast<hipEvent_t>(start_event) : nullptr;
     hipEvent_t e1 = r0 + n >= d->n_req ? static_cast<hipEvent_t>(stop_event) : nullptr;
