@@ -356,8 +356,24 @@ def gdn_launch_stats(step, stream, L: int, K: int) -> dict:
         e1.record()
         torch.cuda.synchronize()
         stack.append(e0.elapsed_time(e1) / L)
+    # The same span-only stacks with every dispatch timing itself: the
+    # kernel's duration when the previous kernel is the same one. (On this
+    # GPU a kernel that follows a different kernel takes 1-2.5 us longer, the
+    # same for a plain store stream: in the step each span follows a conv.)
+    so = []
+    reps = max(1, min(K, 10))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+    evh = [(hrs.event_handle(a), hrs.event_handle(b)) for (a, b) in evs]
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        for l in range(L):
+            step.launch_gdn(l, h, evh[l])
+        torch.cuda.synchronize()
+        so += [evs[l][0].elapsed_time(evs[l][1]) for l in range(L)]
+    so = np.array(so)
     return {"avg_s": float(gdn_ms.mean()) / 1e3, "median_s": float(np.median(gdn_ms)) / 1e3,
             "min_s": float(gdn_ms.min()) / 1e3, "stack_s": float(np.median(stack)) / 1e3, "phases": phases,
+            "span_only_avg_s": float(so.mean()) / 1e3, "span_only_median_s": float(np.median(so)) / 1e3,
             "t_events": (t2, t3)}
 
 
@@ -396,9 +412,32 @@ def measure_workload(name: str, steps: int, warmup: int, cpu_seconds: float) -> 
            "median_launch_us": gs["median_s"] * 1e6, "min_launch_us": gs["min_s"] * 1e6,
            "frac": nbytes / gs["avg_s"] / 1e9 / HBM_PEAK_GBS,
            "stack_us_per_layer": gs["stack_s"] * 1e6, "stack_frac": nbytes / gs["stack_s"] / 1e9 / HBM_PEAK_GBS,
+           "span_only_launch_avg_us": gs["span_only_avg_s"] * 1e6,
+           "span_only_launch_median_us": gs["span_only_median_s"] * 1e6,
+           "span_only_frac": nbytes / gs["span_only_avg_s"] / 1e9 / HBM_PEAK_GBS,
            "traffic": measured_traffic(name), "phases_ms": gs["phases"]}
+    # The NEXT-row steps on the same buffers: f3 (the step as one graph), f2
+    # (zero-copy rollback), f1 (fused layers) and their graph replays.
+    nxt = {"f3_hip_graph_step_ms": time_steps(step, stream, steps, warmup, graph=True)}
+    if w.vocab:
+        from hybrid_recurrent_state_amd.step import FusedVerifyStep, ZeroCopyVerifyStep
+        variants = [("f2_zero_copy_step_ms", ZeroCopyVerifyStep)]
+        if shape.conv_channels == 2 * w.n_kheads * w.d_k + w.n_vheads * w.d_v:
+            variants.append(("f1_fused_layer_step_ms", FusedVerifyStep))
+        for key, cls in variants:
+            v = cls(bufs, parent=loaded.parent, runs=loaded.runs)
+            nxt[key] = time_steps(v, stream, steps, warmup)
+            del v
+            v = cls(bufs, parent=loaded.parent, runs=loaded.runs)
+            v.run(stream)
+            nxt[key.replace("_step_ms", "_graph_step_ms")] = time_steps(v, stream, steps, warmup, graph=True)
+            del v
+        bufs.ckpt2 = None
+    rec["next_rows"] = nxt
+    log(f"  next rows {nxt}")
     log(f"  step {ms:.3f} ms, gdn launch avg {rec['avg_launch_us']:.2f} us (frac {rec['frac']:.3f}), "
-        f"stack {rec['stack_us_per_layer']:.2f} us (frac {rec['stack_frac']:.3f})")
+        f"stack {rec['stack_us_per_layer']:.2f} us (frac {rec['stack_frac']:.3f}), span-only launches avg "
+        f"{rec['span_only_launch_avg_us']:.2f} us (frac {rec['span_only_frac']:.3f})")
     del step, bufs
     torch.cuda.empty_cache()
     if cpu_seconds > 0:
@@ -546,6 +585,9 @@ def main():
                 "avg_launch_us": gdn_avg_s * 1e6, "median_launch_us": gdn_med_s * 1e6,
                 "min_launch_us": gs["min_s"] * 1e6, "frac": achieved / HBM_PEAK_GBS,
                 "stack_us_per_layer": stack_s * 1e6, "stack_frac": gdn_bytes / stack_s / 1e9 / HBM_PEAK_GBS,
+                "span_only_launch_avg_us": gs["span_only_avg_s"] * 1e6,
+                "span_only_launch_median_us": gs["span_only_median_s"] * 1e6,
+                "span_only_frac": gdn_bytes / gs["span_only_avg_s"] / 1e9 / HBM_PEAK_GBS,
                 "traffic": traffic, "phases_ms": phases}
     cpu = None
     if not args.no_cpu_baseline:
@@ -593,7 +635,9 @@ def main():
                      "avg_launch_us": gdn_avg_s * 1e6, "median_launch_us": gdn_med_s * 1e6,
                      "store_stream_gbs": store_gbs, "frac_of_store_stream": achieved / store_gbs,
                      "stack_us_per_layer": stack_s * 1e6,
-                     "stack_frac": gdn_bytes / stack_s / 1e9 / HBM_PEAK_GBS},
+                     "stack_frac": gdn_bytes / stack_s / 1e9 / HBM_PEAK_GBS,
+                     "span_only_launch_avg_us": gs["span_only_avg_s"] * 1e6,
+                     "span_only_frac": gdn_bytes / gs["span_only_avg_s"] / 1e9 / HBM_PEAK_GBS},
         "gdn_tokens_per_s_per_layer": R * T / gdn_avg_s,
         "draft_tokens_per_s_per_layer": R * (T - 1) * L / (ms_per_step / 1e3),
         "phases_ms": phases,

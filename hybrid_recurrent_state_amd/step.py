@@ -212,9 +212,15 @@ class VerifyStep:
         """The conv span of layer l alone."""
         _check(lib.conv1d_verify_span(self.conv_p, *self.layer_args[l][0], stream), "conv1d_verify_span")
 
-    def launch_gdn(self, l: int, stream: int) -> None:
-        """The GDN span of layer l alone (its inputs as the step leaves them)."""
-        _check(lib.gdn_verify_span(self.gdn_p, *self.layer_args[l][1], stream), "gdn_verify_span")
+    def launch_gdn(self, l: int, stream: int, events=None) -> None:
+        """The GDN span of layer l alone (its inputs as the step leaves them).
+        events: optional (start, stop) raw hipEvent_t handles recorded by the
+        dispatch itself."""
+        if events is None:
+            _check(lib.gdn_verify_span(self.gdn_p, *self.layer_args[l][1], stream), "gdn_verify_span")
+        else:
+            _check(lib.gdn_verify_span_timed(self.gdn_p, *self.layer_args[l][1], stream, events[0], events[1]),
+                   "gdn_verify_span")
 
     def launch_accept(self, stream: int) -> None:
         if self.accept_desc is not None:
