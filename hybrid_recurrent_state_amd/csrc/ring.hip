@@ -1,9 +1,9 @@
 // ring_set_2d / ring_get_2d: batched feature-ring row copies with wraparound.
 //
 // lucebox PR #533 ("feat: DFlash support for tensor-parallel Qwen3.6
-// targets"), Changes: synchronise the feature ring with one get_2d and one
-// set_2d per non-wrapping run, instead of two host/device transfers and a
-// stream synchronisation per token.
+// targets"), Changes: the draft's feature ring is kept in step on the device
+// by 2-D row copies (a set and a get per stretch of rows that does not wrap),
+// so no per-token host round trip or stream wait is left.
 //
 // MI355X design: the host splits wrapping runs into non-wrapping segments and
 // passes them in the kernel arguments, so one launch copies every row of

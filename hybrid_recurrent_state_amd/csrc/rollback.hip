@@ -3,10 +3,11 @@
 // index read from device memory.
 //
 // lucebox PR #533 ("feat: DFlash support for tensor-parallel Qwen3.6
-// targets"), Changes: restore SSM and convolution state on device and
-// synchronize once after rollback. lucebox PR #506 ("perf(dflash):
-// split-chain fast rollback with F32 SSM checkpoints"), Summary: restore
-// the captured F32 checkpoint instead of replaying the accepted tokens.
+// targets"), Changes: both states go back to the accepted position without
+// leaving the device, with a single wait once the rollback is done. lucebox
+// PR #506 ("perf(dflash): split-chain fast rollback with F32 SSM
+// checkpoints"), Summary: the state comes from the float32 checkpoint that
+// verification stored at that position, so no accepted token is re-run.
 //
 // MI355X design: a plain HBM-bound copy. The grid is (64 KiB chunk, layer x
 // request) of 1024-thread blocks; each thread issues four 16-byte
