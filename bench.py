@@ -154,8 +154,8 @@ def cpu_baseline(w, seconds: float):
 
 def chunked_prefill_row(reps: int = 10, T: int = 1024, R: int = 1):
     """f4: one long chain span without capture (prefill length T) on the Qwen
-    GDN layer shape, by gdn_span_chunked (one launch, 64-position chunks,
-    k k^T on the matrix cores) and by the recurrent kernel (gdn_verify_span
+    GDN layer shape, by gdn_span_chunked (a pre-pass over all chunks, then
+    the sequential pass; 64-position chunks, matrix cores) and by the recurrent kernel (gdn_verify_span
     without capture, T / 64 launches of 64 positions carrying the state in
     place). Inputs: seeded bf16 q, k (unit norm), v, gates as in synth."""
     import torch
@@ -171,9 +171,10 @@ def chunked_prefill_row(reps: int = 10, T: int = 1024, R: int = 1):
     state0 = rn(R, Hv, d, d) * 0.02
     out = torch.empty(R, T, Hv, d, device="cuda")
     st = state0.clone()
+    ws = torch.empty(hrs.gdn_span_chunked_workspace_bytes(R, T, Hk, Hv), dtype=torch.uint8, device="cuda")
 
     def chunked():
-        hrs.gdn_span_chunked(q, k, v, a, b, st, None, out)
+        hrs.gdn_span_chunked(q, k, v, a, b, st, None, out, ws)
 
     def recurrent():
         for t0 in range(0, T, 64):
@@ -194,7 +195,8 @@ def chunked_prefill_row(reps: int = 10, T: int = 1024, R: int = 1):
     b16 = torch.sigmoid(rn(R16, T16, Hv)).to(torch.bfloat16)
     st16 = rn(R16, Hv, d, d) * 0.02
     out16 = torch.empty(R16, T16, Hv, d, device="cuda")
-    for name, fn in (("chunked_r16", lambda: hrs.gdn_span_chunked(q16, k16, v16, a16, b16, st16, None, out16)),
+    ws16 = torch.empty(hrs.gdn_span_chunked_workspace_bytes(R16, T16, Hk, Hv), dtype=torch.uint8, device="cuda")
+    for name, fn in (("chunked_r16", lambda: hrs.gdn_span_chunked(q16, k16, v16, a16, b16, st16, None, out16, ws16)),
                      ("recurrent_r16", lambda: hrs.gdn_verify_span(q16, k16, v16, a16, b16, st16, None, out16))):
         for _ in range(2):
             fn()
@@ -206,7 +208,7 @@ def chunked_prefill_row(reps: int = 10, T: int = 1024, R: int = 1):
         e1.record()
         torch.cuda.synchronize()
         res[name] = e0.elapsed_time(e1) / reps
-    del q16, k16, v16, a16, b16, st16, out16
+    del q16, k16, v16, a16, b16, st16, out16, ws16
     for name, fn in (("chunked", chunked), ("recurrent", recurrent)):
         for _ in range(2):
             fn()

@@ -98,7 +98,9 @@ _SIGNATURES = {
     "gdn_verify_span_timed": (_i32, [ctypes.POINTER(GdnDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "gdn_verify_span_from": (_i32, [ctypes.POINTER(GdnDesc), ctypes.POINTER(SpanSource), _p, _p, _p, _p, _p, _p,
                                     _p, _p, _p]),
-    "gdn_span_chunked": (_i32, [ctypes.POINTER(ChunkedDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "gdn_span_chunked_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(ChunkedDesc)]),
+    "gdn_span_chunked": (_i32, [ctypes.POINTER(ChunkedDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t,
+                                _p]),
     "gdn_layer_verify_span": (_i32, [ctypes.POINTER(GdnLayerDesc), _p, _p, _p, _p, _p, _p,
                                      ctypes.POINTER(SpanSource), _p, _p, _p, _p]),
     "conv1d_verify_span_nocapture": (_i32, [ctypes.POINTER(ConvDesc), _p, _p, _p, _p, _p]),
@@ -350,10 +352,18 @@ def gdn_verify_span_from(src_ckpt, src_node, q, k, v, a, b, ckpt, out, parent=No
     _check(st, "gdn_verify_span_from")
 
 
-def gdn_span_chunked(q, k, v, a, b, state, ckpt, out, q_scale: float = 1.0, log_gates: bool = False, stream=None):
+def gdn_span_chunked_workspace_bytes(n_req: int, n_pos: int, n_kheads: int, n_vheads: int, d: int = 128) -> int:
+    """Device workspace bytes gdn_span_chunked needs for these sizes."""
+    g = GdnDesc(n_req, n_pos, n_kheads, n_vheads, d, d, HRS_BF16, 1.0, HRS_CHAIN, None)
+    return int(lib.gdn_span_chunked_workspace_bytes(ctypes.byref(ChunkedDesc(g, 0, HRS_F32))))
+
+
+def gdn_span_chunked(q, k, v, a, b, state, ckpt, out, workspace, q_scale: float = 1.0, log_gates: bool = False,
+                     stream=None):
     """Chunked (64-position) gated delta rule over a long chain span: same
     arguments as gdn_verify_span without a parent; ckpt None updates state
-    in place. log_gates: `a` holds log decays. out may be f32 or bf16."""
+    in place. log_gates: `a` holds log decays. out may be f32 or bf16.
+    workspace: device tensor of at least gdn_span_chunked_workspace_bytes."""
     R, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     torch = _torch()
@@ -367,11 +377,13 @@ def gdn_span_chunked(q, k, v, a, b, state, ckpt, out, q_scale: float = 1.0, log_
     chk("state", state, (R, Hv, dv, dk), _f32())
     chk("ckpt", ckpt, (R, T, Hv, dv, dk), _f32(), optional=True)
     chk("out", out, (R, T, Hv, dv), (torch.float32, torch.bfloat16))
+    chk("workspace", workspace)
     chk.on_gpu()
     g = GdnDesc(R, T, Hk, Hv, dk, dv, _dtype_code(q), float(q_scale), HRS_CHAIN, None)
     d = ChunkedDesc(g, int(bool(log_gates)), _dtype_code(out))
+    nbytes = workspace.numel() * workspace.element_size()
     st = lib.gdn_span_chunked(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(state), _ptr(ckpt),
-                              _ptr(out), _stream(stream))
+                              _ptr(out), _ptr(workspace), nbytes, _stream(stream))
     _check(st, "gdn_span_chunked")
 
 

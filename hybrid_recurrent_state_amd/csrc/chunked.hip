@@ -9,35 +9,33 @@
 // it inside a chunk of C positions starting from state S_0: with
 // G[t][j] = a_{j+1} ... a_t (G[t][t] = 1) and g_t = a_0 ... a_t,
 //   w_t + sum_{j<t} b_t G[t][j] (k_t . k_j) w_j = b_t (v_t - g_t S_0 k_t),
-// a unit lower-triangular system (I + A) W = Y for all value rows at once.
-// After solving it the states and outputs follow from the cheap rank-1
-// recurrence S_t = a_t S_{t-1} + w_t k_t^T, which has no dot product on its
-// critical path.
+// a unit lower-triangular system (I + A) W = Y for all value rows at once, so
+// W = T Y with T = (I + A)^-1. The outputs need no state either:
+//   o_t = g_t S_0 q_t + sum_{j<=t} P[t][j] w_j,  P[t][j] = G[t][j] (q_t . k_j),
+// i.e. O = g QS + (P T) Y; and the chunk-end state is
+//   S_C = g_{C-1} S_0 + sum_t G[C-1][t] w_t k_t^T.
+// T, P T, g and G[C-1][.] depend on k, q and the gates only, not on S_0.
 //
-// The outputs need no state either: o_t = g_t S_0 q_t + sum_{j<=t} G[t][j]
-// (q_t . k_j) w_j.
-//
-// MI355X design. One block of 4 waves per (request, value head, 16 state
-// rows); each lane keeps 8 columns of one row of S in VGPRs across all
-// chunks (the layout of gdn_verify_span). Per chunk of 64 positions:
-//  1. k, q and the block's v rows staged in LDS as f32 from registers that
-//     were loaded while the previous chunk was processed;
-//  2. K K^T and Q K^T (64 x 64 each) on the matrix cores (bf16 inputs:
-//     32x32x16 MFMA, exact products and f32 accumulation, one 32x32 tile of
-//     each per wave; f32 inputs: vector FMA), and X = K S_0^T, QS = Q S_0^T
-//     for the block's rows (16x16x4 f32 MFMA, one 16-position tile per wave);
-//  3. G, g, A = strictly lower (b_t G[t][j] (K K^T)[t][j]) and P = lower
-//     (G[t][j] (Q K^T)[t][j]) by running products, four lanes per row
-//     (16 columns each, the decays above a lane's segment from the other
-//     lanes; no division, no logarithm: zero and tiny decays are exact);
-//  4. Y = b (V - g X), then (I + A) W = Y by blocks of 16 positions: a
-//     block-row update by all threads, then forward substitution inside the
-//     16 x 16 diagonal block with one lane per state row;
-//  5. outputs O = g QS + P W;
-//  6. with capture, states S_t = a_t S_{t-1} + w_t k_t^T (8 FMAs per lane
-//     and position, no dot product), each stored with nontemporal 16-byte
-//     stores; without, only the chunk-end state S_C = g S_0 + (G_C W)^T K on
-//     the matrix cores.
+// MI355X design: two kernels per segment of up to 32 chunks.
+//  * Pre-pass, one block of 4 waves per (request, value head, chunk), all
+//    chunks in parallel: K K^T and Q K^T on the matrix cores (bf16 inputs:
+//    32x32x16 MFMA, exact products, f32 accumulation), the decay products
+//    (running products, four lanes per row, no division or logarithm: zero
+//    and tiny decays are exact), T by forward substitution (four lanes per
+//    column, the partial sums joined by DPP), P T (16x16x4 f32 MFMA); written
+//    to the caller's workspace.
+//  * Sequential kernel, one block of 4 waves per (request, value head, 16
+//    state rows); each lane keeps 8 columns of one row of S in VGPRs across
+//    all chunks (the layout of gdn_verify_span). Per chunk: X = K S_0^T and
+//    QS = Q S_0^T (16x16x4 f32 MFMA), Y = b (V - g X), then W = T Y and
+//    P T Y with one pass of MFMAs over Y, the outputs, and the state: with
+//    capture S_t = a_t S_{t-1} + w_t k_t^T (8 FMAs per lane and position,
+//    no dot product), each stored with nontemporal 16-byte stores; without,
+//    the chunk-end state on the matrix cores. The next chunk's inputs and
+//    pre-pass record are loaded into registers while a chunk is processed.
+//    Blocks are ordered so that the 8 row blocks of one head fall on one XCD
+//    (workgroups go to XCDs round robin), where they share the head's k, q,
+//    T and P T through that XCD's L2.
 // Positions past the end of the span are padded with a = 1, b = 0, k = q =
 // v = 0 (identity steps) and never streamed.
 #include <hip/hip_runtime.h>
@@ -52,32 +50,54 @@ namespace {
 
 constexpr int kC = 64;          // positions per chunk
 constexpr int kDK = 128;        // d_k = d_v (the built size)
-constexpr int kRows = 16;       // state rows per block
+constexpr int kRows = 16;       // state rows per sequential block
+constexpr int kRowBlocks = kDK / kRows;
 constexpr int kThreads = 256;   // 4 waves
 constexpr int kLPR = 16;        // lanes per state row in the streaming pass
 constexpr int kNCH = kDK / (4 * kLPR);   // float4 chunks per lane (2)
 constexpr int kKS = kDK + 4;    // LDS row stride of k and q (spreads 4 rows over banks)
 constexpr int kSS = kDK + 4;    // LDS row stride of the state rows (16-byte rows, 4-bank offsets)
-constexpr int kAS = kC + 4;     // LDS row stride of K K^T / A and Q K^T / P (16-byte rows)
+constexpr int kTS = kC + 4;     // LDS row stride of the 64-wide matrices (16-byte rows)
+constexpr int kSegChunks = 32;  // chunks per pre-pass + sequential launch pair
 
-// LDS layout, in floats.
-constexpr int kOffK = 0;
-constexpr int kOffQ = kOffK + kC * kKS;
+// Pre-pass record of one (request, value head, chunk) in the workspace, in
+// floats: T = (I + A)^-1 and P T row-major, then g_t and G[C-1][t].
+constexpr int kRecT = 0;
+constexpr int kRecPT = kRecT + kC * kC;
+constexpr int kRecG = kRecPT + kC * kC;
+constexpr int kRecGC = kRecG + kC;
+constexpr int kRecFloats = kRecGC + kC;
+
+// Sequential kernel LDS layout, in floats.
+constexpr int kOffK = 0;                          // [C][kKS] k rows (f32)
+constexpr int kOffQ = kOffK + kC * kKS;           // [C][kKS] q rows (f32, unscaled)
 constexpr int kOffV = kOffQ + kC * kKS;           // [C][16] v rows of the block
 constexpr int kOffS0 = kOffV + kC * kRows;        // [16][kSS] S_0 rows
-constexpr int kOffA = kOffS0 + kRows * kSS;       // [C][kAS] K K^T, then A
-constexpr int kOffP = kOffA + kC * kAS;           // [C][kAS] Q K^T, then P = G (Q K^T), lower incl.
-constexpr int kOffX = kOffP + kC * kAS;           // [C][16] X, then Y, then W
-constexpr int kOffQS = kOffX + kC * kRows;        // [C][16] Q S_0^T
-constexpr int kOffGC = kOffQS + kC * kRows;       // [C] G[n-1][t]: decay from position t to the chunk end
-constexpr int kOffG = kOffGC + kC;                // [C] g_t
-constexpr int kOffAv = kOffG + kC;                // [C] a_t
+constexpr int kOffT = kOffS0 + kRows * kSS;       // [C][kTS] T
+constexpr int kOffPT = kOffT + kC * kTS;          // [C][kTS] P T
+constexpr int kOffY = kOffPT + kC * kTS;          // [16][kTS] Y^T (state row, position)
+constexpr int kOffW = kOffY + kRows * kTS;        // [16][kTS] W^T
+constexpr int kOffG = kOffW + kRows * kTS;        // [C] g_t
+constexpr int kOffGC = kOffG + kC;                // [C] G[n-1][t] (follows g_t, as in the record)
+constexpr int kOffAv = kOffGC + kC;               // [C] a_t
 constexpr int kOffBv = kOffAv + kC;               // [C] b_t
-constexpr int kTS = 20;                           // LDS row stride of the diagonal-block inverses
-constexpr int kOffTb = kOffBv + kC;               // [4][16][kTS] (I + A_bb)^-1 of the 16 x 16 diagonal blocks
-constexpr int kOffRb = kOffTb + 4 * 16 * kTS;     // [16][16] right-hand side of one block
-constexpr int kLdsFloats = kOffRb + 16 * kRows;
+constexpr int kLdsFloats = kOffBv + kC;
 constexpr size_t kLdsBytes = static_cast<size_t>(kLdsFloats) * sizeof(float);
+
+// Pre-pass LDS layout: k and q staged first; A, P, T and T^T take their
+// place once the Gram products are in registers.
+constexpr int kPOffK = 0;
+constexpr int kPOffQ = kC * kKS;
+constexpr int kPOffA = 0;
+constexpr int kPOffP = kC * kTS;
+constexpr int kPOffT = 2 * kC * kTS;
+constexpr int kPOffTt = 3 * kC * kTS;
+constexpr int kPOffAv = (2 * kC * kKS > 4 * kC * kTS) ? 2 * kC * kKS : 4 * kC * kTS;
+constexpr int kPOffBv = kPOffAv + kC;
+constexpr int kPOffG = kPOffBv + kC;
+constexpr int kPOffGC = kPOffG + kC;
+constexpr int kPLdsFloats = kPOffGC + kC;
+constexpr size_t kPLdsBytes = static_cast<size_t>(kPLdsFloats) * sizeof(float);
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -91,6 +111,7 @@ struct ChunkArgs {
   float* state;
   float* ckpt;
   void* out;       // float or bf16 (OUTBF)
+  int32_t n_req;
   int32_t n_pos;
   int32_t n_kheads;
   int32_t n_vheads;
@@ -98,10 +119,6 @@ struct ChunkArgs {
   float q_scale;
 };
 
-// K K^T and Q K^T of the chunk into A and P (64 x 64 each). bf16 inputs:
-// 32 x 32 tiles on the matrix cores, operands read from the bf16 inputs
-// (exact products, f32 accumulation); each wave computes one tile of each.
-// f32 inputs: vector FMA from the staged rows.
 // Eight staged f32 values that are bf16-exact, packed back into bf16 pairs
 // (the upper halves of their bit patterns).
 __device__ __forceinline__ bf16x8 pack_bf16(const float* p) {
@@ -115,16 +132,19 @@ __device__ __forceinline__ bf16x8 pack_bf16(const float* p) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// K K^T and Q K^T of the staged chunk into A and P (64 x 64 each; q is
-// staged unscaled). bf16 inputs: 32 x 32 tiles on the matrix cores, operands
-// packed back to bf16 from the staged rows (exact), f32 accumulation; each
-// wave computes one tile of each. f32 inputs: vector FMA.
+// K K^T and Q K^T of the staged chunk (q unscaled), computed into registers
+// and then written over the staging area as A and P (64 x 64 each, row
+// stride kTS); the block barrier between the two keeps every read of k and
+// q ahead of the writes. bf16 inputs: 32 x 32 tiles on the matrix cores,
+// operands packed back to bf16 from the staged rows (exact), f32
+// accumulation, one tile of each per wave. f32 inputs: vector FMA, 2 x 8
+// outputs of each per thread.
 template <typename TIn>
 __device__ __forceinline__ void gram(float* lds) {
-  float* const A = lds + kOffA;
-  float* const P = lds + kOffP;
-  const float* const K = lds + kOffK;
-  const float* const Q = lds + kOffQ;
+  const float* const K = lds + kPOffK;
+  const float* const Q = lds + kPOffQ;
+  float* const A = lds + kPOffA;
+  float* const P = lds + kPOffP;
   const int tid = threadIdx.x;
   if constexpr (sizeof(TIn) == 2) {
     const int wave = tid >> 6;
@@ -140,42 +160,42 @@ __device__ __forceinline__ void gram(float* lds) {
       acc_k = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack_bf16(K + ra * kKS + kk + ko), b8, acc_k, 0, 0, 0);
       acc_q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack_bf16(Q + ra * kKS + kk + ko), b8, acc_q, 0, 0, 0);
     }
+    __syncthreads();
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 32 * ti + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      A[row * kAS + 32 * tj + (lane & 31)] = acc_k[r];
-      P[row * kAS + 32 * tj + (lane & 31)] = acc_q[r];
+      A[row * kTS + 32 * tj + (lane & 31)] = acc_k[r];
+      P[row * kTS + 32 * tj + (lane & 31)] = acc_q[r];
     }
   } else {
-    // 2 x 8 register tiles.
-    for (int tile = tid; tile < (kC / 2) * (kC / 8); tile += kThreads) {
-      const int t0 = (tile / (kC / 8)) * 2;
-      const int j0 = (tile % (kC / 8)) * 8;
-      float ak[2][8] = {}, aq[2][8] = {};
-      for (int c = 0; c < kDK; c += 4) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(K + t0 * kKS + c);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(K + (t0 + 1) * kKS + c);
-        const f32x4 z0 = *reinterpret_cast<const f32x4*>(Q + t0 * kKS + c);
-        const f32x4 z1 = *reinterpret_cast<const f32x4*>(Q + (t0 + 1) * kKS + c);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const f32x4 y = *reinterpret_cast<const f32x4*>(K + (j0 + j) * kKS + c);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            ak[0][j] = __builtin_fmaf(x0[u], y[u], ak[0][j]);
-            ak[1][j] = __builtin_fmaf(x1[u], y[u], ak[1][j]);
-            aq[0][j] = __builtin_fmaf(z0[u], y[u], aq[0][j]);
-            aq[1][j] = __builtin_fmaf(z1[u], y[u], aq[1][j]);
-          }
-        }
-      }
+    static_assert((kC / 2) * (kC / 8) == kThreads, "one 2 x 8 tile per thread");
+    const int t0 = (tid / (kC / 8)) * 2;
+    const int j0 = (tid % (kC / 8)) * 8;
+    float ak[2][8] = {}, aq[2][8] = {};
+    for (int c = 0; c < kDK; c += 4) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(K + t0 * kKS + c);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(K + (t0 + 1) * kKS + c);
+      const f32x4 z0 = *reinterpret_cast<const f32x4*>(Q + t0 * kKS + c);
+      const f32x4 z1 = *reinterpret_cast<const f32x4*>(Q + (t0 + 1) * kKS + c);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        A[t0 * kAS + j0 + j] = ak[0][j];
-        A[(t0 + 1) * kAS + j0 + j] = ak[1][j];
-        P[t0 * kAS + j0 + j] = aq[0][j];
-        P[(t0 + 1) * kAS + j0 + j] = aq[1][j];
+        const f32x4 y = *reinterpret_cast<const f32x4*>(K + (j0 + j) * kKS + c);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          ak[0][j] = __builtin_fmaf(x0[u], y[u], ak[0][j]);
+          ak[1][j] = __builtin_fmaf(x1[u], y[u], ak[1][j]);
+          aq[0][j] = __builtin_fmaf(z0[u], y[u], aq[0][j]);
+          aq[1][j] = __builtin_fmaf(z1[u], y[u], aq[1][j]);
+        }
       }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      A[t0 * kTS + j0 + j] = ak[0][j];
+      A[(t0 + 1) * kTS + j0 + j] = ak[1][j];
+      P[t0 * kTS + j0 + j] = aq[0][j];
+      P[(t0 + 1) * kTS + j0 + j] = aq[1][j];
     }
   }
 }
@@ -206,14 +226,26 @@ template <> struct Raw8<float> {
 
 constexpr int kKQItems = kC * (kDK / 8) / kThreads;   // k (and q) 8-element items per thread (4)
 
+// The gates are kept as loaded (bf16 bits or f32) and widened when staged:
+// widening at the load would wait for it there, and with it for every load
+// issued before it (the memory counter drains in order).
 template <typename TIn>
 struct ChunkRegs {
   Raw8<TIn> k[kKQItems], q[kKQItems], v;
-  float a, b;
+  TIn a, b;
 };
 
-// Issue the loads of the chunk starting at c0 (n positions) into registers.
-template <typename TIn, bool LOGG>
+template <typename TIn> __device__ __forceinline__ TIn gate_one();
+template <> __device__ __forceinline__ float gate_one<float>() { return 1.0f; }
+template <> __device__ __forceinline__ uint16_t gate_one<uint16_t>() { return 0x3F80; }   // bf16 1.0
+template <typename TIn> __device__ __forceinline__ float gate_widen(TIn x);
+template <> __device__ __forceinline__ float gate_widen<float>(float x) { return x; }
+template <> __device__ __forceinline__ float gate_widen<uint16_t>(uint16_t x) { return bf16_one(x); }
+
+// Issue the loads of the chunk starting at c0 (n positions) into registers:
+// k and q of key head g, the gates of value head h, and with WITHV the 16 v
+// rows from row0 of value head h.
+template <typename TIn, bool WITHV>
 __device__ __forceinline__ void fetch_chunk(const ChunkArgs& args, ChunkRegs<TIn>& rg, int r, int h, int g, int row0,
                                             int c0, int n) {
   const int T = args.n_pos;
@@ -235,7 +267,7 @@ __device__ __forceinline__ void fetch_chunk(const ChunkArgs& args, ChunkRegs<TIn
       rg.q[i].zero();
     }
   }
-  {
+  if constexpr (WITHV) {
     const int t = tid / (kRows / 8);
     const int i0 = (tid % (kRows / 8)) * 8;
     if (tid < kC * (kRows / 8) && t < n)
@@ -243,18 +275,19 @@ __device__ __forceinline__ void fetch_chunk(const ChunkArgs& args, ChunkRegs<TIn
     else
       rg.v.zero();
   }
-  rg.a = 1.0f;
-  rg.b = 0.0f;
+  rg.a = gate_one<TIn>();
+  rg.b = TIn(0);
   if (tid < n) {
     const size_t src = (static_cast<size_t>(r) * T + c0 + tid) * args.n_vheads + h;
-    rg.a = load_elem<TIn>(static_cast<const TIn*>(args.a), src);   // the log decay with log gates
-    rg.b = load_elem<TIn>(static_cast<const TIn*>(args.b), src);
+    rg.a = static_cast<const TIn*>(args.a)[src];   // the log decay with log gates
+    rg.b = static_cast<const TIn*>(args.b)[src];
   }
 }
 
-// Write a fetched chunk into the staging buffers (f32; q unscaled).
-template <typename TIn, bool LOGG>
-__device__ __forceinline__ void stage_chunk(float* lds, const ChunkRegs<TIn>& rg, int n) {
+// Write a fetched chunk into LDS as f32: k and q (unscaled) at kOffK/kOffQ,
+// with WITHV the v rows at kOffV, and a_t, b_t at av/bv.
+template <typename TIn, bool LOGG, bool WITHV>
+__device__ __forceinline__ void stage_chunk(float* lds, const ChunkRegs<TIn>& rg, int n, float* av, float* bv) {
   const int tid = threadIdx.x;
   float* const Kl = lds + kOffK;
   float* const Ql = lds + kOffQ;
@@ -271,17 +304,20 @@ __device__ __forceinline__ void stage_chunk(float* lds, const ChunkRegs<TIn>& rg
     *reinterpret_cast<f32x4*>(Ql + t * kKS + j) = f32x4{x[0], x[1], x[2], x[3]};
     *reinterpret_cast<f32x4*>(Ql + t * kKS + j + 4) = f32x4{x[4], x[5], x[6], x[7]};
   }
-  if (tid < kC * (kRows / 8)) {
-    float x[8];
-    rg.v.widen(x);
-    float* const lv = lds + kOffV + (tid / (kRows / 8)) * kRows + (tid % (kRows / 8)) * 8;
-    *reinterpret_cast<f32x4*>(lv) = f32x4{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<f32x4*>(lv + 4) = f32x4{x[4], x[5], x[6], x[7]};
+  if constexpr (WITHV) {
+    if (tid < kC * (kRows / 8)) {
+      float x[8];
+      rg.v.widen(x);
+      float* const lv = lds + kOffV + (tid / (kRows / 8)) * kRows + (tid % (kRows / 8)) * 8;
+      *reinterpret_cast<f32x4*>(lv) = f32x4{x[0], x[1], x[2], x[3]};
+      *reinterpret_cast<f32x4*>(lv + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    }
   }
   if (tid < kC) {
     // Log-space gates: a_t = exp(g_t) (positions past the span end keep a = 1).
-    lds[kOffAv + tid] = (LOGG && tid < n) ? expf(rg.a) : rg.a;
-    lds[kOffBv + tid] = rg.b;
+    const float a = gate_widen<TIn>(rg.a);
+    av[tid] = (LOGG && tid < n) ? expf(a) : a;
+    bv[tid] = gate_widen<TIn>(rg.b);
   }
 }
 
@@ -292,80 +328,341 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// LOGG: `a` holds log decays; OUTBF: outputs are written as bf16.
-template <typename TIn, bool CAPTURE, bool LOGG, bool OUTBF>
-__global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs args) {
+// Pre-pass: one block per (request, value head, chunk) of the segment that
+// starts at chunk chunk0 and holds n_seg chunks; record
+// ((r * Hv + h) * n_seg + chunk - chunk0) of ws.
+template <typename TIn, bool LOGG>
+__global__ __launch_bounds__(kThreads) void gdn_chunk_prep_kernel(const ChunkArgs args, float* ws, int chunk0,
+                                                                  int n_seg) {
   extern __shared__ float lds[];
   const int T = args.n_pos;
   const int Hv = args.n_vheads;
-  const int nrb = kDK / kRows;
-  const int W = blockIdx.x;
-  const int row0 = (W % nrb) * kRows;
-  const int h = (W / nrb) % Hv;
-  const int r = W / (nrb * Hv);
+  const int cl = blockIdx.x % n_seg;
+  const int h = (blockIdx.x / n_seg) % Hv;
+  const int r = blockIdx.x / (n_seg * Hv);
+  const int c0 = (chunk0 + cl) * kC;
+  const int n = min(kC, T - c0);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  float* const A = lds + kPOffA;
+  float* const P = lds + kPOffP;
+  float* const Tl = lds + kPOffT;
+  float* const Tt = lds + kPOffTt;
+  float* const Av = lds + kPOffAv;
+  float* const Bv = lds + kPOffBv;
+  float* const Gv = lds + kPOffG;
+  float* const GC = lds + kPOffGC;
+  float* const rec = ws + (static_cast<size_t>(r) * Hv + h) * n_seg * kRecFloats +
+                     static_cast<size_t>(cl) * kRecFloats;
+  const float p_scale = args.q_scale;
+
+  {
+    ChunkRegs<TIn> rg;
+    fetch_chunk<TIn, false>(args, rg, r, h, h / args.group, 0, c0, n);
+    stage_chunk<TIn, LOGG, false>(lds, rg, n, Av, Bv);
+  }
+  __syncthreads();
+  gram<TIn>(lds);
+  __syncthreads();
+  // Row t: A[t][j] = b_t G[t][j] (K K^T)[t][j] for j < t (0 elsewhere),
+  // P[t][j] = q_scale G[t][j] (q_t . k_j) for j <= t (0 elsewhere), and g_t,
+  // where G[t][j] = a_{j+1} ... a_t (1 for j >= t). Four lanes share a row,
+  // each 16 columns [16 s, 16 s + 16): a lane multiplies the decays of its
+  // own segment into running products from the segment's top down (no
+  // division, no logarithm: zero and tiny decays are exact), and the product
+  // of the decays above its segment comes from the other three lanes.
+  {
+    const int t = tid >> 2;
+    const int sg = tid & 3;
+    const int j0 = 16 * sg;
+    float av[16];   // a_{j0} .. a_{j0 + 15}
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(Av + j0 + j);
+      av[j] = x.x; av[j + 1] = x.y; av[j + 2] = x.z; av[j + 3] = x.w;
+    }
+    float own = 1.0f;   // this segment's decays with index <= t
+#pragma unroll
+    for (int i = 15; i >= 0; --i) own *= (j0 + i <= t) ? av[i] : 1.0f;
+    const int base = tid & ~3;
+    float above = 1.0f;   // the segments above, highest first
+#pragma unroll
+    for (int k = 3; k >= 1; --k) {
+      const float o = __shfl(own, base + k);
+      if (k > sg) above *= o;
+    }
+    const float bt = Bv[t];
+    float* const arow = A + t * kTS;
+    float* const prow = P + t * kTS;
+    const bool last = t == n - 1;   // this row's products are the decays to the chunk end
+    float gp = above;               // G[t][j] for the current j
+#pragma unroll
+    for (int j = 12; j >= 0; j -= 4) {
+      const f32x4 kv = *reinterpret_cast<const f32x4*>(arow + j0 + j);
+      const f32x4 qv = *reinterpret_cast<const f32x4*>(prow + j0 + j);
+      f32x4 ka, qa, gc;
+#pragma unroll
+      for (int u = 3; u >= 0; --u) {
+        const int jj = j0 + j + u;   // column
+        if (j + u < 15) gp *= (jj < t) ? av[j + u + 1] : 1.0f;
+        ka[u] = (jj < t) ? bt * gp * kv[u] : 0.0f;
+        qa[u] = (jj <= t) ? (p_scale * gp) * qv[u] : 0.0f;
+        gc[u] = gp;
+      }
+      *reinterpret_cast<f32x4*>(arow + j0 + j) = ka;
+      *reinterpret_cast<f32x4*>(prow + j0 + j) = qa;
+      if (last) *reinterpret_cast<f32x4*>(GC + j0 + j) = gc;
+    }
+    if (sg == 0) Gv[t] = av[0] * gp;   // g_t = a_0 G[t][0]
+  }
+  __syncthreads();
+  // T = (I + A)^-1 by blocks of 16: T_ii = (I + A_ii)^-1 for the four
+  // diagonal blocks (wave i, forward substitution, column j = lane / 4 by the
+  // four lanes of a quad: lane s sums the terms k in [4 s, 4 s + 4) and keeps
+  // T[k][j] for those k, DPP joins the partial sums), then the blocks below
+  // the diagonal level by level, T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, on
+  // the matrix cores. Entries of A on and above the diagonal are 0. T is
+  // kept row-major and transposed (T^T rows are the columns the products
+  // read as 16-byte loads).
+  {
+    const int col = lane >> 2;
+    const int sub = lane & 3;
+    const int d0 = 16 * wave;
+    float xs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = 0.0f;
+      if (i > 0) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(A + (d0 + i) * kTS + d0 + 4 * sub);
+        p = __builtin_fmaf(a4.x, xs[0], __builtin_fmaf(a4.y, xs[1], __builtin_fmaf(a4.z, xs[2], a4.w * xs[3])));
+      }
+      const float x = ((i == col) ? 1.0f : 0.0f) - group_sum<4>(p);
+      if (sub == (i >> 2)) xs[i & 3] = x;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Tl[(d0 + 4 * sub + m) * kTS + d0 + col] = xs[m];
+    *reinterpret_cast<f32x4*>(Tt + (d0 + col) * kTS + d0 + 4 * sub) = f32x4{xs[0], xs[1], xs[2], xs[3]};
+    // Blocks above the diagonal are 0 (never read; written so the record is defined).
+    for (int e = tid; e < kC * kC; e += kThreads) {
+      const int rr = e >> 6, cc = e & 63;
+      if ((cc >> 4) > (rr >> 4)) Tl[rr * kTS + cc] = 0.0f;
+    }
+  }
+  __syncthreads();
+  {
+    const int ii = lane & 15;
+    const int kq = lane >> 4;
+    for (int lev = 1; lev < 4; ++lev) {
+      if (wave < 4 - lev) {
+        const int bi = wave + lev, bj = wave;
+        f32x4 m = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int bk = bj; bk < bi; ++bk) {
+          const f32x4 av = *reinterpret_cast<const f32x4*>(A + (16 * bi + ii) * kTS + 16 * bk + 4 * kq);
+          const f32x4 tv = *reinterpret_cast<const f32x4*>(Tt + (16 * bj + ii) * kTS + 16 * bk + 4 * kq);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) m = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], tv[u], m, 0, 0, 0);
+        }
+        // The product's lanes hold M[4 kq + u][ii], the B operand of the
+        // next product in the same lane order.
+        const f32x4 td = *reinterpret_cast<const f32x4*>(Tl + (16 * bi + ii) * kTS + 16 * bi + 4 * kq);
+        f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o = __builtin_amdgcn_mfma_f32_16x16x4f32(td[u], m[u], o, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Tl[(16 * bi + 4 * kq + u) * kTS + 16 * bj + ii] = -o[u];
+        *reinterpret_cast<f32x4*>(Tt + (16 * bj + ii) * kTS + 16 * bi + 4 * kq) = f32x4{-o.x, -o.y, -o.z, -o.w};
+      }
+      __syncthreads();
+    }
+  }
+  // The record: T, g and G[n-1][.] copied out, P T on the matrix cores
+  // (16x16x4 f32 MFMA, 16 x 16 tiles; P T is lower triangular like both
+  // factors, so tile (i, j) sums over the blocks k in [j, i]: 20 block
+  // products, 5 per wave; tiles right of the diagonal are 0).
+  {
+    const int t = tid >> 2;
+    const int col = (tid & 3) * 16;
+#pragma unroll
+    for (int m = 0; m < 16; m += 4)
+      *reinterpret_cast<f32x4*>(rec + kRecT + t * kC + col + m) =
+          *reinterpret_cast<const f32x4*>(Tl + t * kTS + col + m);
+    if (tid < 2 * kC / 4)
+      *reinterpret_cast<f32x4*>(rec + kRecG + 4 * tid) = *reinterpret_cast<const f32x4*>(Gv + 4 * tid);
+  }
+  {
+    // Tiles per wave, (i, j) packed as 4 i + j; 16 ends a list. The first
+    // list is computed, the second written as zeros.
+    constexpr uint8_t kTiles[4][4] = {{12, 0, 16, 16}, {8, 4, 16, 16}, {13, 9, 16, 16}, {14, 5, 10, 15}};
+    constexpr uint8_t kZeros[4][2] = {{1, 2}, {3, 6}, {7, 16}, {11, 16}};
+    const int i = lane & 15;
+    const int kq = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tile = kTiles[wave][e];
+      if (tile == 16) break;
+      const int ti = tile >> 2, tj = tile & 3;
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int c = 16 * tj; c < 16 * ti + 16; c += 16) {
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(P + (16 * ti + i) * kTS + c + 4 * kq);
+        const f32x4 tv = *reinterpret_cast<const f32x4*>(Tt + (16 * tj + i) * kTS + c + 4 * kq);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[u], tv[u], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rec[kRecPT + (16 * ti + 4 * kq + u) * kC + 16 * tj + i] = acc[u];
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int tile = kZeros[wave][e];
+      if (tile == 16) break;
+      const int ti = tile >> 2, tj = tile & 3;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rec[kRecPT + (16 * ti + 4 * kq + u) * kC + 16 * tj + i] = 0.0f;
+    }
+  }
+}
+
+// The pre-pass record of one chunk in registers (T and P T rows t = tid / 4,
+// columns [16 (tid % 4), + 16); g and G[n-1][.] in the first 32 threads).
+struct RecRegs {
+  f32x4 t[4], pt[4], g;
+};
+
+__device__ __forceinline__ void fetch_rec(const float* rec, RecRegs& rr) {
+  const int tid = threadIdx.x;
+  const int row = tid >> 2;
+  const int col = (tid & 3) * 16;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    rr.t[m] = *reinterpret_cast<const f32x4*>(rec + kRecT + row * kC + col + 4 * m);
+    rr.pt[m] = *reinterpret_cast<const f32x4*>(rec + kRecPT + row * kC + col + 4 * m);
+  }
+  if (tid < 2 * kC / 4) rr.g = *reinterpret_cast<const f32x4*>(rec + kRecG + 4 * tid);
+}
+
+__device__ __forceinline__ void stage_rec(float* lds, const RecRegs& rr) {
+  const int tid = threadIdx.x;
+  const int row = tid >> 2;
+  const int col = (tid & 3) * 16;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    *reinterpret_cast<f32x4*>(lds + kOffT + row * kTS + col + 4 * m) = rr.t[m];
+    *reinterpret_cast<f32x4*>(lds + kOffPT + row * kTS + col + 4 * m) = rr.pt[m];
+  }
+  if (tid < 2 * kC / 4) *reinterpret_cast<f32x4*>(lds + kOffG + 4 * tid) = rr.g;
+}
+
+// Sequential pass over the segment's chunks. init: the state the segment
+// starts from, request r's rows at init + r * init_rstride (the state
+// buffer, or with capture the checkpoint before the segment). LOGG: `a`
+// holds log decays; OUTBF: outputs are written as bf16.
+template <typename TIn, bool CAPTURE, bool LOGG, bool OUTBF>
+__global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs args, const float* ws, int chunk0,
+                                                               int n_seg, const float* init, size_t init_rstride) {
+  extern __shared__ float lds[];
+  const int T = args.n_pos;
+  const int Hv = args.n_vheads;
+  const int n_heads = args.n_req * Hv;
+  // Block order: head-major with the 8 row blocks of a head on one XCD when
+  // the head count allows it (block b runs on XCD b % 8).
+  int hh, rb;
+  if ((n_heads & 7) == 0) {
+    const int x = blockIdx.x & 7;
+    const int sl = blockIdx.x >> 3;
+    hh = x + 8 * (sl >> 3);
+    rb = sl & 7;
+  } else {
+    hh = blockIdx.x / kRowBlocks;
+    rb = blockIdx.x % kRowBlocks;
+  }
+  const int row0 = rb * kRows;
+  const int h = hh % Hv;
+  const int r = hh / Hv;
   const int g = h / args.group;
   const int tid = threadIdx.x;
+  const int wave = tid >> 6;
   const int lane = tid & 63;
   const int li = lane % kLPR;
-  const int row_blk = (tid >> 6) * (64 / kLPR) + lane / kLPR;   // 0..15
+  const int kq = lane >> 4;
+  const int srow = lane & 15;
+  const int row_blk = wave * (64 / kLPR) + lane / kLPR;   // 0..15
   const size_t head_elems = static_cast<size_t>(kDK) * kDK;
   const size_t pos_stride = static_cast<size_t>(Hv) * head_elems;
   float* const Kl = lds + kOffK;
   float* const Ql = lds + kOffQ;
   float* const Vl = lds + kOffV;
   float* const S0 = lds + kOffS0;
-  float* const A = lds + kOffA;
-  float* const P = lds + kOffP;
-  float* const X = lds + kOffX;
-  float* const QS = lds + kOffQS;
-  float* const GC = lds + kOffGC;
-  float* const Tb = lds + kOffTb;
-  float* const Rb = lds + kOffRb;
+  float* const Tl = lds + kOffT;
+  float* const PTl = lds + kOffPT;
+  float* const Yt = lds + kOffY;
+  float* const Wt = lds + kOffW;
   float* const Gv = lds + kOffG;
+  float* const GC = lds + kOffGC;
   float* const Av = lds + kOffAv;
   float* const Bv = lds + kOffBv;
-  // q is staged unscaled; q_scale enters P and QS.
-  const float p_scale = args.q_scale;
+  const float* const rec0 = ws + (static_cast<size_t>(r) * Hv + h) * n_seg * kRecFloats;
 
-  float* const state_row = args.state + (static_cast<size_t>(r) * Hv + h) * head_elems +
-                           static_cast<size_t>(row0 + row_blk) * kDK;
-  float* const ckpt_row0 = CAPTURE ? args.ckpt + static_cast<size_t>(r) * T * pos_stride +
-                                         static_cast<size_t>(h) * head_elems +
-                                         static_cast<size_t>(row0 + row_blk) * kDK
-                                   : nullptr;
+  const size_t row_off = static_cast<size_t>(h) * head_elems + static_cast<size_t>(row0 + row_blk) * kDK;
+  const float* const init_row = init + r * init_rstride + row_off;
+  float* const state_row = args.state + static_cast<size_t>(r) * pos_stride + row_off;
+  float* const ckpt_row0 = CAPTURE ? args.ckpt + static_cast<size_t>(r) * T * pos_stride + row_off : nullptr;
   const size_t out_h = (static_cast<size_t>(r) * T * Hv + h) * kDK + row0;   // element offset
 
   f32x4 s[kNCH];
 #pragma unroll
-  for (int m = 0; m < kNCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(state_row + 4 * (li + kLPR * m));
+  for (int m = 0; m < kNCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(init_row + 4 * (li + kLPR * m));
+
+  // A chunk's outputs wait in registers until the next chunk is staged:
+  // stored right away they would sit in the memory counter in front of the
+  // next chunk's prefetched loads, and staging would wait for them too.
+  f32x4 o_pend = {0.0f, 0.0f, 0.0f, 0.0f};
+  size_t o_elem = 0;   // element of the first pending output
+  int o_cnt = 0;       // pending outputs (positions of this lane still in the span)
+  auto store_pending = [&]() {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u < o_cnt) {
+        const size_t e = o_elem + static_cast<size_t>(u) * Hv * kDK;
+        if constexpr (OUTBF)
+          static_cast<uint16_t*>(args.out)[e] = static_cast<uint16_t>(bf16_rne(o_pend[u]));
+        else
+          static_cast<float*>(args.out)[e] = o_pend[u];
+      }
+    }
+  };
 
   ChunkRegs<TIn> rg;
-  fetch_chunk<TIn, LOGG>(args, rg, r, h, g, row0, 0, min(kC, T));
-  for (int c0 = 0; c0 < T; c0 += kC) {
+  RecRegs rr;
+  fetch_chunk<TIn, true>(args, rg, r, h, g, row0, chunk0 * kC, min(kC, T - chunk0 * kC));
+  fetch_rec(rec0, rr);
+  for (int cl = 0; cl < n_seg; ++cl) {
+    const int c0 = (chunk0 + cl) * kC;
     const int n = min(kC, T - c0);
     __syncthreads();   // the previous chunk's LDS reads are done
-    // 1. Stage the fetched chunk (k, q unscaled, the block's v rows, gates)
-    //    and the current state rows, then fetch the next chunk: its loads
-    //    complete while this one is processed.
-    stage_chunk<TIn, LOGG>(lds, rg, n);
+    // 1. Stage the fetched chunk and its record and the current state rows,
+    //    then fetch the next chunk: its loads complete while this one is
+    //    processed.
+    stage_chunk<TIn, LOGG, true>(lds, rg, n, Av, Bv);
+    stage_rec(lds, rr);
 #pragma unroll
     for (int m = 0; m < kNCH; ++m) *reinterpret_cast<f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m)) = s[m];
-    if (c0 + kC < T) fetch_chunk<TIn, LOGG>(args, rg, r, h, g, row0, c0 + kC, min(kC, T - c0 - kC));
+    if (cl + 1 < n_seg) {
+      fetch_chunk<TIn, true>(args, rg, r, h, g, row0, c0 + kC, min(kC, T - c0 - kC));
+      fetch_rec(rec0 + static_cast<size_t>(cl + 1) * kRecFloats, rr);
+    }
     __syncthreads();
-    // 2. K K^T and Q K^T (matrix cores for bf16), X = K S_0^T and
-    //    QS = Q S_0^T.
-    gram<TIn>(lds);
+    store_pending();
+    // 2. X = K S_0^T and QS = Q S_0^T on the matrix cores (16x16x4 f32
+    //    MFMA, exact f32 products): wave w takes positions [16 w, 16 w + 16)
+    //    for all 16 state rows; in each step of 4 MFMAs over 16 columns, lane
+    //    group kq supplies columns [c + 4 kq, c + 4 kq + 4), so a lane reads
+    //    its operands as 16-byte LDS loads. Then Y = b (V - g X), stored
+    //    transposed, and q_scale g QS kept in the lanes that hold it.
+    const int tb = 16 * wave + 4 * kq;   // this lane's 4 positions of the wave's tile
+    f32x4 qsg;
     {
-      // X and QS on the matrix cores (16x16x4 f32 MFMA, exact f32 products):
-      // wave w takes positions [16 w, 16 w + 16) for all 16 state rows. In
-      // each step of 4 MFMAs over 16 columns, lane group kq = lane / 16
-      // supplies columns [c + 4 kq, c + 4 kq + 4), so a lane reads its
-      // operands as 16-byte LDS loads.
-      const int wave = tid >> 6;
-      const int lane = tid & 63;
-      const int row = 16 * wave + (lane & 15);    // position (A operand row)
-      const int srow = lane & 15;                  // state row (B operand column)
-      const int kq = lane >> 4;
+      const int row = 16 * wave + srow;
       f32x4 xk = {}, xq = {};
 #pragma unroll 2
       for (int c = 0; c < kDK; c += 16) {
@@ -378,179 +675,57 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
           xq = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[u], sv[u], xq, 0, 0, 0);
         }
       }
+      const f32x4 g4 = *reinterpret_cast<const f32x4*>(Gv + tb);
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(Bv + tb);
+      f32x4 y;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int t = 16 * wave + 4 * kq + u;
-        X[t * kRows + srow] = xk[u];
-        QS[t * kRows + srow] = xq[u];
+        y[u] = b4[u] * __builtin_fmaf(-g4[u], xk[u], Vl[(tb + u) * kRows + srow]);
+        qsg[u] = (g4[u] * args.q_scale) * xq[u];
       }
+      *reinterpret_cast<f32x4*>(Yt + srow * kTS + tb) = y;
     }
     __syncthreads();
-    // 3. Row t: A[t][j] = b_t G[t][j] (K K^T)[t][j] for j < t, P[t][j] =
-    //    G[t][j] (q_t . k_j) for j <= t, and g_t, where G[t][j] = a_{j+1}
-    //    ... a_t (1 for j >= t). Four lanes share a row, each 16 columns
-    //    [16 s, 16 s + 16): a lane multiplies the decays of its own segment
-    //    into running products from the segment's top down (no division, no
-    //    logarithm: zero and tiny decays are exact), and the product of the
-    //    decays above its segment comes from the other three lanes.
+    // 3. W = T Y and P T Y in one pass over Y (16x16x4 f32 MFMA; wave w
+    //    takes positions [16 w, 16 w + 16), T and P T are lower triangular so
+    //    columns past 16 w + 15 are skipped); outputs o = q_scale g QS + P T Y,
+    //    stored after the next chunk is staged.
     {
-      const int t = tid >> 2;
-      const int sg = tid & 3;
-      const int j0 = 16 * sg;
-      float av[16];   // a_{j0} .. a_{j0 + 15}
+      const int trow = 16 * wave + srow;
+      f32x4 wacc = {}, oacc = {};
+      for (int c = 0; c <= 16 * wave; c += 16) {
+        const f32x4 tv = *reinterpret_cast<const f32x4*>(Tl + trow * kTS + c + 4 * kq);
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(PTl + trow * kTS + c + 4 * kq);
+        const f32x4 yv = *reinterpret_cast<const f32x4*>(Yt + srow * kTS + c + 4 * kq);
 #pragma unroll
-      for (int j = 0; j < 16; j += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(Av + j0 + j);
-        av[j] = x.x; av[j + 1] = x.y; av[j + 2] = x.z; av[j + 3] = x.w;
-      }
-      // Product of this segment's decays with index <= t (the factor that
-      // every column of the segments below needs).
-      float own = 1.0f;
-#pragma unroll
-      for (int i = 15; i >= 0; --i) own *= (j0 + i <= t) ? av[i] : 1.0f;
-      // Product of the segments above (lanes sg + 1 .. 3 of this row),
-      // highest first.
-      const int base = tid & ~3;
-      float above = 1.0f;
-#pragma unroll
-      for (int k = 3; k >= 1; --k) {
-        const float o = __shfl(own, base + k);
-        if (k > sg) above *= o;
-      }
-      const float bt = Bv[t];
-      float* const arow = A + t * kAS;
-      float* const prow = P + t * kAS;
-      const bool last = t == n - 1;   // this row's products are the decays to the chunk end
-      float gp = above;               // G[t][j] for the current j
-#pragma unroll
-      for (int j = 12; j >= 0; j -= 4) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(arow + j0 + j);
-        const f32x4 qv = *reinterpret_cast<const f32x4*>(prow + j0 + j);
-        f32x4 ka, qa, gc;
-#pragma unroll
-        for (int u = 3; u >= 0; --u) {
-          const int jj = j0 + j + u;   // column
-          if (j + u < 15) gp *= (jj < t) ? av[j + u + 1] : 1.0f;
-          ka[u] = bt * gp * kv[u];
-          qa[u] = (p_scale * gp) * qv[u];
-          gc[u] = gp;
+        for (int u = 0; u < 4; ++u) {
+          wacc = __builtin_amdgcn_mfma_f32_16x16x4f32(tv[u], yv[u], wacc, 0, 0, 0);
+          oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[u], yv[u], oacc, 0, 0, 0);
         }
-        *reinterpret_cast<f32x4*>(arow + j0 + j) = ka;
-        *reinterpret_cast<f32x4*>(prow + j0 + j) = qa;
-        if (last) *reinterpret_cast<f32x4*>(GC + j0 + j) = gc;
       }
-      if (sg == 0) Gv[t] = av[0] * gp;   // g_t = a_0 G[t][0]
+      *reinterpret_cast<f32x4*>(Wt + srow * kTS + tb) = wacc;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o_pend[u] = qsg[u] + oacc[u];
+      o_elem = out_h + static_cast<size_t>(c0 + tb) * Hv * kDK + srow;
+      o_cnt = min(4, max(0, n - tb));
     }
     __syncthreads();
-    // 4. Y = b (V - g X) in place of X (waves 1-3) while wave 0 inverts the
-    //    four 16 x 16 diagonal blocks of I + A (one lane per column of one
-    //    block, forward substitution in registers); then (I + A) W = Y block
-    //    by block: R = Y_b - A_b,<b W_<b, W_b = (I + A_bb)^-1 R, W in place of Y.
-    if (tid < 64) {
-      const int bi = tid >> 4;
-      const int col = tid & 15;
-      const float* ab = A + (16 * bi) * kAS + 16 * bi;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float r[16];
-#pragma unroll
-        for (int j = 0; j < 16; j += 4) {
-          const f32x4 v4 = *reinterpret_cast<const f32x4*>(ab + i * kAS + j);
-          r[j] = v4.x; r[j + 1] = v4.y; r[j + 2] = v4.z; r[j + 3] = v4.w;
-        }
-        float acc0 = (i == col) ? 1.0f : 0.0f, acc1 = 0.0f;
-#pragma unroll
-        for (int j = 0; j < i; ++j) {
-          if (j & 1) acc1 = __builtin_fmaf(-r[j], x[j], acc1);
-          else acc0 = __builtin_fmaf(-r[j], x[j], acc0);
-        }
-        x[i] = acc0 + acc1;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) Tb[(bi * 16 + i) * kTS + col] = x[i];
-    } else {
-      for (int e = tid - 64; e < kC * kRows; e += kThreads - 64) {
-        const int t = e / kRows;
-        X[e] = Bv[t] * __builtin_fmaf(-Gv[t], X[e], Vl[e]);
-      }
-    }
-    __syncthreads();
-    for (int blk = 0; blk < kC / 16; ++blk) {
-      const int i = tid >> 4;          // row inside the block
-      const int col = tid & 15;
-      const int t = 16 * blk + i;
-      {
-        float acc0 = X[t * kRows + col], acc1 = 0.0f;
-        for (int j = 0; j < 16 * blk; j += 4) {
-          const f32x4 av4 = *reinterpret_cast<const f32x4*>(A + t * kAS + j);
-          acc0 = __builtin_fmaf(-av4.x, X[j * kRows + col], acc0);
-          acc1 = __builtin_fmaf(-av4.y, X[(j + 1) * kRows + col], acc1);
-          acc0 = __builtin_fmaf(-av4.z, X[(j + 2) * kRows + col], acc0);
-          acc1 = __builtin_fmaf(-av4.w, X[(j + 3) * kRows + col], acc1);
-        }
-        Rb[i * kRows + col] = acc0 + acc1;
-      }
-      __syncthreads();
-      {
-        const float* trow = Tb + (blk * 16 + i) * kTS;
-        float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; j += 4) {
-          const f32x4 t4 = *reinterpret_cast<const f32x4*>(trow + j);
-          acc0 = __builtin_fmaf(t4.x, Rb[j * kRows + col], acc0);
-          acc1 = __builtin_fmaf(t4.y, Rb[(j + 1) * kRows + col], acc1);
-          acc0 = __builtin_fmaf(t4.z, Rb[(j + 2) * kRows + col], acc0);
-          acc1 = __builtin_fmaf(t4.w, Rb[(j + 3) * kRows + col], acc1);
-        }
-        X[t * kRows + col] = acc0 + acc1;
-      }
-      __syncthreads();
-    }
-    // 5. Outputs: o_t = g_t (q_t . S_0 rows) + sum_{j <= t} P[t][j] w_j; a
-    //    thread takes 4 state rows of one position.
-    {
-      const int t = tid >> 2;
-      const int c4 = (tid & 3) * 4;
-      if (t < n) {
-        const f32x4 qs = *reinterpret_cast<const f32x4*>(QS + t * kRows + c4);
-        const float gt = Gv[t] * args.q_scale;
-        f32x4 acc = {gt * qs.x, gt * qs.y, gt * qs.z, gt * qs.w};
-        for (int j = 0; j <= t; j += 4) {
-          const f32x4 p4 = *reinterpret_cast<const f32x4*>(P + t * kAS + j);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            // Entries past the diagonal (j + u > t) are skipped; the block's
-            // positions past the span end have w = 0 (b = 0).
-            const float pv = (j + u <= t) ? p4[u] : 0.0f;
-            const f32x4 w4 = *reinterpret_cast<const f32x4*>(X + (j + u) * kRows + c4);
-            acc.x = __builtin_fmaf(pv, w4.x, acc.x);
-            acc.y = __builtin_fmaf(pv, w4.y, acc.y);
-            acc.z = __builtin_fmaf(pv, w4.z, acc.z);
-            acc.w = __builtin_fmaf(pv, w4.w, acc.w);
-          }
-        }
-        const size_t o = out_h + static_cast<size_t>(c0 + t) * Hv * kDK + c4;
-        if constexpr (OUTBF) {
-          u32x2 w;
-          w.x = bf16_rne(acc.x) | (bf16_rne(acc.y) << 16);
-          w.y = bf16_rne(acc.z) | (bf16_rne(acc.w) << 16);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(args.out) + o) = w;
-        } else {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(args.out) + o) = acc;
-        }
-      }
-    }
     if constexpr (CAPTURE) {
-      // 6. States: S_t = a_t S_{t-1} + w_t k_t^T, each checkpointed; 8
+      // 4. States: S_t = a_t S_{t-1} + w_t k_t^T, each checkpointed; 8
       //    positions at a time so their LDS reads are issued together.
       for (int t0 = 0; t0 < n; t0 += 8) {
         float at[8], wt[8];
         f32x4 kk[8][kNCH];
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(Wt + row_blk * kTS + t0);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(Wt + row_blk * kTS + t0 + 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          wt[u] = w0[u];
+          wt[u + 4] = w1[u];
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           at[u] = Av[t0 + u];
-          wt[u] = X[(t0 + u) * kRows + row_blk];
 #pragma unroll
           for (int m = 0; m < kNCH; ++m)
             kk[u][m] = *reinterpret_cast<const f32x4*>(Kl + (t0 + u) * kKS + 4 * (li + kLPR * m));
@@ -574,31 +749,38 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
         }
       }
     } else {
-      // 6. State at the chunk end only: S_C = g_{n-1} S_0 + sum_t G[n-1][t]
+      // 4. State at the chunk end only: S_C = g_{n-1} S_0 + sum_t G[n-1][t]
       //    w_t k_t^T on the matrix cores (16x16x4 f32 MFMA; wave w takes
-      //    columns [32 w, 32 w + 32)), written over S_0 and read back into
-      //    the lanes' registers.
-      const int wave = tid >> 6;
-      const int lane = tid & 63;
-      const int i = lane & 15;
-      const int kq = lane >> 4;
-      f32x4 d0 = {}, d1 = {};
+      //    columns [32 w, 32 w + 32)), every operand read before the first
+      //    product; written over S_0 and read back into the lanes' registers.
+      f32x4 wv[4];
+      float k0[4][4], k1[4][4];
 #pragma unroll
-      for (int tb = 0; tb < kC; tb += 16) {
-        const int tq = tb + 4 * kq;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int tq = 16 * q4 + 4 * kq;
         const f32x4 gc = *reinterpret_cast<const f32x4*>(GC + tq);
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(Wt + srow * kTS + tq);
+        wv[q4] = f32x4{gc.x * w4.x, gc.y * w4.y, gc.z * w4.z, gc.w * w4.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float wv = gc[u] * X[(tq + u) * kRows + i];
-          const float* krow = Kl + (tq + u) * kKS + 32 * wave + (lane & 15);
-          d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv, krow[0], d0, 0, 0, 0);
-          d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv, krow[16], d1, 0, 0, 0);
+          const float* krow = Kl + (tq + u) * kKS + 32 * wave + srow;
+          k0[q4][u] = krow[0];
+          k1[q4][u] = krow[16];
+        }
+      }
+      f32x4 d0 = {}, d1 = {};
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[q4][u], k0[q4][u], d0, 0, 0, 0);
+          d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[q4][u], k1[q4][u], d1, 0, 0, 0);
         }
       }
       const float gn = Gv[n - 1];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        float* e0 = S0 + (4 * kq + u) * kSS + 32 * wave + (lane & 15);
+        float* e0 = S0 + (4 * kq + u) * kSS + 32 * wave + srow;
         e0[0] = __builtin_fmaf(gn, e0[0], d0[u]);
         e0[16] = __builtin_fmaf(gn, e0[16], d1[u]);
       }
@@ -607,6 +789,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
       for (int m = 0; m < kNCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m));
     }
   }
+  store_pending();
   if (!CAPTURE) {
 #pragma unroll
     for (int m = 0; m < kNCH; ++m) *reinterpret_cast<f32x4*>(state_row + 4 * (li + kLPR * m)) = s[m];
@@ -614,24 +797,58 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
 }
 
 template <typename TIn, bool CAPTURE, bool LOGG>
-hipError_t launch_out(const ChunkArgs& args, int blocks, bool out_bf16, hipStream_t s) {
+hipError_t launch_seq(const ChunkArgs& args, const float* ws, int chunk0, int n_seg, const float* init,
+                      size_t init_rstride, bool out_bf16, hipStream_t s) {
+  const int blocks = args.n_req * args.n_vheads * kRowBlocks;
   if (out_bf16)
     hipLaunchKernelGGL((gdn_chunked_kernel<TIn, CAPTURE, LOGG, true>), dim3(blocks), dim3(kThreads), kLdsBytes, s,
-                       args);
+                       args, ws, chunk0, n_seg, init, init_rstride);
   else
     hipLaunchKernelGGL((gdn_chunked_kernel<TIn, CAPTURE, LOGG, false>), dim3(blocks), dim3(kThreads), kLdsBytes, s,
-                       args);
+                       args, ws, chunk0, n_seg, init, init_rstride);
   return launch_error();
 }
 
+// One segment: the pre-pass of its chunks, then the sequential pass.
+template <typename TIn, bool LOGG>
+hipError_t launch_segment(const ChunkArgs& args, float* ws, int chunk0, int n_seg, const float* init,
+                          size_t init_rstride, bool capture, bool out_bf16, hipStream_t s) {
+  const int pblocks = args.n_req * args.n_vheads * n_seg;
+  hipLaunchKernelGGL((gdn_chunk_prep_kernel<TIn, LOGG>), dim3(pblocks), dim3(kThreads), kPLdsBytes, s, args, ws,
+                     chunk0, n_seg);
+  const hipError_t e = launch_error();
+  if (e != hipSuccess) return e;
+  return capture ? launch_seq<TIn, true, LOGG>(args, ws, chunk0, n_seg, init, init_rstride, out_bf16, s)
+                 : launch_seq<TIn, false, LOGG>(args, ws, chunk0, n_seg, init, init_rstride, out_bf16, s);
+}
+
 template <typename TIn>
-hipError_t launch_chunked(const ChunkArgs& args, int blocks, bool capture, bool log_gates, bool out_bf16,
+hipError_t launch_chunked(const ChunkArgs& args, float* ws, bool capture, bool log_gates, bool out_bf16,
                           hipStream_t s) {
-  if (capture)
-    return log_gates ? launch_out<TIn, true, true>(args, blocks, out_bf16, s)
-                     : launch_out<TIn, true, false>(args, blocks, out_bf16, s);
-  return log_gates ? launch_out<TIn, false, true>(args, blocks, out_bf16, s)
-                   : launch_out<TIn, false, false>(args, blocks, out_bf16, s);
+  const int n_chunks = (args.n_pos + kC - 1) / kC;
+  const size_t pos_stride = static_cast<size_t>(args.n_vheads) * kDK * kDK;
+  for (int chunk0 = 0; chunk0 < n_chunks; chunk0 += kSegChunks) {
+    const int n_seg = std::min(kSegChunks, n_chunks - chunk0);
+    // The first segment starts from `state`; later ones from the state after
+    // the previous segment: `state` itself without capture (updated in
+    // place), the checkpoint of the position before the segment with.
+    const float* init = args.state;
+    size_t init_rstride = pos_stride;
+    if (capture && chunk0 > 0) {
+      init = args.ckpt + static_cast<size_t>(chunk0 * kC - 1) * pos_stride;
+      init_rstride = static_cast<size_t>(args.n_pos) * pos_stride;
+    }
+    const hipError_t e =
+        log_gates ? launch_segment<TIn, true>(args, ws, chunk0, n_seg, init, init_rstride, capture, out_bf16, s)
+                  : launch_segment<TIn, false>(args, ws, chunk0, n_seg, init, init_rstride, capture, out_bf16, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+size_t workspace_bytes(int n_req, int n_vheads, int n_pos) {
+  const int n_chunks = (n_pos + kC - 1) / kC;
+  return static_cast<size_t>(n_req) * n_vheads * std::min(n_chunks, kSegChunks) * kRecFloats * sizeof(float);
 }
 
 }  // namespace
@@ -639,8 +856,16 @@ hipError_t launch_chunked(const ChunkArgs& args, int blocks, bool capture, bool 
 
 using namespace hrs;
 
+extern "C" size_t gdn_span_chunked_workspace_bytes(const hrs_chunked_desc* cd) {
+  if (cd == nullptr) return 0;
+  const hrs_gdn_desc* d = &cd->gdn;
+  if (d->n_req < 1 || d->n_vheads < 1 || d->n_pos < 1 || d->n_pos > HRS_MAX_CHUNKED_POS) return 0;
+  return workspace_bytes(d->n_req, d->n_vheads, d->n_pos);
+}
+
 extern "C" int gdn_span_chunked(const hrs_chunked_desc* cd, const void* q, const void* k, const void* v,
-                                const void* a, const void* b, float* state, float* ckpt, void* out, void* stream) {
+                                const void* a, const void* b, float* state, float* ckpt, void* out, void* workspace,
+                                size_t workspace_bytes_given, void* stream) {
   if (cd == nullptr) return HRS_EINVAL;
   const hrs_gdn_desc* d = &cd->gdn;
   if (d->n_req < 1 || d->n_kheads < 1 || d->n_vheads < 1 || d->d_k < 1 || d->d_v < 1) return HRS_EINVAL;
@@ -648,25 +873,26 @@ extern "C" int gdn_span_chunked(const hrs_chunked_desc* cd, const void* q, const
   if (!dtype_ok(d->in_dtype) || !dtype_ok(cd->out_dtype)) return HRS_EINVAL;
   if (d->topo != HRS_CHAIN) return d->topo == HRS_TREE ? HRS_EUNSUPPORTED : HRS_EINVAL;
   if (d->n_pos < 1 || d->n_pos > HRS_MAX_CHUNKED_POS) return HRS_EINVAL;
-  if (!q || !k || !v || !a || !b || !state || !out) return HRS_EINVAL;
-  if (static_cast<int64_t>(d->n_req) * d->n_vheads * (kDK / kRows) > (1 << 30)) return HRS_EINVAL;
+  if (!q || !k || !v || !a || !b || !state || !out || !workspace) return HRS_EINVAL;
+  if (static_cast<int64_t>(d->n_req) * d->n_vheads * kRowBlocks > (1 << 30)) return HRS_EINVAL;
+  if (static_cast<int64_t>(d->n_req) * d->n_vheads * kSegChunks > (1 << 30)) return HRS_EINVAL;
+  if (workspace_bytes_given < workspace_bytes(d->n_req, d->n_vheads, d->n_pos)) return HRS_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(a) || !aligned16(b) || !aligned16(state) ||
-      !aligned16(out) || (ckpt && !aligned16(ckpt)))
+      !aligned16(out) || (ckpt && !aligned16(ckpt)) || !aligned16(workspace))
     return HRS_EALIGN;
   if (d->d_k != kDK || d->d_v != kDK) return HRS_EUNSUPPORTED;
 
   ChunkArgs args;
   args.q = q; args.k = k; args.v = v; args.a = a; args.b = b;
   args.state = state; args.ckpt = ckpt; args.out = out;
-  args.n_pos = d->n_pos; args.n_kheads = d->n_kheads; args.n_vheads = d->n_vheads;
+  args.n_req = d->n_req; args.n_pos = d->n_pos; args.n_kheads = d->n_kheads; args.n_vheads = d->n_vheads;
   args.group = d->n_vheads / d->n_kheads; args.q_scale = d->q_scale;
-  const int blocks = d->n_req * d->n_vheads * (kDK / kRows);
   const bool logg = cd->log_gates != 0;
   const bool obf = cd->out_dtype == HRS_BF16;
+  float* ws = static_cast<float*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const hipError_t e = d->in_dtype == HRS_BF16
-                           ? launch_chunked<uint16_t>(args, blocks, ckpt != nullptr, logg, obf, s)
-                           : launch_chunked<float>(args, blocks, ckpt != nullptr, logg, obf, s);
+  const hipError_t e = d->in_dtype == HRS_BF16 ? launch_chunked<uint16_t>(args, ws, ckpt != nullptr, logg, obf, s)
+                                               : launch_chunked<float>(args, ws, ckpt != nullptr, logg, obf, s);
   return e == hipSuccess ? HRS_OK : HRS_EDEVICE;
 }

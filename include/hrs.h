@@ -216,6 +216,13 @@ typedef struct {
                            rounded to the nearest bf16, ties to even) */
 } hrs_chunked_desc;
 
+/* Bytes of device workspace gdn_span_chunked needs for this descriptor:
+ * n_req x n_vheads x min(ceil(n_pos / 64), 32) x 33,280 (one record of T,
+ * P T and the decays per request, value head and chunk of a 32-chunk
+ * segment; 34 MB for one request of 32 heads at any length from 2,048
+ * positions). 0 for a NULL descriptor or sizes out of range. */
+size_t gdn_span_chunked_workspace_bytes(const hrs_chunked_desc* desc);
+
 /*
  * gdn_span_chunked - the gated delta rule of gdn_verify_span over a long
  * chain span (prefill length, up to HRS_MAX_CHUNKED_POS positions), computed
@@ -226,23 +233,28 @@ typedef struct {
  * solve the unit lower-triangular system
  *     w_t + sum_{j<t} b_t G[t][j] (k_t . k_j) w_j = b_t (v_t - g_t S_0 k_t),
  * G[t][j] = a_{j+1}...a_t, g_t = a_0...a_t (products inside the chunk, so
- * zero or tiny decays are exact), with k k^T on the matrix cores; then
- * S_t = a_t S_{t-1} + w_t k_t^T and o_t = S_t (q_scale q_t) as in
- * gdn_verify_span. Same mathematics, different rounding order: results agree
- * with gdn_verify_span to f32 rounding, not bit for bit.
+ * zero or tiny decays are exact), i.e. W = T Y with T the inverse of the
+ * system's matrix; then S_t = a_t S_{t-1} + w_t k_t^T and o_t = S_t
+ * (q_scale q_t) as in gdn_verify_span. Same mathematics, different rounding
+ * order: results agree with gdn_verify_span to f32 rounding, not bit for bit.
  *
  * Arguments, layouts and capture as gdn_verify_span, chain only
  * (desc->gdn.topo must be HRS_CHAIN; parent is ignored), with two variants:
  * log-space gates and bf16 outputs (`out` [R][T][Hv][d_v] in out_dtype).
  * ckpt != NULL writes every position's state and leaves `state` unchanged;
  * ckpt == NULL updates `state` in place to the state after the last
- * position. Errors: HRS_EINVAL (sizes, NULL pointers, n_pos outside
- * [1, HRS_MAX_CHUNKED_POS], out_dtype), HRS_EALIGN, HRS_EUNSUPPORTED (tree
- * topology; d_k or d_v other than 128), HRS_EDEVICE.
+ * position. workspace: caller-owned device memory of at least
+ * gdn_span_chunked_workspace_bytes(desc) bytes, 16-byte aligned, contents
+ * ignored and overwritten (the per-chunk T, P T and decays; spans longer
+ * than 32 chunks reuse it segment by segment, two launches per segment).
+ * Errors: HRS_EINVAL (sizes, NULL pointers or workspace, a workspace smaller
+ * than required, n_pos outside [1, HRS_MAX_CHUNKED_POS], out_dtype),
+ * HRS_EALIGN, HRS_EUNSUPPORTED (tree topology; d_k or d_v other than 128),
+ * HRS_EDEVICE.
  */
 int gdn_span_chunked(const hrs_chunked_desc* desc, const void* q, const void* k, const void* v,
                      const void* a, const void* b, float* state, float* ckpt, void* out,
-                     void* stream);
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 typedef struct {
   hrs_gdn_desc gdn;    /* shapes, dtype, q_scale and topology of the span */

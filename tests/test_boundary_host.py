@@ -394,11 +394,13 @@ def test_chunked_entry_rejections():
     E = hrs
 
     def call(n_req=1, n_pos=200, Hk=2, Hv=4, dk=128, dv=128, dt=hrs.HRS_BF16, topo=hrs.HRS_CHAIN, q=FAKE, state=FAKE,
-             ckpt=None, out=FAKE, desc=True, out_dt=hrs.HRS_F32, log_gates=0):
+             ckpt=None, out=FAKE, desc=True, out_dt=hrs.HRS_F32, log_gates=0, ws=FAKE, ws_bytes=None):
         g = hrs.GdnDesc(n_req, n_pos, Hk, Hv, dk, dv, dt, 1.0, topo, None)
         d = hrs.ChunkedDesc(g, log_gates, out_dt)
+        if ws_bytes is None:
+            ws_bytes = hrs.lib.gdn_span_chunked_workspace_bytes(ctypes.byref(d))
         return hrs.lib.gdn_span_chunked(ctypes.byref(d) if desc else None, q, FAKE, FAKE, FAKE, FAKE, state, ckpt,
-                                        out, None)
+                                        out, ws, ws_bytes, None)
     assert call(desc=False) == E.HRS_EINVAL
     assert call(n_req=0) == E.HRS_EINVAL
     assert call(Hv=3) == E.HRS_EINVAL
@@ -415,6 +417,11 @@ def test_chunked_entry_rejections():
     assert call(ckpt=MIS) == E.HRS_EALIGN
     assert call(out=MIS) == E.HRS_EALIGN
     assert call(dk=64, dv=64) == E.HRS_EUNSUPPORTED
+    assert call(ws=None) == E.HRS_EINVAL
+    assert call(ws_bytes=0) == E.HRS_EINVAL
+    assert call(ws_bytes=1 * 4 * 4 * 33280 - 1) == E.HRS_EINVAL
+    assert call(ws=MIS) == E.HRS_EALIGN
+    assert call(ws_bytes=1 * 4 * 4 * 33280) == E.HRS_EDEVICE
     assert call(n_pos=(1 << 20)) == E.HRS_EDEVICE
     assert call(ckpt=FAKE, out_dt=hrs.HRS_BF16, log_gates=1) == E.HRS_EDEVICE
     assert call() == E.HRS_EDEVICE

@@ -2,8 +2,9 @@
 the GDN oracle (the plain recurrence), through the C ABI: final states,
 outputs and, with capture, every checkpoint within max relative error 1e-4
 per tile; spans that end inside a chunk, exactly on a chunk boundary and
-within the first chunk; bf16 (matrix-core k k^T) and f32 inputs; zero decays;
-agreement with gdn_verify_span on short spans."""
+within the first chunk; spans over more than one 32-chunk segment (the
+workspace reused); bf16 (matrix-core k k^T) and f32 inputs; zero decays;
+agreement with gdn_verify_span on short spans; workspace contents ignored."""
 import numpy as np
 import pytest
 
@@ -22,6 +23,18 @@ def hrs():
     return m
 
 
+def workspace(hrs, q, v, fill=None):
+    """A workspace of exactly the size the library asks for, filled with a
+    byte pattern (the kernels must not depend on its contents)."""
+    import torch
+    R, T, Hk = q.shape[:3]
+    n = hrs.gdn_span_chunked_workspace_bytes(R, T, Hk, v.shape[2])
+    assert n > 0
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5 if fill is None else fill)
+    return ws
+
+
 def run(hrs, units, capture, q_scale=1.0):
     import torch
     st = lambda name: to_torch(np.stack([getattr(u, name) for u in units]))
@@ -30,7 +43,7 @@ def run(hrs, units, capture, q_scale=1.0):
     Hv, dv = v.shape[2], v.shape[3]
     ckpt = torch.full((R, T, Hv, dv, dk), float("nan"), device="cuda") if capture else None
     out = torch.full((R, T, Hv, dv), float("nan"), device="cuda")
-    hrs.gdn_span_chunked(q, k, v, a, b, state, ckpt, out, q_scale=q_scale)
+    hrs.gdn_span_chunked(q, k, v, a, b, state, ckpt, out, workspace(hrs, q, v), q_scale=q_scale)
     torch.cuda.synchronize()
     return (to_numpy(ckpt) if capture else None), to_numpy(out), to_numpy(state)
 
@@ -70,6 +83,18 @@ def test_chunked_long_span(hrs):
     check(units, ck, out, state, False, what="T=1000")
 
 
+@pytest.mark.parametrize("T,capture,Hv", [(2048, False, 8), (2100, False, 2), (2113, True, 1)])
+def test_chunked_spans_over_several_segments(hrs, T, capture, Hv):
+    """More than 32 chunks: the pre-pass records of the second segment
+    overwrite the first's in the workspace, and the second segment starts
+    from the state the first left (in place, or the checkpoint before it)."""
+    w = scaled(QWEN_LAYER_CHAIN, n_req=2 if capture else 1, n_pos=T, n_kheads=1, n_vheads=Hv)
+    units = [gen_unit(w, 0, r) for r in range(w.n_req)]
+    say(f"chunked segments T={T} capture={capture}")
+    ck, out, state = run(hrs, units, capture)
+    check(units, ck, out, state, capture, what=f"T={T}")
+
+
 def test_chunked_zero_and_unit_decays(hrs):
     w = scaled(QWEN_LAYER_CHAIN, n_req=1, n_pos=100, n_kheads=2, n_vheads=4)
     u = gen_unit(w, 0, 0)
@@ -91,7 +116,8 @@ def test_chunked_matches_recurrent_kernel_on_short_spans(hrs):
     R, T, Hv, d = 3, 17, 32, 128
     ck1 = torch.empty((R, T, Hv, d, d), device="cuda"); out1 = torch.empty((R, T, Hv, d), device="cuda")
     ck2 = torch.empty_like(ck1); out2 = torch.empty_like(out1)
-    hrs.gdn_span_chunked(q, k, v, a, b, state, ck1, out1)
+    ws = workspace(hrs, q, v)
+    hrs.gdn_span_chunked(q, k, v, a, b, state, ck1, out1, ws)
     hrs.gdn_verify_span(q, k, v, a, b, state, ck2, out2)
     torch.cuda.synchronize()
     c1, c2, o1, o2 = to_numpy(ck1), to_numpy(ck2), to_numpy(out1), to_numpy(out2)
@@ -103,7 +129,8 @@ def test_chunked_matches_recurrent_kernel_on_short_spans(hrs):
     # outputs are the same computation
     st2 = state.clone()
     out3 = torch.empty_like(out1)
-    hrs.gdn_span_chunked(q, k, v, a, b, st2, None, out3)
+    ws.fill_(0x5A)
+    hrs.gdn_span_chunked(q, k, v, a, b, st2, None, out3, ws)
     torch.cuda.synchronize()
     s2, last = to_numpy(st2), to_numpy(ck1[:, -1])
     for r in range(R):
@@ -126,7 +153,7 @@ def test_chunked_log_gates(hrs):
     R, T, Hv, d = 2, 90, 8, 128
     ckpt = torch.full((R, T, Hv, d, d), float("nan"), device="cuda")
     out = torch.full((R, T, Hv, d), float("nan"), device="cuda")
-    hrs.gdn_span_chunked(q, k, v, g, b, state, ckpt, out, log_gates=True)
+    hrs.gdn_span_chunked(q, k, v, g, b, state, ckpt, out, workspace(hrs, q, v), log_gates=True)
     torch.cuda.synchronize()
     ck, o = to_numpy(ckpt), to_numpy(out)
     for r, u in enumerate(units):
@@ -150,8 +177,8 @@ def test_chunked_bf16_outputs(hrs):
     out32 = torch.empty((R, T, Hv, d), device="cuda")
     out16 = torch.empty((R, T, Hv, d), device="cuda", dtype=torch.bfloat16)
     s1, s2 = st("state"), st("state")
-    hrs.gdn_span_chunked(q, k, v, a, b, s1, None, out32, q_scale=0.5)
-    hrs.gdn_span_chunked(q, k, v, a, b, s2, None, out16, q_scale=0.5)
+    hrs.gdn_span_chunked(q, k, v, a, b, s1, None, out32, workspace(hrs, q, v), q_scale=0.5)
+    hrs.gdn_span_chunked(q, k, v, a, b, s2, None, out16, workspace(hrs, q, v, fill=0xFF), q_scale=0.5)
     torch.cuda.synchronize()
     o32 = to_numpy(out32)
     o16 = to_numpy(out16)
