@@ -61,28 +61,44 @@ constexpr int kTS = kC + 4;     // LDS row stride of the 64-wide matrices (16-by
 constexpr int kSegChunks = 32;  // chunks per pre-pass + sequential launch pair
 
 // Pre-pass record of one (request, value head, chunk) in the workspace, in
-// floats: T = (I + A)^-1 and P T row-major, then g_t and G[C-1][t].
+// floats: the 10 lower 16 x 16 tiles of T = (I + A)^-1, then those of P T
+// (both are lower triangular), then g_t and G[C-1][t]. A tile (i, j), j <= i,
+// sits at index i (i + 1) / 2 + j, in the order the sequential kernel's
+// matrix-core operands read it: lane l = 16 kq + r of wave i holds row
+// 16 i + r, columns 16 j + 4 kq .. + 3, as floats [4 l, 4 l + 4) of the tile.
+constexpr int kTiles = 10;
 constexpr int kRecT = 0;
-constexpr int kRecPT = kRecT + kC * kC;
-constexpr int kRecG = kRecPT + kC * kC;
+constexpr int kRecPT = kRecT + kTiles * 256;
+constexpr int kRecG = kRecPT + kTiles * 256;
 constexpr int kRecGC = kRecG + kC;
 constexpr int kRecFloats = kRecGC + kC;
 
-// Sequential kernel LDS layout, in floats.
-constexpr int kOffK = 0;                          // [C][kKS] k rows (f32)
-constexpr int kOffQ = kOffK + kC * kKS;           // [C][kKS] q rows (f32, unscaled)
-constexpr int kOffV = kOffQ + kC * kKS;           // [C][16] v rows of the block
-constexpr int kOffS0 = kOffV + kC * kRows;        // [16][kSS] S_0 rows
-constexpr int kOffT = kOffS0 + kRows * kSS;       // [C][kTS] T
-constexpr int kOffPT = kOffT + kC * kTS;          // [C][kTS] P T
-constexpr int kOffY = kOffPT + kC * kTS;          // [16][kTS] Y^T (state row, position)
-constexpr int kOffW = kOffY + kRows * kTS;        // [16][kTS] W^T
-constexpr int kOffG = kOffW + kRows * kTS;        // [C] g_t
-constexpr int kOffGC = kOffG + kC;                // [C] G[n-1][t] (follows g_t, as in the record)
-constexpr int kOffAv = kOffGC + kC;               // [C] a_t
-constexpr int kOffBv = kOffAv + kC;               // [C] b_t
-constexpr int kLdsFloats = kOffBv + kC;
-constexpr size_t kLdsBytes = static_cast<size_t>(kLdsFloats) * sizeof(float);
+__host__ __device__ constexpr int tile_index(int i, int j) { return i * (i + 1) / 2 + j; }
+
+// Sequential kernel LDS layout, in bytes. BF (bf16 inputs): k and q staged
+// as bf16, and the chunk's starting state also as three bf16 parts whose sum
+// is the f32 value (the operands of the bf16 products); f32 inputs: k and q
+// as f32. T and P T never go through LDS: each wave loads its own 16 rows
+// straight into its matrix-core operand registers.
+template <bool BF>
+struct SeqLds {
+  static constexpr int kKRow = BF ? (kDK + 8) * 2 : kKS * 4;   // bytes per k or q row (16-byte rows)
+  static constexpr int kSplRow = (kDK + 8) * 2;                // bytes per row of one state part
+  static constexpr int K = 0;                                  // [C] rows of k
+  static constexpr int Q = K + kC * kKRow;                     // [C] rows of q (unscaled)
+  static constexpr int V = Q + kC * kKRow;                     // f32 [C][16] v rows of the block
+  static constexpr int S0 = V + kC * kRows * 4;                // f32 [16][kSS] S_0 rows
+  static constexpr int SPL = S0 + kRows * kSS * 4;             // BF: bf16 [3][16] S_0 parts
+  static constexpr int Y = SPL + (BF ? 3 * kRows * kSplRow : 0);   // f32 [16][kTS] Y^T (state row, position)
+  static constexpr int W = Y + kRows * kTS * 4;                // f32 [16][kTS] W^T
+  static constexpr int G = W + kRows * kTS * 4;                // f32 [C] g_t
+  static constexpr int GC = G + kC * 4;                        // f32 [C] G[n-1][t] (follows g_t, as in the record)
+  static constexpr int AV = GC + kC * 4;                       // f32 [C] a_t
+  static constexpr int BV = AV + kC * 4;                       // f32 [C] b_t
+  static constexpr int BYTES = BV + kC * 4;
+  static_assert(Q % 16 == 0 && V % 16 == 0 && S0 % 16 == 0 && SPL % 16 == 0 && Y % 16 == 0 && W % 16 == 0,
+                "16-byte LDS rows");
+};
 
 // Pre-pass LDS layout: k and q staged first; A, P, T and T^T take their
 // place once the Gram products are in registers.
@@ -284,13 +300,13 @@ __device__ __forceinline__ void fetch_chunk(const ChunkArgs& args, ChunkRegs<TIn
   }
 }
 
-// Write a fetched chunk into LDS as f32: k and q (unscaled) at kOffK/kOffQ,
-// with WITHV the v rows at kOffV, and a_t, b_t at av/bv.
-template <typename TIn, bool LOGG, bool WITHV>
+// Pre-pass staging: a fetched chunk's k and q (unscaled) into LDS as f32,
+// and a_t, b_t at av/bv.
+template <typename TIn, bool LOGG>
 __device__ __forceinline__ void stage_chunk(float* lds, const ChunkRegs<TIn>& rg, int n, float* av, float* bv) {
   const int tid = threadIdx.x;
-  float* const Kl = lds + kOffK;
-  float* const Ql = lds + kOffQ;
+  float* const Kl = lds + kPOffK;
+  float* const Ql = lds + kPOffQ;
 #pragma unroll
   for (int i = 0; i < kKQItems; ++i) {
     const int e = tid + i * kThreads;
@@ -303,15 +319,6 @@ __device__ __forceinline__ void stage_chunk(float* lds, const ChunkRegs<TIn>& rg
     rg.q[i].widen(x);
     *reinterpret_cast<f32x4*>(Ql + t * kKS + j) = f32x4{x[0], x[1], x[2], x[3]};
     *reinterpret_cast<f32x4*>(Ql + t * kKS + j + 4) = f32x4{x[4], x[5], x[6], x[7]};
-  }
-  if constexpr (WITHV) {
-    if (tid < kC * (kRows / 8)) {
-      float x[8];
-      rg.v.widen(x);
-      float* const lv = lds + kOffV + (tid / (kRows / 8)) * kRows + (tid % (kRows / 8)) * 8;
-      *reinterpret_cast<f32x4*>(lv) = f32x4{x[0], x[1], x[2], x[3]};
-      *reinterpret_cast<f32x4*>(lv + 4) = f32x4{x[4], x[5], x[6], x[7]};
-    }
   }
   if (tid < kC) {
     // Log-space gates: a_t = exp(g_t) (positions past the span end keep a = 1).
@@ -360,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep_kernel(const ChunkArg
   {
     ChunkRegs<TIn> rg;
     fetch_chunk<TIn, false>(args, rg, r, h, h / args.group, 0, c0, n);
-    stage_chunk<TIn, LOGG, false>(lds, rg, n, Av, Bv);
+    stage_chunk<TIn, LOGG>(lds, rg, n, Av, Bv);
   }
   __syncthreads();
   gram<TIn>(lds);
@@ -476,81 +483,136 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep_kernel(const ChunkArg
       __syncthreads();
     }
   }
-  // The record: T, g and G[n-1][.] copied out, P T on the matrix cores
-  // (16x16x4 f32 MFMA, 16 x 16 tiles; P T is lower triangular like both
-  // factors, so tile (i, j) sums over the blocks k in [j, i]: 20 block
-  // products, 5 per wave; tiles right of the diagonal are 0).
+  // The record: T's lower tiles, g and G[n-1][.] copied out in the reader's
+  // order; P T on the matrix cores (16x16x4 f32 MFMA) as the transposed
+  // product T^T P^T, whose output lanes hold exactly the reader's 4-column
+  // pieces of P T: tile (i, j) sums over the blocks k in [j, i], 20 block
+  // products over the 10 tiles, 5 per wave.
   {
-    const int t = tid >> 2;
-    const int col = (tid & 3) * 16;
-#pragma unroll
-    for (int m = 0; m < 16; m += 4)
-      *reinterpret_cast<f32x4*>(rec + kRecT + t * kC + col + m) =
-          *reinterpret_cast<const f32x4*>(Tl + t * kTS + col + m);
+    const int i = lane & 15;
+    const int kq = lane >> 4;
+    for (int c = 0; c <= wave; ++c)
+      *reinterpret_cast<f32x4*>(rec + kRecT + tile_index(wave, c) * 256 + 4 * lane) =
+          *reinterpret_cast<const f32x4*>(Tl + (16 * wave + i) * kTS + 16 * c + 4 * kq);
     if (tid < 2 * kC / 4)
       *reinterpret_cast<f32x4*>(rec + kRecG + 4 * tid) = *reinterpret_cast<const f32x4*>(Gv + 4 * tid);
   }
   {
-    // Tiles per wave, (i, j) packed as 4 i + j; 16 ends a list. The first
-    // list is computed, the second written as zeros.
-    constexpr uint8_t kTiles[4][4] = {{12, 0, 16, 16}, {8, 4, 16, 16}, {13, 9, 16, 16}, {14, 5, 10, 15}};
-    constexpr uint8_t kZeros[4][2] = {{1, 2}, {3, 6}, {7, 16}, {11, 16}};
+    // Tiles per wave, (i, j) packed as 4 i + j; 16 ends a list.
+    constexpr uint8_t kPtTiles[4][4] = {{12, 0, 16, 16}, {8, 4, 16, 16}, {13, 9, 16, 16}, {14, 5, 10, 15}};
     const int i = lane & 15;
     const int kq = lane >> 4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int tile = kTiles[wave][e];
+      const int tile = kPtTiles[wave][e];
       if (tile == 16) break;
       const int ti = tile >> 2, tj = tile & 3;
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int c = 16 * tj; c < 16 * ti + 16; c += 16) {
-        const f32x4 pv = *reinterpret_cast<const f32x4*>(P + (16 * ti + i) * kTS + c + 4 * kq);
         const f32x4 tv = *reinterpret_cast<const f32x4*>(Tt + (16 * tj + i) * kTS + c + 4 * kq);
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(P + (16 * ti + i) * kTS + c + 4 * kq);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[u], tv[u], acc, 0, 0, 0);
+        for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tv[u], pv[u], acc, 0, 0, 0);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) rec[kRecPT + (16 * ti + 4 * kq + u) * kC + 16 * tj + i] = acc[u];
-    }
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int tile = kZeros[wave][e];
-      if (tile == 16) break;
-      const int ti = tile >> 2, tj = tile & 3;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) rec[kRecPT + (16 * ti + 4 * kq + u) * kC + 16 * tj + i] = 0.0f;
+      *reinterpret_cast<f32x4*>(rec + kRecPT + tile_index(ti, tj) * 256 + 4 * lane) = acc;
     }
   }
 }
 
-// The pre-pass record of one chunk in registers (T and P T rows t = tid / 4,
-// columns [16 (tid % 4), + 16); g and G[n-1][.] in the first 32 threads).
+// The pre-pass record of one chunk in registers, in the layout of the
+// matrix-core operands that read it: wave w's lane (i, kq) = (lane % 16,
+// lane / 16) holds T[16 w + i][16 c + 4 kq + u] and the same of P T for the
+// column blocks c <= w (one coalesced 16-byte load per lane and tile); the
+// first 32 threads also hold g and G[n-1][.] (4 values each).
 struct RecRegs {
   f32x4 t[4], pt[4], g;
 };
 
 __device__ __forceinline__ void fetch_rec(const float* rec, RecRegs& rr) {
   const int tid = threadIdx.x;
-  const int row = tid >> 2;
-  const int col = (tid & 3) * 16;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    rr.t[m] = *reinterpret_cast<const f32x4*>(rec + kRecT + row * kC + col + 4 * m);
-    rr.pt[m] = *reinterpret_cast<const f32x4*>(rec + kRecPT + row * kC + col + 4 * m);
+  for (int c = 0; c < 4; ++c) {
+    if (c <= wave) {
+      rr.t[c] = *reinterpret_cast<const f32x4*>(rec + kRecT + tile_index(wave, c) * 256 + 4 * lane);
+      rr.pt[c] = *reinterpret_cast<const f32x4*>(rec + kRecPT + tile_index(wave, c) * 256 + 4 * lane);
+    }
   }
   if (tid < 2 * kC / 4) rr.g = *reinterpret_cast<const f32x4*>(rec + kRecG + 4 * tid);
 }
 
-__device__ __forceinline__ void stage_rec(float* lds, const RecRegs& rr) {
+// Sequential staging of a fetched chunk: k and q (bf16 as loaded, or f32),
+// the block's v rows and a_t, b_t as f32.
+template <typename TIn, bool LOGG>
+__device__ __forceinline__ void stage_seq(char* lds, const ChunkRegs<TIn>& rg, int n) {
+  using L = SeqLds<sizeof(TIn) == 2>;
   const int tid = threadIdx.x;
-  const int row = tid >> 2;
-  const int col = (tid & 3) * 16;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    *reinterpret_cast<f32x4*>(lds + kOffT + row * kTS + col + 4 * m) = rr.t[m];
-    *reinterpret_cast<f32x4*>(lds + kOffPT + row * kTS + col + 4 * m) = rr.pt[m];
+  for (int i = 0; i < kKQItems; ++i) {
+    const int e = tid + i * kThreads;
+    const int t = e / (kDK / 8);
+    const int j = (e % (kDK / 8)) * 8;
+    char* const kd = lds + L::K + t * L::kKRow;
+    char* const qd = lds + L::Q + t * L::kKRow;
+    if constexpr (sizeof(TIn) == 2) {
+      *reinterpret_cast<u32x4*>(kd + 2 * j) = rg.k[i].v;
+      *reinterpret_cast<u32x4*>(qd + 2 * j) = rg.q[i].v;
+    } else {
+      *reinterpret_cast<f32x4*>(kd + 4 * j) = rg.k[i].a;
+      *reinterpret_cast<f32x4*>(kd + 4 * j + 16) = rg.k[i].b;
+      *reinterpret_cast<f32x4*>(qd + 4 * j) = rg.q[i].a;
+      *reinterpret_cast<f32x4*>(qd + 4 * j + 16) = rg.q[i].b;
+    }
   }
-  if (tid < 2 * kC / 4) *reinterpret_cast<f32x4*>(lds + kOffG + 4 * tid) = rr.g;
+  if (tid < kC * (kRows / 8)) {
+    float x[8];
+    rg.v.widen(x);
+    float* const lv = reinterpret_cast<float*>(lds + L::V) + (tid / (kRows / 8)) * kRows + (tid % (kRows / 8)) * 8;
+    *reinterpret_cast<f32x4*>(lv) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(lv + 4) = f32x4{x[4], x[5], x[6], x[7]};
+  }
+  if (tid < kC) {
+    // Log-space gates: a_t = exp(g_t) (positions past the span end keep a = 1).
+    const float a = gate_widen<TIn>(rg.a);
+    reinterpret_cast<float*>(lds + L::AV)[tid] = (LOGG && tid < n) ? expf(a) : a;
+    reinterpret_cast<float*>(lds + L::BV)[tid] = gate_widen<TIn>(rg.b);
+  }
+}
+
+// f32 x as hi + mid + lo, three bf16 values whose sum is x exactly (x
+// finite): hi keeps the top 8 significant bits, x - hi (exact) the next 16,
+// split the same way; the last 8 bits fit a bf16 as they are.
+__device__ __forceinline__ void split3(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
+  const uint32_t hb = __float_as_uint(x) & 0xFFFF0000u;
+  const float r1 = x - __uint_as_float(hb);
+  const uint32_t mb = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = r1 - __uint_as_float(mb);
+  h = hb >> 16;
+  m = mb >> 16;
+  l = __float_as_uint(r2) >> 16;
+}
+
+// One value of row t of the staged k, column c, as f32.
+template <bool BF>
+__device__ __forceinline__ float k_at(const char* lds, int t, int c) {
+  using L = SeqLds<BF>;
+  if constexpr (BF)
+    return bf16_one(*reinterpret_cast<const uint16_t*>(lds + L::K + t * L::kKRow + 2 * c));
+  else
+    return *reinterpret_cast<const float*>(lds + L::K + t * L::kKRow + 4 * c);
+}
+
+// Four consecutive values of row t of the staged k from column c (c % 4 == 0).
+template <bool BF>
+__device__ __forceinline__ f32x4 k4_at(const char* lds, int t, int c) {
+  using L = SeqLds<BF>;
+  if constexpr (BF) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(lds + L::K + t * L::kKRow + 2 * c);
+    return f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+  } else {
+    return *reinterpret_cast<const f32x4*>(lds + L::K + t * L::kKRow + 4 * c);
+  }
 }
 
 // Sequential pass over the segment's chunks. init: the state the segment
@@ -560,7 +622,10 @@ __device__ __forceinline__ void stage_rec(float* lds, const RecRegs& rr) {
 template <typename TIn, bool CAPTURE, bool LOGG, bool OUTBF>
 __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs args, const float* ws, int chunk0,
                                                                int n_seg, const float* init, size_t init_rstride) {
-  extern __shared__ float lds[];
+  constexpr bool BF = sizeof(TIn) == 2;
+  using L = SeqLds<BF>;
+  extern __shared__ float lds_f[];
+  char* const lds = reinterpret_cast<char*>(lds_f);
   const int T = args.n_pos;
   const int Hv = args.n_vheads;
   const int n_heads = args.n_req * Hv;
@@ -589,18 +654,14 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
   const int row_blk = wave * (64 / kLPR) + lane / kLPR;   // 0..15
   const size_t head_elems = static_cast<size_t>(kDK) * kDK;
   const size_t pos_stride = static_cast<size_t>(Hv) * head_elems;
-  float* const Kl = lds + kOffK;
-  float* const Ql = lds + kOffQ;
-  float* const Vl = lds + kOffV;
-  float* const S0 = lds + kOffS0;
-  float* const Tl = lds + kOffT;
-  float* const PTl = lds + kOffPT;
-  float* const Yt = lds + kOffY;
-  float* const Wt = lds + kOffW;
-  float* const Gv = lds + kOffG;
-  float* const GC = lds + kOffGC;
-  float* const Av = lds + kOffAv;
-  float* const Bv = lds + kOffBv;
+  const float* const Vl = reinterpret_cast<const float*>(lds + L::V);
+  float* const S0 = reinterpret_cast<float*>(lds + L::S0);
+  float* const Yt = reinterpret_cast<float*>(lds + L::Y);
+  float* const Wt = reinterpret_cast<float*>(lds + L::W);
+  float* const Gv = reinterpret_cast<float*>(lds + L::G);
+  float* const GC = reinterpret_cast<float*>(lds + L::GC);
+  const float* const Av = reinterpret_cast<const float*>(lds + L::AV);
+  const float* const Bv = reinterpret_cast<const float*>(lds + L::BV);
   const float* const rec0 = ws + (static_cast<size_t>(r) * Hv + h) * n_seg * kRecFloats;
 
   const size_t row_off = static_cast<size_t>(h) * head_elems + static_cast<size_t>(row0 + row_blk) * kDK;
@@ -633,46 +694,88 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
   };
 
   ChunkRegs<TIn> rg;
-  RecRegs rr;
+  RecRegs cur, nxt;
   fetch_chunk<TIn, true>(args, rg, r, h, g, row0, chunk0 * kC, min(kC, T - chunk0 * kC));
-  fetch_rec(rec0, rr);
+  fetch_rec(rec0, nxt);
   for (int cl = 0; cl < n_seg; ++cl) {
     const int c0 = (chunk0 + cl) * kC;
     const int n = min(kC, T - c0);
     __syncthreads();   // the previous chunk's LDS reads are done
-    // 1. Stage the fetched chunk and its record and the current state rows,
-    //    then fetch the next chunk: its loads complete while this one is
-    //    processed.
-    stage_chunk<TIn, LOGG, true>(lds, rg, n, Av, Bv);
-    stage_rec(lds, rr);
+    // 1. Stage the fetched chunk, its decays and the current state rows (as
+    //    f32 and, for the bf16 products, as three bf16 parts), take over
+    //    the record's T and P T rows, then fetch the next chunk: its loads
+    //    complete while this one is processed.
+    stage_seq<TIn, LOGG>(lds, rg, n);
+    cur = nxt;
+    if (tid < 2 * kC / 4) *reinterpret_cast<f32x4*>(Gv + 4 * tid) = cur.g;
 #pragma unroll
-    for (int m = 0; m < kNCH; ++m) *reinterpret_cast<f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m)) = s[m];
+    for (int m = 0; m < kNCH; ++m) {
+      *reinterpret_cast<f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m)) = s[m];
+      if constexpr (BF) {
+        uint32_t hp[4], mp[4], lp[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split3(s[m][e], hp[e], mp[e], lp[e]);
+        char* const sp = lds + L::SPL + row_blk * L::kSplRow + 2 * 4 * (li + kLPR * m);
+        *reinterpret_cast<u32x2*>(sp) = u32x2{hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16)};
+        *reinterpret_cast<u32x2*>(sp + kRows * L::kSplRow) = u32x2{mp[0] | (mp[1] << 16), mp[2] | (mp[3] << 16)};
+        *reinterpret_cast<u32x2*>(sp + 2 * kRows * L::kSplRow) = u32x2{lp[0] | (lp[1] << 16), lp[2] | (lp[3] << 16)};
+      }
+    }
     if (cl + 1 < n_seg) {
       fetch_chunk<TIn, true>(args, rg, r, h, g, row0, c0 + kC, min(kC, T - c0 - kC));
-      fetch_rec(rec0 + static_cast<size_t>(cl + 1) * kRecFloats, rr);
+      fetch_rec(rec0 + static_cast<size_t>(cl + 1) * kRecFloats, nxt);
     }
     __syncthreads();
     store_pending();
-    // 2. X = K S_0^T and QS = Q S_0^T on the matrix cores (16x16x4 f32
-    //    MFMA, exact f32 products): wave w takes positions [16 w, 16 w + 16)
-    //    for all 16 state rows; in each step of 4 MFMAs over 16 columns, lane
-    //    group kq supplies columns [c + 4 kq, c + 4 kq + 4), so a lane reads
-    //    its operands as 16-byte LDS loads. Then Y = b (V - g X), stored
-    //    transposed, and q_scale g QS kept in the lanes that hold it.
+    // 2. X = K S_0^T and QS = Q S_0^T: wave w takes positions [16 w,
+    //    16 w + 16) for all 16 state rows. bf16 inputs: three bf16 products
+    //    per operand pair (16x16x32 MFMA: k and q are bf16, S_0 = hi + mid +
+    //    lo exactly, each product exact, f32 accumulation); f32 inputs: f32
+    //    products (16x16x4 MFMA), lane group kq supplying columns [c + 4 kq,
+    //    c + 4 kq + 4) of each 16, so a lane reads its operands as 16-byte
+    //    LDS loads. Then Y = b (V - g X), stored transposed, and q_scale g QS
+    //    kept in the lanes that hold it.
     const int tb = 16 * wave + 4 * kq;   // this lane's 4 positions of the wave's tile
     f32x4 qsg;
     {
       const int row = 16 * wave + srow;
-      f32x4 xk = {}, xq = {};
-#pragma unroll 2
-      for (int c = 0; c < kDK; c += 16) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(Kl + row * kKS + c + 4 * kq);
-        const f32x4 qv = *reinterpret_cast<const f32x4*>(Ql + row * kKS + c + 4 * kq);
-        const f32x4 sv = *reinterpret_cast<const f32x4*>(S0 + srow * kSS + c + 4 * kq);
+      f32x4 xk, xq;
+      if constexpr (BF) {
+        f32x4 xh = {}, xm = {}, xl = {}, qh = {}, qm = {}, ql = {};
+#pragma unroll
+        for (int c = 0; c < kDK; c += 32) {
+          const int col = 2 * (c + 8 * kq);
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lds + L::K + row * L::kKRow + col);
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(lds + L::Q + row * L::kKRow + col);
+          const char* const sp = lds + L::SPL + srow * L::kSplRow + col;
+          const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sp);
+          const bf16x8 sm = *reinterpret_cast<const bf16x8*>(sp + kRows * L::kSplRow);
+          const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sp + 2 * kRows * L::kSplRow);
+          xh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sh, xh, 0, 0, 0);
+          qh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, sh, qh, 0, 0, 0);
+          xm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sm, xm, 0, 0, 0);
+          qm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, sm, qm, 0, 0, 0);
+          xl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sl, xl, 0, 0, 0);
+          ql = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, sl, ql, 0, 0, 0);
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          xk = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[u], sv[u], xk, 0, 0, 0);
-          xq = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[u], sv[u], xq, 0, 0, 0);
+          xk[u] = (xl[u] + xm[u]) + xh[u];
+          xq[u] = (ql[u] + qm[u]) + qh[u];
+        }
+      } else {
+        xk = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        xq = xk;
+#pragma unroll 2
+        for (int c = 0; c < kDK; c += 16) {
+          const f32x4 kv = *reinterpret_cast<const f32x4*>(lds + L::K + row * L::kKRow + 4 * (c + 4 * kq));
+          const f32x4 qv = *reinterpret_cast<const f32x4*>(lds + L::Q + row * L::kKRow + 4 * (c + 4 * kq));
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(S0 + srow * kSS + c + 4 * kq);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            xk = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[u], sv[u], xk, 0, 0, 0);
+            xq = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[u], sv[u], xq, 0, 0, 0);
+          }
         }
       }
       const f32x4 g4 = *reinterpret_cast<const f32x4*>(Gv + tb);
@@ -687,20 +790,21 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
     }
     __syncthreads();
     // 3. W = T Y and P T Y in one pass over Y (16x16x4 f32 MFMA; wave w
-    //    takes positions [16 w, 16 w + 16), T and P T are lower triangular so
-    //    columns past 16 w + 15 are skipped); outputs o = q_scale g QS + P T Y,
-    //    stored after the next chunk is staged.
+    //    takes positions [16 w, 16 w + 16) with its T and P T rows in
+    //    registers; both are lower triangular, so the column blocks past w
+    //    are skipped); outputs o = q_scale g QS + P T Y, stored after the
+    //    next chunk is staged.
     {
-      const int trow = 16 * wave + srow;
       f32x4 wacc = {}, oacc = {};
-      for (int c = 0; c <= 16 * wave; c += 16) {
-        const f32x4 tv = *reinterpret_cast<const f32x4*>(Tl + trow * kTS + c + 4 * kq);
-        const f32x4 pv = *reinterpret_cast<const f32x4*>(PTl + trow * kTS + c + 4 * kq);
-        const f32x4 yv = *reinterpret_cast<const f32x4*>(Yt + srow * kTS + c + 4 * kq);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          wacc = __builtin_amdgcn_mfma_f32_16x16x4f32(tv[u], yv[u], wacc, 0, 0, 0);
-          oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[u], yv[u], oacc, 0, 0, 0);
+      for (int c = 0; c < 4; ++c) {
+        if (c <= wave) {
+          const f32x4 yv = *reinterpret_cast<const f32x4*>(Yt + srow * kTS + 16 * c + 4 * kq);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            wacc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.t[c][u], yv[u], wacc, 0, 0, 0);
+            oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.pt[c][u], yv[u], oacc, 0, 0, 0);
+          }
         }
       }
       *reinterpret_cast<f32x4*>(Wt + srow * kTS + tb) = wacc;
@@ -727,8 +831,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
         for (int u = 0; u < 8; ++u) {
           at[u] = Av[t0 + u];
 #pragma unroll
-          for (int m = 0; m < kNCH; ++m)
-            kk[u][m] = *reinterpret_cast<const f32x4*>(Kl + (t0 + u) * kKS + 4 * (li + kLPR * m));
+          for (int m = 0; m < kNCH; ++m) kk[u][m] = k4_at<BF>(lds, t0 + u, 4 * (li + kLPR * m));
         }
         const int un = min(8, n - t0);
 #pragma unroll
@@ -750,31 +853,87 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
       }
     } else {
       // 4. State at the chunk end only: S_C = g_{n-1} S_0 + sum_t G[n-1][t]
-      //    w_t k_t^T on the matrix cores (16x16x4 f32 MFMA; wave w takes
-      //    columns [32 w, 32 w + 32)), every operand read before the first
-      //    product; written over S_0 and read back into the lanes' registers.
-      f32x4 wv[4];
-      float k0[4][4], k1[4][4];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int tq = 16 * q4 + 4 * kq;
-        const f32x4 gc = *reinterpret_cast<const f32x4*>(GC + tq);
-        const f32x4 w4 = *reinterpret_cast<const f32x4*>(Wt + srow * kTS + tq);
-        wv[q4] = f32x4{gc.x * w4.x, gc.y * w4.y, gc.z * w4.z, gc.w * w4.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float* krow = Kl + (tq + u) * kKS + 32 * wave + srow;
-          k0[q4][u] = krow[0];
-          k1[q4][u] = krow[16];
-        }
-      }
+      //    w_t k_t^T on the matrix cores (wave w takes columns [32 w, 32 w +
+      //    32)), every operand read before the first product; written over
+      //    S_0 and read back into the lanes' registers. bf16 inputs: the f32
+      //    factors G[n-1][t] w_t as three bf16 parts against bf16 k (16x16x32
+      //    MFMA, exact products); f32 inputs: 16x16x4 f32 MFMA.
       f32x4 d0 = {}, d1 = {};
+      if constexpr (BF) {
+        bf16x8 ah[2], am[2], al[2], b0[2], b1[2];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const int t8 = 32 * c2 + 8 * kq;
+          const f32x4 g0 = *reinterpret_cast<const f32x4*>(GC + t8);
+          const f32x4 g1 = *reinterpret_cast<const f32x4*>(GC + t8 + 4);
+          const f32x4 w0 = *reinterpret_cast<const f32x4*>(Wt + srow * kTS + t8);
+          const f32x4 w1 = *reinterpret_cast<const f32x4*>(Wt + srow * kTS + t8 + 4);
+          uint32_t hp[8], mp[8], lp[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            split3(g0[e] * w0[e], hp[e], mp[e], lp[e]);
+            split3(g1[e] * w1[e], hp[e + 4], mp[e + 4], lp[e + 4]);
+          }
+          u32x4 kb0, kb1;
+          uint32_t kv0[8], kv1[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const char* kr = lds + L::K + (t8 + e) * L::kKRow + 2 * (32 * wave + srow);
+            kv0[e] = *reinterpret_cast<const uint16_t*>(kr);
+            kv1[e] = *reinterpret_cast<const uint16_t*>(kr + 32);
+          }
+          u32x4 hh, mm, ll;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hh[e] = hp[2 * e] | (hp[2 * e + 1] << 16);
+            mm[e] = mp[2 * e] | (mp[2 * e + 1] << 16);
+            ll[e] = lp[2 * e] | (lp[2 * e + 1] << 16);
+            kb0[e] = kv0[2 * e] | (kv0[2 * e + 1] << 16);
+            kb1[e] = kv1[2 * e] | (kv1[2 * e + 1] << 16);
+          }
+          ah[c2] = __builtin_bit_cast(bf16x8, hh);
+          am[c2] = __builtin_bit_cast(bf16x8, mm);
+          al[c2] = __builtin_bit_cast(bf16x8, ll);
+          b0[c2] = __builtin_bit_cast(bf16x8, kb0);
+          b1[c2] = __builtin_bit_cast(bf16x8, kb1);
+        }
+        f32x4 d0m = {}, d0l = {}, d1m = {}, d1l = {};
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[c2], b0[c2], d0, 0, 0, 0);
+          d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[c2], b1[c2], d1, 0, 0, 0);
+          d0m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[c2], b0[c2], d0m, 0, 0, 0);
+          d1m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[c2], b1[c2], d1m, 0, 0, 0);
+          d0l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[c2], b0[c2], d0l, 0, 0, 0);
+          d1l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[c2], b1[c2], d1l, 0, 0, 0);
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[q4][u], k0[q4][u], d0, 0, 0, 0);
-          d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[q4][u], k1[q4][u], d1, 0, 0, 0);
+          d0[u] = (d0l[u] + d0m[u]) + d0[u];
+          d1[u] = (d1l[u] + d1m[u]) + d1[u];
+        }
+      } else {
+        f32x4 wv[4];
+        float k0[4][4], k1[4][4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int tq = 16 * q4 + 4 * kq;
+          const f32x4 gc = *reinterpret_cast<const f32x4*>(GC + tq);
+          const f32x4 w4 = *reinterpret_cast<const f32x4*>(Wt + srow * kTS + tq);
+          wv[q4] = f32x4{gc.x * w4.x, gc.y * w4.y, gc.z * w4.z, gc.w * w4.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            k0[q4][u] = k_at<BF>(lds, tq + u, 32 * wave + srow);
+            k1[q4][u] = k_at<BF>(lds, tq + u, 32 * wave + srow + 16);
+          }
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[q4][u], k0[q4][u], d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[q4][u], k1[q4][u], d1, 0, 0, 0);
+          }
         }
       }
       const float gn = Gv[n - 1];
@@ -800,12 +959,13 @@ template <typename TIn, bool CAPTURE, bool LOGG>
 hipError_t launch_seq(const ChunkArgs& args, const float* ws, int chunk0, int n_seg, const float* init,
                       size_t init_rstride, bool out_bf16, hipStream_t s) {
   const int blocks = args.n_req * args.n_vheads * kRowBlocks;
+  constexpr size_t lds = SeqLds<sizeof(TIn) == 2>::BYTES;
   if (out_bf16)
-    hipLaunchKernelGGL((gdn_chunked_kernel<TIn, CAPTURE, LOGG, true>), dim3(blocks), dim3(kThreads), kLdsBytes, s,
-                       args, ws, chunk0, n_seg, init, init_rstride);
+    hipLaunchKernelGGL((gdn_chunked_kernel<TIn, CAPTURE, LOGG, true>), dim3(blocks), dim3(kThreads), lds, s, args,
+                       ws, chunk0, n_seg, init, init_rstride);
   else
-    hipLaunchKernelGGL((gdn_chunked_kernel<TIn, CAPTURE, LOGG, false>), dim3(blocks), dim3(kThreads), kLdsBytes, s,
-                       args, ws, chunk0, n_seg, init, init_rstride);
+    hipLaunchKernelGGL((gdn_chunked_kernel<TIn, CAPTURE, LOGG, false>), dim3(blocks), dim3(kThreads), lds, s, args,
+                       ws, chunk0, n_seg, init, init_rstride);
   return launch_error();
 }
 

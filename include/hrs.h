@@ -217,9 +217,9 @@ typedef struct {
 } hrs_chunked_desc;
 
 /* Bytes of device workspace gdn_span_chunked needs for this descriptor:
- * n_req x n_vheads x min(ceil(n_pos / 64), 32) x 33,280 (one record of T,
+ * n_req x n_vheads x min(ceil(n_pos / 64), 32) x 20,992 (one record of T,
  * P T and the decays per request, value head and chunk of a 32-chunk
- * segment; 34 MB for one request of 32 heads at any length from 2,048
+ * segment; 21.5 MB for one request of 32 heads at any length from 2,048
  * positions). 0 for a NULL descriptor or sizes out of range. */
 size_t gdn_span_chunked_workspace_bytes(const hrs_chunked_desc* desc);
 

@@ -419,9 +419,9 @@ def test_chunked_entry_rejections():
     assert call(dk=64, dv=64) == E.HRS_EUNSUPPORTED
     assert call(ws=None) == E.HRS_EINVAL
     assert call(ws_bytes=0) == E.HRS_EINVAL
-    assert call(ws_bytes=1 * 4 * 4 * 33280 - 1) == E.HRS_EINVAL
+    assert call(ws_bytes=1 * 4 * 4 * 20992 - 1) == E.HRS_EINVAL
     assert call(ws=MIS) == E.HRS_EALIGN
-    assert call(ws_bytes=1 * 4 * 4 * 33280) == E.HRS_EDEVICE
+    assert call(ws_bytes=1 * 4 * 4 * 20992) == E.HRS_EDEVICE
     assert call(n_pos=(1 << 20)) == E.HRS_EDEVICE
     assert call(ckpt=FAKE, out_dt=hrs.HRS_BF16, log_gates=1) == E.HRS_EDEVICE
     assert call() == E.HRS_EDEVICE
