@@ -157,28 +157,32 @@ __global__ __launch_bounds__(64) void accept_walk_kernel(const AcceptArgs args) 
   __shared__ int32_t depth[HRS_MAX_POS];
   __shared__ int32_t matched[HRS_MAX_POS];
   __shared__ int32_t len_s;
-  // Everything the walk reads is gathered first, by all lanes at once: the
-  // row's chunk keys (maximum per row in LDS), the draft tokens and the
-  // parents; the walk itself then touches LDS only.
-  if (lane < T_) {
-    const int32_t tk = args.tokens[static_cast<size_t>(r) * T_ + lane];
-    const int32_t pr = args.tree ? args.parent[rl * T_ + lane] : lane - 1;
-    row_key[lane] = 0;
-    tok[lane] = tk;
-    par[lane] = pr;
-  }
-  __syncthreads();
+  // Everything the walk reads is loaded first, by all lanes at once and in
+  // one round trip to memory: the row's chunk keys (eight per lane, from
+  // clamped indices), the draft tokens and the parents; the walk itself then
+  // touches LDS only.
   const int n_keys = T_ * args.n_chunks;
   const uint64_t* k = args.keys + static_cast<size_t>(r) * n_keys;
-  // Eight keys per lane are loaded (unconditionally, from clamped indices)
-  // before the LDS maxima take them, so their latencies overlap.
-  for (int i0 = lane; i0 < n_keys; i0 += 64 * 8) {
+  const int tl = min(lane, T_ - 1);
+  const int32_t tk = args.tokens[static_cast<size_t>(r) * T_ + tl];
+  const int32_t pr = args.tree ? args.parent[rl * T_ + tl] : tl - 1;
+  for (int i0 = 0; i0 < n_keys; i0 += 64 * 8) {
     uint64_t kv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kv[j] = k[min(i0 + 64 * j, n_keys - 1)];
+    for (int j = 0; j < 8; ++j) kv[j] = k[min(i0 + lane + 64 * j, n_keys - 1)];
+    if (i0 == 0) {
+      if (lane < T_) {
+        row_key[lane] = 0;
+        tok[lane] = tk;
+        par[lane] = pr;
+      }
+      __syncthreads();
+    }
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (i0 + 64 * j < n_keys) atomicMax(&row_key[(i0 + 64 * j) / args.n_chunks], static_cast<unsigned long long>(kv[j]));
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + lane + 64 * j;
+      if (i < n_keys) atomicMax(&row_key[i / args.n_chunks], static_cast<unsigned long long>(kv[j]));
+    }
   }
   __syncthreads();
   if (lane < T_) {
@@ -187,6 +191,21 @@ __global__ __launch_bounds__(64) void accept_walk_kernel(const AcceptArgs args) 
     args.argmax[static_cast<size_t>(r) * T_ + lane] = idx;
   }
   __syncthreads();
+  if (!args.tree) {
+    // Chain: position t is accepted when every position 1..t matches, i.e.
+    // draft token t equals the argmax at t - 1; the accepted length is the
+    // run of matches from position 1 (one ballot), the path 0..len.
+    const bool m = lane >= 1 && lane < T_ && tok[lane] == am[lane - 1];
+    const uint64_t mask = __ballot(m);
+    const int len = __builtin_ctzll(~(mask >> 1));
+    if (lane == 0) {
+      args.accept_node[r] = len;
+      args.accept_len[r] = len;
+      args.bonus[r] = am[len];
+    }
+    if (lane < T_) args.path[static_cast<size_t>(r) * T_ + lane] = lane <= len ? lane : -1;
+    return;
+  }
   if (lane == 0) {
     matched[0] = 1;
     depth[0] = 0;
