@@ -317,7 +317,13 @@ def gdn_launch_stats(step, stream, L: int, K: int) -> dict:
       region is not used for the step time. Average and median per launch.
     * Phase split: one step with events between its phases.
     * Per stack: the step's L GDN spans back to back with no other kernel
-      between them (launch gaps included), event-timed, median of 3."""
+      between them (launch gaps included), event-timed, median of 3.
+    * In the step: the L (conv, GDN) layer pairs back to back minus the L
+      conv spans back to back, per layer (event-timed stacks, median of 3):
+      the GDN span's share of the step's layer time. (Events recorded by a
+      dispatch that follows a different kernel open before that kernel has
+      finished, so the per-launch events above overstate a span that
+      follows a conv; these differences of stacks do not.)"""
     import torch
     import hybrid_recurrent_state_amd as hrs
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
@@ -349,19 +355,23 @@ def gdn_launch_stats(step, stream, L: int, K: int) -> dict:
     phases = {"conv+gdn": ph[0].elapsed_time(ph[1]), "accept": ph[1].elapsed_time(ph[2]),
               "rollback": ph[2].elapsed_time(ph[3]), "ring": ph[3].elapsed_time(ph[4])}
 
-    stack = []
-    for _ in range(3):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for l in range(L):
-            step.launch_gdn(l, h)
-        e1.record()
-        torch.cuda.synchronize()
-        stack.append(e0.elapsed_time(e1) / L)
+    def stack_of(launch) -> float:
+        out = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for l in range(L):
+                launch(l)
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) / L)
+        return float(np.median(out))
+
+    stack = [stack_of(lambda l: step.launch_gdn(l, h))]
+    layer_stack = stack_of(lambda l: step.launch_layer(l, h))
+    conv_stack = stack_of(lambda l: step.launch_conv(l, h))
     # The same span-only stacks with every dispatch timing itself: the
-    # kernel's duration when the previous kernel is the same one. (On this
-    # GPU a kernel that follows a different kernel takes 1-2.5 us longer, the
-    # same for a plain store stream: in the step each span follows a conv.)
+    # kernel's duration when the previous kernel is the same one.
     so = []
     reps = max(1, min(K, 10))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
@@ -376,7 +386,8 @@ def gdn_launch_stats(step, stream, L: int, K: int) -> dict:
     return {"avg_s": float(gdn_ms.mean()) / 1e3, "median_s": float(np.median(gdn_ms)) / 1e3,
             "min_s": float(gdn_ms.min()) / 1e3, "stack_s": float(np.median(stack)) / 1e3, "phases": phases,
             "span_only_avg_s": float(so.mean()) / 1e3, "span_only_median_s": float(np.median(so)) / 1e3,
-            "t_events": (t2, t3)}
+            "layer_stack_s": layer_stack / 1e3, "conv_stack_s": conv_stack / 1e3,
+            "in_step_span_s": (layer_stack - conv_stack) / 1e3, "t_events": (t2, t3)}
 
 
 def measure_workload(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
@@ -417,6 +428,9 @@ def measure_workload(name: str, steps: int, warmup: int, cpu_seconds: float) -> 
            "span_only_launch_avg_us": gs["span_only_avg_s"] * 1e6,
            "span_only_launch_median_us": gs["span_only_median_s"] * 1e6,
            "span_only_frac": nbytes / gs["span_only_avg_s"] / 1e9 / HBM_PEAK_GBS,
+           "in_step_span_us": gs["in_step_span_s"] * 1e6,
+           "in_step_span_frac": nbytes / gs["in_step_span_s"] / 1e9 / HBM_PEAK_GBS,
+           "layer_stack_us": gs["layer_stack_s"] * 1e6, "conv_stack_us": gs["conv_stack_s"] * 1e6,
            "traffic": measured_traffic(name), "phases_ms": gs["phases"]}
     # The NEXT-row steps on the same buffers: f3 (the step as one graph), f2
     # (zero-copy rollback), f1 (fused layers) and their graph replays.
@@ -439,7 +453,8 @@ def measure_workload(name: str, steps: int, warmup: int, cpu_seconds: float) -> 
     log(f"  next rows {nxt}")
     log(f"  step {ms:.3f} ms, gdn launch avg {rec['avg_launch_us']:.2f} us (frac {rec['frac']:.3f}), "
         f"stack {rec['stack_us_per_layer']:.2f} us (frac {rec['stack_frac']:.3f}), span-only launches avg "
-        f"{rec['span_only_launch_avg_us']:.2f} us (frac {rec['span_only_frac']:.3f})")
+        f"{rec['span_only_launch_avg_us']:.2f} us (frac {rec['span_only_frac']:.3f}), in the step "
+        f"{rec['in_step_span_us']:.2f} us (frac {rec['in_step_span_frac']:.3f})")
     del step, bufs
     torch.cuda.empty_cache()
     if cpu_seconds > 0:
@@ -522,7 +537,8 @@ def main():
     store_gbs = store_stream_gbs()
     log(f"store-stream reference {store_gbs:.0f} GB/s")
     log(f"step {ms_per_step:.3f} ms (with GDN events {(t3 - t2) * 1e3 / K:.3f} ms); gdn launch avg "
-        f"{gdn_avg_s * 1e6:.1f} us = {achieved:.0f} GB/s; traffic {traffic}; phases {phases}")
+        f"{gdn_avg_s * 1e6:.1f} us = {achieved:.0f} GB/s; in the step (layer stack - conv stack) "
+        f"{gs['in_step_span_s'] * 1e6:.1f} us; traffic {traffic}; phases {phases}")
 
     next_rows = None
     if not args.no_next:
@@ -590,6 +606,9 @@ def main():
                 "span_only_launch_avg_us": gs["span_only_avg_s"] * 1e6,
                 "span_only_launch_median_us": gs["span_only_median_s"] * 1e6,
                 "span_only_frac": gdn_bytes / gs["span_only_avg_s"] / 1e9 / HBM_PEAK_GBS,
+                "in_step_span_us": gs["in_step_span_s"] * 1e6,
+                "in_step_span_frac": gdn_bytes / gs["in_step_span_s"] / 1e9 / HBM_PEAK_GBS,
+                "layer_stack_us": gs["layer_stack_s"] * 1e6, "conv_stack_us": gs["conv_stack_s"] * 1e6,
                 "traffic": traffic, "phases_ms": phases}
     cpu = None
     if not args.no_cpu_baseline:
@@ -639,7 +658,9 @@ def main():
                      "stack_us_per_layer": stack_s * 1e6,
                      "stack_frac": gdn_bytes / stack_s / 1e9 / HBM_PEAK_GBS,
                      "span_only_launch_avg_us": gs["span_only_avg_s"] * 1e6,
-                     "span_only_frac": gdn_bytes / gs["span_only_avg_s"] / 1e9 / HBM_PEAK_GBS},
+                     "span_only_frac": gdn_bytes / gs["span_only_avg_s"] / 1e9 / HBM_PEAK_GBS,
+                     "in_step_span_us": gs["in_step_span_s"] * 1e6,
+                     "in_step_span_frac": gdn_bytes / gs["in_step_span_s"] / 1e9 / HBM_PEAK_GBS},
         "gdn_tokens_per_s_per_layer": R * T / gdn_avg_s,
         "draft_tokens_per_s_per_layer": R * (T - 1) * L / (ms_per_step / 1e3),
         "phases_ms": phases,
