@@ -641,17 +641,19 @@ __device__ __forceinline__ void run_positions(const float* buf, f32x4* stash, f3
 
 // Producer staging of one item (a window of positions of one unit) into buf,
 // by NTH threads (p = index among them); at a unit's first window also its
-// initial state rows and the valid flag. ONE_WAIT: the state-row and gate
-// loads are issued before the input loads and all are written afterwards, so
-// the thread waits for memory once; otherwise each part waits in turn.
-template <int DK, int NTH, int RPB, int POS_FLOATS, typename TIn, bool FUSED, bool ONE_WAIT>
+// initial state rows and the valid flag, unless STATE is false (the block's
+// first item, whose rows the consumers load themselves). ONE_WAIT: the
+// state-row and gate loads are issued before the input loads and all are
+// written afterwards, so the thread waits for memory once; otherwise each
+// part waits in turn.
+template <int DK, int NTH, int RPB, int POS_FLOATS, typename TIn, bool FUSED, bool ONE_WAIT, bool STATE = true>
 __device__ __forceinline__ void produce_item(const GdnArgs& args, const Hot& hs, float* buf, float* state_lds,
                                              int* flag_lds, const Unit& u, int t0, int tn, int p) {
   constexpr int N4 = RPB * DK / 4;   // float4 chunks of a unit's state rows
   constexpr int SPT = (N4 + NTH - 1) / NTH;
   static_assert(kWindow <= NTH, "one gate pair per staging thread");
   const int T = hs.n_pos;
-  const float* init = t0 == 0 ? initial_rows<DK>(args, hs, u) : nullptr;
+  const float* init = (STATE && t0 == 0) ? initial_rows<DK>(args, hs, u) : nullptr;
   if constexpr (ONE_WAIT) {
     const TIn* ag = static_cast<const TIn*>(hs.a);
     const TIn* bg = static_cast<const TIn*>(hs.b);
@@ -687,7 +689,7 @@ __device__ __forceinline__ void produce_item(const GdnArgs& args, const Hot& hs,
     }
     stage_window<DK, NTH, RPB, POS_FLOATS, TIn, false, FUSED>(args, hs, buf, u, t0, tn, p);
   }
-  if (t0 == 0 && p == 0) flag_lds[0] = init != nullptr;
+  if (STATE && t0 == 0 && p == 0) flag_lds[0] = init != nullptr;
 }
 
 // NW waves own the unit's rows (the consumers). NP == 0: the same waves also
@@ -799,9 +801,22 @@ __global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const voi
     // block of a launch holds at least one unit (the grid never has more
     // blocks than units), so item 0 is staged straight from the preloaded
     // arguments, before anything waits for the rest of the argument block.
-    produce_item<DK, (NW + NP) * 64, RPB, POS_FLOATS, TIn, FUSED, true>(args, hs, lds, state_lds, flag_lds,
-                                                                        unit_of(hs, blockIdx.x, RPB), 0,
-                                                                        min(kWindow, T), tid);
+    // The consumers load the first unit's state rows straight into their
+    // registers in the same round of loads (no trip through LDS, and no
+    // barrier for them before the first position).
+    const Unit u0 = unit_of(hs, blockIdx.x, RPB);
+    bool valid0 = false;
+    if (consumer) {
+      const float* init0 = initial_rows<DK>(args, hs, u0);
+      valid0 = init0 != nullptr;
+      if (valid0) {
+#pragma unroll
+        for (int m = 0; m < NCH; ++m)
+          s[m] = *reinterpret_cast<const f32x4*>(init0 + static_cast<size_t>(row_blk) * DK + 4 * (li + LPR * m));
+      }
+    }
+    produce_item<DK, (NW + NP) * 64, RPB, POS_FLOATS, TIn, FUSED, true, false>(args, hs, lds, state_lds, flag_lds,
+                                                                               u0, 0, min(kWindow, T), tid);
     __syncthreads();
     auto item_unit = [&](int i) { return unit_of(hs, blockIdx.x + (i / nwin) * args.n_blocks, RPB); };
     const int n_my = (args.n_units - 1 - static_cast<int>(blockIdx.x)) / args.n_blocks + 1;
@@ -813,8 +828,8 @@ __global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const voi
       const int j = i % nwin;
       if (consumer && j == 0) {
         const Unit u = unit_of(hs, blockIdx.x + (i / nwin) * args.n_blocks, RPB);
-        valid = flag_lds[0] != 0;
-        if (valid) {
+        valid = i == 0 ? valid0 : flag_lds[0] != 0;
+        if (valid && i > 0) {
 #pragma unroll
           for (int m = 0; m < NCH; ++m)
             s[m] = *reinterpret_cast<const f32x4*>(state_lds + row_blk * DK + 4 * (li + LPR * m));
@@ -822,7 +837,9 @@ __global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const voi
         ckpt_row0 = ckpt_of(u);
         out_r = out_of(u);
       }
-      __syncthreads();  // the state rows and flag are read: producers may replace them
+      // The state rows and flag are read: producers may replace them (the
+      // first item's rows came from memory, so it needs no barrier here).
+      if (i > 0) __syncthreads();
       if (consumer) {
         if (valid) {
           const int t0 = j * kWindow;
