@@ -252,6 +252,40 @@ __device__ __forceinline__ void stage_plain(const GdnArgs& args, const Hot& hs, 
   }
 }
 
+// Sixteen consecutive elements as loaded (bf16 bits or f32; the source must
+// be 16-byte aligned), widened one at a time where they are used: the raw
+// form of bf16 takes half the registers of f32.
+template <typename TIn> struct Raw16;
+template <> struct Raw16<uint16_t> {
+  u32x4 v[2];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    v[0] = reinterpret_cast<const u32x4*>(p)[0];
+    v[1] = reinterpret_cast<const u32x4*>(p)[1];
+  }
+  __device__ __forceinline__ float at(int c) const {
+    const uint32_t w = v[c >> 3][(c >> 1) & 3];
+    return (c & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+};
+template <> struct Raw16<float> {
+  f32x4 v[4];
+  __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = reinterpret_cast<const f32x4*>(p)[i];
+  }
+  __device__ __forceinline__ float at(int c) const { return v[c >> 2][c & 3]; }
+};
+
+// SiLU z / (1 + e^-z) from the hardware base-2 exponential and reciprocal:
+// e^-z = 2^(-z log2 e); a few ulp from the correctly rounded value (large
+// negative z gives -0 through 1 / inf, large positive z gives z). Both
+// fused launch shapes use it, so a request's results do not depend on how
+// many requests share its launch.
+__device__ __forceinline__ float silu_fast(float z) {
+  const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // Staging, fused layer: for every staged position, the conv (and SiLU) of
 // the unit's channels, written where the plain staging puts q, k and v: q
 // and k of key head g scaled to unit L2 norm (q also by q_scale), and the
@@ -295,7 +329,7 @@ __device__ __forceinline__ void stage_fused(const GdnArgs& args, const Hot& hs, 
       dst = buf + tt * POS_FLOATS + 2 * DK + (i % VI) * CPI;
     }
     const int t = t0 + tt;
-    float win[4][CPI];
+    Raw16<TIn> win[4];
 #pragma unroll
     for (int m = 0; m < 3; ++m) {
       int src;
@@ -307,20 +341,20 @@ __device__ __forceinline__ void stage_fused(const GdnArgs& args, const Hot& hs, 
       }
       const TIn* ptr = src >= 0 ? x + (static_cast<size_t>(u.r) * T + src) * C + ch
                                 : cs + (static_cast<size_t>(u.r) * 3 + (-1 - src)) * C + ch;
-      load16<TIn>(ptr, win[m]);
+      win[m].load(ptr);
     }
-    load16<TIn>(x + (static_cast<size_t>(u.r) * T + t) * C + ch, win[3]);
-    float w[4 * CPI];
+    win[3].load(x + (static_cast<size_t>(u.r) * T + t) * C + ch);
+    Raw16<TIn> w[4];   // w[c][m] is element 4 c + m of the 64 weights
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load16<TIn>(wc + static_cast<size_t>(ch) * 4 + CPI * i, w + CPI * i);
+    for (int i = 0; i < 4; ++i) w[i].load(wc + static_cast<size_t>(ch) * 4 + CPI * i);
     float y[CPI];
     float ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPI; ++c) {
-      float acc = w[c * 4] * win[0][c];
+      float acc = w[c >> 2].at(4 * (c & 3)) * win[0].at(c);
 #pragma unroll
-      for (int m = 1; m < 4; ++m) acc = __builtin_fmaf(w[c * 4 + m], win[m][c], acc);
-      y[c] = args.silu ? acc / (1.0f + expf(-acc)) : acc;
+      for (int m = 1; m < 4; ++m) acc = __builtin_fmaf(w[c >> 2].at(4 * (c & 3) + m), win[m].at(c), acc);
+      y[c] = args.silu ? silu_fast(acc) : acc;
       ss = __builtin_fmaf(y[c], y[c], ss);
     }
     if (part < 2) {
