@@ -83,12 +83,14 @@ def test_chunked_long_span(hrs):
     check(units, ck, out, state, False, what="T=1000")
 
 
-@pytest.mark.parametrize("T,capture,Hv", [(2048, False, 8), (2100, False, 2), (2113, True, 1)])
-def test_chunked_spans_over_several_segments(hrs, T, capture, Hv):
+@pytest.mark.parametrize("T,capture,Hv,dt", [(2048, False, 8, BF16), (2100, False, 2, BF16), (2113, True, 1, BF16),
+                                             (2070, False, 2, F32)])
+def test_chunked_spans_over_several_segments(hrs, T, capture, Hv, dt):
     """More than 32 chunks: the pre-pass records of the second segment
     overwrite the first's in the workspace, and the second segment starts
-    from the state the first left (in place, or the checkpoint before it)."""
-    w = scaled(QWEN_LAYER_CHAIN, n_req=2 if capture else 1, n_pos=T, n_kheads=1, n_vheads=Hv)
+    from the state the first left (in place, or the checkpoint before it);
+    bf16 inputs (bf16 products against the split state) and f32 inputs."""
+    w = scaled(QWEN_LAYER_CHAIN, n_req=2 if capture else 1, n_pos=T, n_kheads=1, n_vheads=Hv, dtype=dt)
     units = [gen_unit(w, 0, r) for r in range(w.n_req)]
     say(f"chunked segments T={T} capture={capture}")
     ck, out, state = run(hrs, units, capture)
@@ -162,6 +164,28 @@ def test_chunked_log_gates(hrs):
         e1 = assert_tiles(ck[r], ock, 2, f"log gates ckpt r={r}")
         e2 = assert_tiles(o[r], oout, 1, f"log gates out r={r}")
         say(f"log gates r={r}: ckpt err {e1:.2e}, out err {e2:.2e}")
+
+
+def test_chunked_log_gates_over_two_segments_with_capture(hrs):
+    """Log-space gates with every state captured over 2,100 positions (two
+    segments): the second segment starts from the checkpoint before it."""
+    import torch
+    from synth import bf16_to_f32
+    w = scaled(QWEN_LAYER_CHAIN, n_req=1, n_pos=2100, n_kheads=1, n_vheads=1)
+    u = gen_unit(w, 0, 0)
+    g = np.log(bf16_to_f32(u.a).astype(np.float64))
+    u.a = bf16_bits(g.astype(np.float32))
+    st = lambda name: to_torch(np.stack([getattr(u, name)]))
+    q, k, v, gl, b, state = st("q"), st("k"), st("v"), st("a"), st("b"), st("state")
+    ckpt = torch.full((1, 2100, 1, 128, 128), float("nan"), device="cuda")
+    out = torch.full((1, 2100, 1, 128), float("nan"), device="cuda")
+    hrs.gdn_span_chunked(q, k, v, gl, b, state, ckpt, out, workspace(hrs, q, v), log_gates=True)
+    torch.cuda.synchronize()
+    a64 = np.exp(bf16_to_f32(u.a).astype(np.float64))
+    ock, oout = ogdn.gdn_span(u.state, u.q, u.k, u.v, a64, u.b, None, 1.0)
+    e1 = assert_tiles(to_numpy(ckpt)[0], ock, 2, "log gates, two segments, ckpt")
+    e2 = assert_tiles(to_numpy(out)[0], oout, 1, "log gates, two segments, out")
+    say(f"log gates two segments: ckpt err {e1:.2e}, out err {e2:.2e}")
 
 
 def test_chunked_bf16_outputs(hrs):
