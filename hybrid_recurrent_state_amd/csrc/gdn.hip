@@ -451,6 +451,97 @@ __device__ __forceinline__ void store_ckpt_rows(float* dst, const f32x4 (&s)[NCH
                                            0, kNtSc1);
 }
 
+// An address that every lane of the wave holds alike, as a wave-uniform
+// value (scalar registers), so that advancing it is scalar work.
+__device__ __forceinline__ uintptr_t wave_uniform(uintptr_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uintptr_t>(hi) << 32) | lo;
+}
+
+// A raw-buffer offset past every resource here: an access there is dropped.
+constexpr uint32_t kDroppedOffset = 0x80000000u;
+
+// The per-position stores of a wave in the tree loop, through raw buffer
+// resources whose base is wave-uniform and advances by a scalar add per
+// position (the lane offsets are loop invariant): the checkpoint rows of
+// one position, with the streaming bit alone (nt; the device-scope bit of
+// the chain loops measured 4% slower on the one-request tree), and the rows'
+// outputs, stored by the first lane of each row (the other lanes' offset
+// lies past the resource, where the hardware drops the write, so no lane
+// mask is needed; in the 16-request chain loop, all 16 lanes of a row
+// storing its value measured 6% slower).
+template <int DK>
+struct TreeStores {
+  static constexpr int LPR = kLanesPerRow;
+  static constexpr int RPW = 64 / LPR;
+  static constexpr int NCH = DK / (4 * LPR);
+  float* ckpt;          // the wave's first checkpoint row at the current position
+  float* out;           // the wave's first output at the current position
+  size_t ckpt_step;     // floats between positions
+  int out_step;
+  uint32_t ckpt_off;    // this lane's byte offset in the wave's checkpoint rows
+  uint32_t out_off;     // this lane's row's byte offset in the wave's outputs (first lane of a row)
+
+  // ckpt_row0 and out_r: this lane's row at position 0 of the unit
+  // (ckpt_row0 may be null: then store_ckpt is never called).
+  __device__ __forceinline__ TreeStores(float* ckpt_row0, float* out_r, int t0, size_t pos_stride, int out_stride,
+                                        int lane) {
+    const int rw = lane / LPR;
+    const int li = lane % LPR;
+    ckpt = reinterpret_cast<float*>(
+        wave_uniform(reinterpret_cast<uintptr_t>(ckpt_row0) - static_cast<uintptr_t>(rw) * DK * sizeof(float) +
+                     static_cast<uintptr_t>(t0) * pos_stride * sizeof(float)));
+    out = reinterpret_cast<float*>(
+        wave_uniform(reinterpret_cast<uintptr_t>(out_r - rw + static_cast<size_t>(t0) * out_stride)));
+    ckpt_step = pos_stride;
+    out_step = out_stride;
+    ckpt_off = static_cast<uint32_t>((rw * DK + 4 * li) * 4);
+    out_off = li == 0 ? static_cast<uint32_t>(rw * 4) : kDroppedOffset;
+  }
+  __device__ __forceinline__ void store_ckpt(const f32x4 (&s)[NCH]) {
+    constexpr int kNt = 2;   // cache-policy bit of the store: nt
+    // Raw buffer (stride 0) of RPW rows; the third dword's data format is 32 bits.
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(ckpt, 0, RPW * DK * 4, 0x00020000);
+#pragma unroll
+    for (int m = 0; m < NCH; ++m)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), rsrc, ckpt_off + m * LPR * 16, 0, kNt);
+    ckpt += ckpt_step;
+  }
+  __device__ __forceinline__ void store_out(float o) {
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(out, 0, RPW * 4, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), rsrc, out_off, 0, 0);
+    out += out_step;
+  }
+};
+
+// One row of S times x (k or q), in every lane of the row: each lane's
+// float4 chunks in turn, then a butterfly over the row's 16 lanes.
+template <int NCH>
+__device__ __forceinline__ float row_dot(const f32x4 (&s)[NCH], const f32x4 (&x)[NCH]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int m = 0; m < NCH; ++m) {
+    acc = __builtin_fmaf(s[m].x, x[m].x, acc);
+    acc = __builtin_fmaf(s[m].y, x[m].y, acc);
+    acc = __builtin_fmaf(s[m].z, x[m].z, acc);
+    acc = __builtin_fmaf(s[m].w, x[m].w, acc);
+  }
+  return group_sum<kLanesPerRow>(acc);
+}
+
+// S <- a S + c k^T on this lane's columns of its row.
+template <int NCH>
+__device__ __forceinline__ void update_row(f32x4 (&s)[NCH], const f32x4 (&k)[NCH], float a, float c) {
+#pragma unroll
+  for (int m = 0; m < NCH; ++m) {
+    s[m].x = __builtin_fmaf(c, k[m].x, a * s[m].x);
+    s[m].y = __builtin_fmaf(c, k[m].y, a * s[m].y);
+    s[m].z = __builtin_fmaf(c, k[m].z, a * s[m].z);
+    s[m].w = __builtin_fmaf(c, k[m].w, a * s[m].w);
+  }
+}
+
 // Positions [t0, t0 + tn) of one unit, for the consumer threads: S rows in
 // VGPRs, staged inputs from LDS, checkpoint and output stores. No barrier and
 // (without RELOAD) no vector-memory load.
@@ -465,40 +556,40 @@ __device__ __forceinline__ void run_positions(const float* buf, f32x4* stash, f3
   const int li = lane % LPR;
   const int row_blk = (tid >> 6) * (64 / LPR) + lane / LPR;
   if constexpr (TREE) {
-    // Tree spans (single-role blocks): the staged inputs of a position are
-    // read from LDS one position ahead, into registers, so their LDS latency
-    // overlaps the previous position (4% faster on 16 requests; the chain
-    // kernel, whose producer waves share the SIMDs, measured 6% slower).
-    f32x4 kn[NCH], qn[NCH];
-    float an = 0.0f, bn = 0.0f, vn = 0.0f;
-    int cn = 0;
-    auto fetch = [&](int tt) {
+    // Tree spans (single-role blocks): each position's inputs are read from
+    // LDS one position ahead (4% faster on 16 requests; the chain kernel,
+    // whose producer waves share the SIMDs, measured 6% slower that way),
+    // into the other of two register sets: the loop is unrolled by two, so
+    // no copies between the sets. With one row-owning wave per SIMD (one
+    // request) this loop was bound by its instruction stream (~8 cycles per
+    // instruction, ~111 instructions and 0.37 us per position); without the
+    // copies and with scalar store addresses, ~85 instructions: 48-layer
+    // span-only stacks 11.6 -> 10.6 us per launch.
+    struct In {
+      f32x4 k[NCH], q[NCH];
+      float a, b, v;
+      int code;    // stash code
+    };
+    TreeStores<DK> st(CAPTURE ? ckpt_row0 : nullptr, out_r, t0, pos_stride, out_stride, lane);
+    auto fetch = [&](int tt, In& d) {
       const float* lp = buf + tt * POS_FLOATS;
 #pragma unroll
       for (int m = 0; m < NCH; ++m) {
-        kn[m] = *reinterpret_cast<const f32x4*>(lp + 4 * (li + LPR * m));
-        qn[m] = *reinterpret_cast<const f32x4*>(lp + DK + 4 * (li + LPR * m));
+        d.k[m] = *reinterpret_cast<const f32x4*>(lp + 4 * (li + LPR * m));
+        d.q[m] = *reinterpret_cast<const f32x4*>(lp + DK + 4 * (li + LPR * m));
       }
-      an = lp[2 * DK + RPB];
-      bn = lp[2 * DK + RPB + 1];
-      vn = lp[2 * DK + row_blk];
-      cn = __builtin_amdgcn_readfirstlane(__float_as_int(lp[2 * DK + RPB + 2]));
+      d.a = lp[2 * DK + RPB];
+      d.b = lp[2 * DK + RPB + 1];
+      d.v = lp[2 * DK + row_blk];
+      d.code = __builtin_amdgcn_readfirstlane(__float_as_int(lp[2 * DK + RPB + 2]));
     };
-    if (tn > 0) fetch(0);
-    for (int tt = 0; tt < tn; ++tt) {
-      const int t = t0 + tt;
-      f32x4 kk[NCH], qq[NCH];
-#pragma unroll
-      for (int m = 0; m < NCH; ++m) { kk[m] = kn[m]; qq[m] = qn[m]; }
-      const float at = an, bt = bn, vt = vn;
-      const int tree_code = cn;
-      if (tt + 1 < tn) fetch(tt + 1);
-      const int rs = static_cast<int8_t>((tree_code >> 8) & 0xFF);
+    auto step = [&](const In& c) {
+      const int rs = static_cast<int8_t>((c.code >> 8) & 0xFF);
       if (rs >= 0) {
 #pragma unroll
         for (int m = 0; m < NCH; ++m) s[m] = stash[(rs * NCH + m) * NTHREADS + tid];
       } else if (RELOAD && rs == kFromGlobal) {
-        const int p = static_cast<int8_t>(tree_code & 0xFF);
+        const int p = static_cast<int8_t>(c.code & 0xFF);
         const float* src = ckpt_row0 + static_cast<size_t>(p) * pos_stride;
 #pragma unroll
         for (int m = 0; m < NCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(src + 4 * (li + LPR * m));
@@ -508,47 +599,26 @@ __device__ __forceinline__ void run_positions(const float* buf, f32x4* stash, f3
         // drain all outstanding checkpoint stores.
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       }
-      float u = 0.0f;
-#pragma unroll
-      for (int m = 0; m < NCH; ++m) {
-        u = __builtin_fmaf(s[m].x, kk[m].x, u);
-        u = __builtin_fmaf(s[m].y, kk[m].y, u);
-        u = __builtin_fmaf(s[m].z, kk[m].z, u);
-        u = __builtin_fmaf(s[m].w, kk[m].w, u);
-      }
-      u = group_sum<LPR>(u);
-      const float c = bt * __builtin_fmaf(-at, u, vt);
-#pragma unroll
-      for (int m = 0; m < NCH; ++m) {
-        s[m].x = __builtin_fmaf(c, kk[m].x, at * s[m].x);
-        s[m].y = __builtin_fmaf(c, kk[m].y, at * s[m].y);
-        s[m].z = __builtin_fmaf(c, kk[m].z, at * s[m].z);
-        s[m].w = __builtin_fmaf(c, kk[m].w, at * s[m].w);
-      }
-      if (CAPTURE) {
-        // Plain streaming stores: the device-scope stores of the chain
-        // loops measured 4% slower on the one-request tree.
-        float* dst = ckpt_row0 + static_cast<size_t>(t) * pos_stride;
-#pragma unroll
-        for (int m = 0; m < NCH; ++m)
-          __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(dst + 4 * (li + LPR * m)));
-      }
-      const int sv = static_cast<int8_t>((tree_code >> 16) & 0xFF);
+      const float u = row_dot<NCH>(s, c.k);
+      update_row<NCH>(s, c.k, c.a, c.b * __builtin_fmaf(-c.a, u, c.v));
+      if (CAPTURE) st.store_ckpt(s);
+      const int sv = static_cast<int8_t>((c.code >> 16) & 0xFF);
       if (sv >= 0) {
 #pragma unroll
         for (int m = 0; m < NCH; ++m) stash[(sv * NCH + m) * NTHREADS + tid] = s[m];
       }
-      float o = 0.0f;
-#pragma unroll
-      for (int m = 0; m < NCH; ++m) {
-        o = __builtin_fmaf(s[m].x, qq[m].x, o);
-        o = __builtin_fmaf(s[m].y, qq[m].y, o);
-        o = __builtin_fmaf(s[m].z, qq[m].z, o);
-        o = __builtin_fmaf(s[m].w, qq[m].w, o);
-      }
-      o = group_sum<LPR>(o);
-      if (li == 0) out_r[static_cast<size_t>(t) * out_stride] = o;
+      st.store_out(row_dot<NCH>(s, c.q));
+    };
+    In A, B;
+    if (tn > 0) fetch(0, A);
+    int tt = 0;
+    for (; tt + 1 < tn; tt += 2) {
+      fetch(tt + 1, B);
+      step(A);
+      fetch(min(tt + 2, tn - 1), A);   // the last pair re-reads its own last position
+      step(B);
     }
+    if (tt < tn) step(A);
   } else if constexpr (NW == 4) {
     // Blocks of one 16-row unit (launches too small to give every CU more
     // than one unit): each SIMD runs one row-owning wave, so the position
