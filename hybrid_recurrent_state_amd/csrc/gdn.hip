@@ -462,17 +462,18 @@ __device__ __forceinline__ uintptr_t wave_uniform(uintptr_t v) {
 // A raw-buffer offset past every resource here: an access there is dropped.
 constexpr uint32_t kDroppedOffset = 0x80000000u;
 
-// The per-position stores of a wave in the tree loop, through raw buffer
-// resources whose base is wave-uniform and advances by a scalar add per
-// position (the lane offsets are loop invariant): the checkpoint rows of
-// one position, with the streaming bit alone (nt; the device-scope bit of
-// the chain loops measured 4% slower on the one-request tree), and the rows'
-// outputs, stored by the first lane of each row (the other lanes' offset
-// lies past the resource, where the hardware drops the write, so no lane
-// mask is needed; in the 16-request chain loop, all 16 lanes of a row
-// storing its value measured 6% slower).
-template <int DK>
-struct TreeStores {
+// The per-position stores of a wave, through raw buffer resources whose
+// base is wave-uniform and advances by a scalar add per position (the lane
+// offsets are loop invariant): the checkpoint rows of one position, with the
+// cache-policy bits BITS (tree loops: the streaming bit alone, nt = 2, since
+// the device-scope bit of the chain loops measured 4% slower on the
+// one-request tree; the fused chain loop: nt and sc1), and the rows' outputs,
+// stored by the first lane of each row (the other lanes' offset lies past the
+// resource, where the hardware drops the write, so no lane mask is needed;
+// in the 16-request chain loop, all 16 lanes of a row storing its value
+// measured 6% slower).
+template <int DK, int BITS>
+struct WaveStores {
   static constexpr int LPR = kLanesPerRow;
   static constexpr int RPW = 64 / LPR;
   static constexpr int NCH = DK / (4 * LPR);
@@ -485,7 +486,7 @@ struct TreeStores {
 
   // ckpt_row0 and out_r: this lane's row at position 0 of the unit
   // (ckpt_row0 may be null: then store_ckpt is never called).
-  __device__ __forceinline__ TreeStores(float* ckpt_row0, float* out_r, int t0, size_t pos_stride, int out_stride,
+  __device__ __forceinline__ WaveStores(float* ckpt_row0, float* out_r, int t0, size_t pos_stride, int out_stride,
                                         int lane) {
     const int rw = lane / LPR;
     const int li = lane % LPR;
@@ -500,12 +501,11 @@ struct TreeStores {
     out_off = li == 0 ? static_cast<uint32_t>(rw * 4) : kDroppedOffset;
   }
   __device__ __forceinline__ void store_ckpt(const f32x4 (&s)[NCH]) {
-    constexpr int kNt = 2;   // cache-policy bit of the store: nt
     // Raw buffer (stride 0) of RPW rows; the third dword's data format is 32 bits.
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(ckpt, 0, RPW * DK * 4, 0x00020000);
 #pragma unroll
     for (int m = 0; m < NCH; ++m)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), rsrc, ckpt_off + m * LPR * 16, 0, kNt);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[m]), rsrc, ckpt_off + m * LPR * 16, 0, BITS);
     ckpt += ckpt_step;
   }
   __device__ __forceinline__ void store_out(float o) {
@@ -544,8 +544,9 @@ __device__ __forceinline__ void update_row(f32x4 (&s)[NCH], const f32x4 (&k)[NCH
 
 // Positions [t0, t0 + tn) of one unit, for the consumer threads: S rows in
 // VGPRs, staged inputs from LDS, checkpoint and output stores. No barrier and
-// (without RELOAD) no vector-memory load.
-template <int DK, int NW, int RPB, int POS_FLOATS, bool TREE, bool RELOAD, bool CAPTURE>
+// (without RELOAD) no vector-memory load. LEAN selects the shorter loop for
+// 32-row chain units (the fused layer's).
+template <int DK, int NW, int RPB, int POS_FLOATS, bool TREE, bool RELOAD, bool CAPTURE, bool LEAN = false>
 __device__ __forceinline__ void run_positions(const float* buf, f32x4* stash, f32x4 (&s)[DK / 64], int t0, int tn,
                                               float* ckpt_row0, float* out_r, size_t pos_stride, int out_stride) {
   constexpr int LPR = kLanesPerRow;
@@ -570,7 +571,7 @@ __device__ __forceinline__ void run_positions(const float* buf, f32x4* stash, f3
       float a, b, v;
       int code;    // stash code
     };
-    TreeStores<DK> st(CAPTURE ? ckpt_row0 : nullptr, out_r, t0, pos_stride, out_stride, lane);
+    WaveStores<DK, 2> st(CAPTURE ? ckpt_row0 : nullptr, out_r, t0, pos_stride, out_stride, lane);
     auto fetch = [&](int tt, In& d) {
       const float* lp = buf + tt * POS_FLOATS;
 #pragma unroll
@@ -697,6 +698,30 @@ __device__ __forceinline__ void run_positions(const float* buf, f32x4* stash, f3
       }
       o = group_sum<LPR>(o);
       if (li == 0) out_r[static_cast<size_t>(t0 + tn - 1) * out_stride] = o;
+    }
+  } else if constexpr (LEAN) {
+    // 32-row units of the fused layer: its producer waves compute the conv,
+    // SiLU and norms on the same SIMDs, so the consumers' instruction count
+    // matters there. The stores take wave-uniform bases advanced by scalar
+    // adds, and the checkpoint stores are kept ahead of the output's sum (the
+    // compiler would sink them to the end of the iteration): 72 instead of 87
+    // instructions per position, 16-request fused step 5.27-5.28 vs
+    // 5.36 ms. The plain kernel measured 0.5% slower this way and keeps the
+    // loop below.
+    WaveStores<DK, 2 | 16> st(CAPTURE ? ckpt_row0 : nullptr, out_r, t0, pos_stride, out_stride, lane);
+    for (int tt = 0; tt < tn; ++tt) {
+      const float* lp = buf + tt * POS_FLOATS;
+      f32x4 kk[NCH], qq[NCH];
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) kk[m] = *reinterpret_cast<const f32x4*>(lp + 4 * (li + LPR * m));
+      const float u = row_dot<NCH>(s, kk);
+      const float at = lp[2 * DK + RPB];
+      update_row<NCH>(s, kk, at, lp[2 * DK + RPB + 1] * __builtin_fmaf(-at, u, lp[2 * DK + row_blk]));
+      if (CAPTURE) st.store_ckpt(s);
+      __builtin_amdgcn_sched_barrier(0);   // the stores stay here
+#pragma unroll
+      for (int m = 0; m < NCH; ++m) qq[m] = *reinterpret_cast<const f32x4*>(lp + DK + 4 * (li + LPR * m));
+      st.store_out(row_dot<NCH>(s, qq));
     }
   } else {
     for (int tt = 0; tt < tn; ++tt) {
@@ -879,7 +904,7 @@ __global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const voi
         stage_window<DK, NC + NX * 64, RPB, POS_FLOATS, TIn, TREE, FUSED>(args, hs, lds, u, t0, tn, tid);
         __syncthreads();
         if (owner)
-          run_positions<DK, NW, RPB, POS_FLOATS, TREE, RELOAD, CAPTURE>(lds, stash, s, t0, tn, ckpt_row0, out_r,
+          run_positions<DK, NW, RPB, POS_FLOATS, TREE, RELOAD, CAPTURE, FUSED>(lds, stash, s, t0, tn, ckpt_row0, out_r,
                                                                         pos_stride, out_stride);
       }
       if (!CAPTURE && owner) {
@@ -947,7 +972,7 @@ __global__ __launch_bounds__((NW + NP + NX) * 64) void gdn_span_kernel(const voi
       if (consumer) {
         if (valid) {
           const int t0 = j * kWindow;
-          run_positions<DK, NW, RPB, POS_FLOATS, false, false, CAPTURE>(
+          run_positions<DK, NW, RPB, POS_FLOATS, false, false, CAPTURE, FUSED>(
               lds + (i & 1) * SB, nullptr, s, t0, min(kWindow, T - t0), ckpt_row0, out_r, pos_stride, out_stride);
         }
       } else if (i + 1 < n_items) {
