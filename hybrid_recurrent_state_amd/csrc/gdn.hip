@@ -178,18 +178,10 @@ __device__ __forceinline__ Hot make_hot(const void* in0, const void* in1, const 
   return h;
 }
 
-// Sixteen consecutive elements as f32 (the source must be 16-byte aligned).
-template <typename TIn>
-__device__ __forceinline__ void load16(const TIn* p, float* o) {
-  load8<TIn>(p, o);
-  load8<TIn>(p + 8, o + 8);
-}
-
 // One row unit: rows [row0, row0 + RPB) of value head h of request r (the
 // index within this launch, which every launch pointer is offset to).
 struct Unit {
-  int r;     // request within this launch
-  int rl;    // the same (geometry tables are per launch too)
+  int r;     // request within this launch (geometry tables are per launch too)
   int h;     // value head
   int g;     // key head
   int row0;  // first row
@@ -201,8 +193,7 @@ __device__ __forceinline__ Unit unit_of(const Hot& hs, int W, int rpb) {
   Unit u;
   u.row0 = (W % nrb) * rpb;
   u.h = (W / nrb) % hs.n_vheads;
-  u.rl = W / (nrb * hs.n_vheads);
-  u.r = u.rl;
+  u.r = W / (nrb * hs.n_vheads);
   u.g = u.h / hs.group;
   return u;
 }
@@ -334,7 +325,7 @@ __device__ __forceinline__ void stage_fused(const GdnArgs& args, const Hot& hs, 
     for (int m = 0; m < 3; ++m) {
       int src;
       if constexpr (TREE) {
-        src = args.geom[3 * args.geom_req * T + (u.rl * T + t) * 3 + m];
+        src = args.geom[3 * args.geom_req * T + (u.r * T + t) * 3 + m];
       } else {
         const int sq = t - 3 + m;
         src = sq >= 0 ? sq : -1 - (t + m);
@@ -385,7 +376,7 @@ __device__ __forceinline__ void stage_gates(const GdnArgs& args, const Hot& hs, 
     buf[e * POS_FLOATS + 2 * DK + RPB] = load_elem<TIn>(ag, src);
     buf[e * POS_FLOATS + 2 * DK + RPB + 1] = load_elem<TIn>(bg, src);
     if constexpr (TREE) {
-      const int gi = u.rl * T + t0 + e;
+      const int gi = u.r * T + t0 + e;
       const int nT = args.geom_req * T;
       const uint32_t code = static_cast<uint8_t>(args.geom[gi]) |
                             (static_cast<uint32_t>(static_cast<uint8_t>(args.geom[nT + gi])) << 8) |
