@@ -21,21 +21,27 @@
 //    chunks in parallel: K K^T and Q K^T on the matrix cores (bf16 inputs:
 //    32x32x16 MFMA, exact products, f32 accumulation), the decay products
 //    (running products, four lanes per row, no division or logarithm: zero
-//    and tiny decays are exact), T by forward substitution (four lanes per
-//    column, the partial sums joined by DPP), P T (16x16x4 f32 MFMA); written
-//    to the caller's workspace.
+//    and tiny decays are exact), T = (I + A)^-1 by 16 x 16 blocks (the
+//    diagonal blocks by forward substitution, four lanes per column joined by
+//    DPP; the blocks below them level by level on 16x16x4 f32 MFMA) and P T
+//    (16x16x4 f32 MFMA); the record is written to the caller's workspace in
+//    the order the sequential kernel's operand registers read it.
 //  * Sequential kernel, one block of 4 waves per (request, value head, 16
 //    state rows); each lane keeps 8 columns of one row of S in VGPRs across
 //    all chunks (the layout of gdn_verify_span). Per chunk: X = K S_0^T and
-//    QS = Q S_0^T (16x16x4 f32 MFMA), Y = b (V - g X), then W = T Y and
-//    P T Y with one pass of MFMAs over Y, the outputs, and the state: with
-//    capture S_t = a_t S_{t-1} + w_t k_t^T (8 FMAs per lane and position,
-//    no dot product), each stored with nontemporal 16-byte stores; without,
-//    the chunk-end state on the matrix cores. The next chunk's inputs and
-//    pre-pass record are loaded into registers while a chunk is processed.
-//    Blocks are ordered so that the 8 row blocks of one head fall on one XCD
-//    (workgroups go to XCDs round robin), where they share the head's k, q,
-//    T and P T through that XCD's L2.
+//    QS = Q S_0^T, Y = b (V - g X), then W = T Y and P T Y from T and P T in
+//    registers (16x16x4 f32 MFMA), the outputs, and the state: with capture
+//    S_t = a_t S_{t-1} + w_t k_t^T (8 FMAs per lane and position, no dot
+//    product), each stored with nontemporal 16-byte stores; without, the
+//    chunk-end state on the matrix cores. With bf16 inputs X, QS and the
+//    chunk-end state are bf16 products (16x16x32 MFMA): the f32 factor (S_0,
+//    or G[C-1][t] w_t) is split into three bf16 parts whose sum is exactly the
+//    f32 value, so every product is exact and the sums are f32; f32 inputs
+//    use 16x16x4 f32 MFMA. The next chunk's inputs and pre-pass record are
+//    loaded into registers while a chunk is processed. Blocks are ordered so
+//    that the 8 row blocks of one head fall on one XCD (workgroups go to XCDs
+//    round robin), where they share the head's k, q and record through that
+//    XCD's L2.
 // Positions past the end of the span are padded with a = 1, b = 0, k = q =
 // v = 0 (identity steps) and never streamed.
 #include <hip/hip_runtime.h>
