@@ -19,13 +19,16 @@
 // lowest index on ties, NaN never wins" in any reduction order, so the result
 // is deterministic. (A 64-bit key per element cost ~14 vector instructions
 // per logit and made pass 1 compute-bound; this form costs ~5.) Pass 2 is one
-// wave per request: the lanes gather the row keys (64-bit maximum per row in
-// LDS), the draft tokens and the parents together, then the acceptance walk
-// runs over the T <= 64 positions in LDS. The kernel boundary orders the two
-// passes. (Finishing each request in pass 1 instead, in the block that counts
-// itself last in a per-request arrival counter, was slower: with 323 blocks
-// per request counting on one address the device-scope atomics serialise,
-// 72 us against 27 us for 16 requests x 17 rows of 151,936 logits.)
+// wave per request: the lanes issue the loads of the row keys, the draft
+// tokens and the parents in one round (64-bit maximum per row in LDS), then
+// a chain is accepted by one ballot (position t matches when its draft token
+// equals the argmax at t - 1; the accepted length is the run of matches from
+// position 1) and a tree by one lane walking its T <= 64 positions in LDS.
+// The kernel boundary orders the two passes. (Finishing each request in pass
+// 1 instead, in the block that counts itself last in a per-request arrival
+// counter, was slower: with 323 blocks per request counting on one address
+// the device-scope atomics serialise, 72 us against 27 us for the two passes
+// at the time, 16 requests x 17 rows of 151,936 logits.)
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
