@@ -11,9 +11,10 @@
 //
 // MI355X design: a plain HBM-bound copy. The grid is (64 KiB chunk, layer x
 // request) of 1024-thread blocks; each thread issues four 16-byte
-// nontemporal loads before its four nontemporal stores, so every wave keeps
+// nontemporal loads before its four streaming stores, so every wave keeps
 // 4 KiB in flight (on 16 requests x 48 layers, 3.3 GB: 542 us, 6.1 TB/s,
-// against 580 us for 256-thread blocks; eight loads per thread were slower). A block whose request carries an index
+// against 580 us for 256-thread blocks; eight loads per thread were slower;
+// 522-531 us, 6.3 TB/s, since the stores also carry the device-scope bit). A block whose request carries an index
 // outside [0, T) copies nothing; block (0, 0) alone writes the status word
 // (the count of such requests), so the word needs no clearing and no atomics.
 #include <hip/hip_runtime.h>
