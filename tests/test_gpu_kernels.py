@@ -223,6 +223,45 @@ def test_gdn_tree_node_equals_chain_over_root_path(hrs):
         assert np.array_equal(ckc[0, -1], ck[0, node]) and np.array_equal(outc[0, -1], out[0, node]), node
 
 
+@pytest.mark.parametrize("n_kheads,n_vheads", [(4, 8), (16, 32)])
+@pytest.mark.parametrize("tree", [False, True])
+def test_gdn_degenerate_gates(hrs, n_kheads, n_vheads, tree):
+    """Gates and keys at the rule's degenerate values, against the oracle and
+    against what the rule then reduces to, exactly: a = b = 0 forgets the
+    state (S' = 0), a = 1 with b = 0 keeps it (S' = S of the parent), k = 0
+    only decays it (S' = a S of the parent, one rounding), and a = 0 with
+    b = 1 writes v k^T alone (a product of two bf16 values: exact in f32).
+    Two launch shapes: 16-row units at 8 value heads, 32-row units on one
+    block per CU at 2 requests x 32 value heads."""
+    T = 12
+    w = scaled(QWEN_LAYER_CHAIN, n_req=2, n_kheads=n_kheads, n_vheads=n_vheads, n_pos=T)
+    parent = (np.array([-1, 0, 1, 1, 3, 2, 5, 4, 7, 0, 9, 10], dtype=np.int32) if tree
+              else np.arange(-1, T - 1, dtype=np.int32))
+    forget, keep, no_key, write_only = (9, 5, 8, 11) if tree else (2, 5, 7, 9)
+    one, zero = bf16_bits(np.float32(1.0)), np.uint16(0)
+    units = []
+    for r in range(2):
+        u = gen_unit(w, 0, r)
+        a, b, k = u.a.copy(), u.b.copy(), u.k.copy()
+        a[forget], b[forget] = zero, zero
+        a[keep], b[keep] = one, zero
+        k[no_key] = zero
+        a[write_only], b[write_only] = zero, one
+        units.append(type(u)(q=u.q, k=k, v=u.v, a=a, b=b, state=u.state, x=u.x, conv_state=u.conv_state))
+    parents = np.tile(parent, (2, 1))
+    ck, out, _ = gpu_gdn(hrs, units, parent=parents if tree else None)
+    check_gdn_vs_oracle(units, ck, out, parents=parents if tree else None, what="degenerate gates")
+    f32 = lambda bits: (bits.astype(np.uint32) << 16).view(np.float32)
+    group = n_vheads // n_kheads
+    for r, u in enumerate(units):
+        assert np.all(ck[r, forget] == 0) and np.all(out[r, forget] == 0), "a = b = 0 must forget the state"
+        assert np.array_equal(ck[r, keep], ck[r, parent[keep]]), "a = 1, b = 0 must keep the parent's state"
+        a_nk = f32(u.a[no_key])                                     # [Hv]
+        assert np.array_equal(ck[r, no_key], a_nk[:, None, None] * ck[r, parent[no_key]]), "k = 0: S' = a S"
+        vk = f32(u.v[write_only])[:, :, None] * np.repeat(f32(u.k[write_only]), group, axis=0)[:, None, :]
+        assert np.array_equal(ck[r, write_only], vk), "a = 0, b = 1: S' = v k^T"
+
+
 def test_gdn_decode_steps_equal_span(hrs):
     """span(T) with capture == T single-position calls without capture that
     advance the state in place (verify == decode), bit for bit."""
