@@ -81,29 +81,36 @@ constexpr int kRecFloats = kRecGC + kC;
 
 __host__ __device__ constexpr int tile_index(int i, int j) { return i * (i + 1) / 2 + j; }
 
-// Sequential kernel LDS layout, in bytes. BF (bf16 inputs): k and q staged
-// as bf16, and the chunk's starting state also as three bf16 parts whose sum
-// is the f32 value (the operands of the bf16 products); f32 inputs: k and q
-// as f32. T and P T never go through LDS: each wave loads its own 16 rows
+// Sequential kernel LDS layout, in bytes: one chunk's inputs (k, q, the
+// block's v rows and the gates; in the producer/consumer form, PC, two such
+// buffers, each also holding the chunk's pre-pass record), then the compute
+// waves' own arrays. BF (bf16 inputs): k and q staged as bf16, and the
+// chunk's starting state also as three bf16 parts whose sum is the f32 value
+// (the operands of the bf16 products); f32 inputs: k and q as f32. Without
+// PC, T and P T never go through LDS: each wave loads its own 16 rows
 // straight into its matrix-core operand registers.
-template <bool BF>
+template <bool BF, bool PC = false>
 struct SeqLds {
   static constexpr int kKRow = BF ? (kDK + 8) * 2 : kKS * 4;   // bytes per k or q row (16-byte rows)
   static constexpr int kSplRow = (kDK + 8) * 2;                // bytes per row of one state part
+  // Offsets within an input buffer.
   static constexpr int K = 0;                                  // [C] rows of k
   static constexpr int Q = K + kC * kKRow;                     // [C] rows of q (unscaled)
   static constexpr int V = Q + kC * kKRow;                     // f32 [C][16] v rows of the block
-  static constexpr int S0 = V + kC * kRows * 4;                // f32 [16][kSS] S_0 rows
+  static constexpr int AV = V + kC * kRows * 4;                // f32 [C] a_t
+  static constexpr int BV = AV + kC * 4;                       // f32 [C] b_t
+  static constexpr int REC = BV + kC * 4;                      // PC: the chunk's pre-pass record
+  static constexpr int IN = REC + (PC ? kRecFloats * 4 : 0);   // bytes of one input buffer
+  // The compute waves' arrays, after the input buffer(s).
+  static constexpr int S0 = (PC ? 2 : 1) * IN;                 // f32 [16][kSS] S_0 rows
   static constexpr int SPL = S0 + kRows * kSS * 4;             // BF: bf16 [3][16] S_0 parts
   static constexpr int Y = SPL + (BF ? 3 * kRows * kSplRow : 0);   // f32 [16][kTS] Y^T (state row, position)
   static constexpr int W = Y + kRows * kTS * 4;                // f32 [16][kTS] W^T
   static constexpr int G = W + kRows * kTS * 4;                // f32 [C] g_t
   static constexpr int GC = G + kC * 4;                        // f32 [C] G[n-1][t] (follows g_t, as in the record)
-  static constexpr int AV = GC + kC * 4;                       // f32 [C] a_t
-  static constexpr int BV = AV + kC * 4;                       // f32 [C] b_t
-  static constexpr int BYTES = BV + kC * 4;
-  static_assert(Q % 16 == 0 && V % 16 == 0 && S0 % 16 == 0 && SPL % 16 == 0 && Y % 16 == 0 && W % 16 == 0,
-                "16-byte LDS rows");
+  static constexpr int BYTES = GC + kC * 4;
+  static_assert(Q % 16 == 0 && V % 16 == 0 && REC % 16 == 0 && IN % 16 == 0 && S0 % 16 == 0 && SPL % 16 == 0 &&
+                    Y % 16 == 0 && W % 16 == 0, "16-byte LDS rows");
 };
 
 // Pre-pass LDS layout: k and q staged first; A, P, T and T^T take their
@@ -269,9 +276,8 @@ template <> __device__ __forceinline__ float gate_widen<uint16_t>(uint16_t x) { 
 // rows from row0 of value head h.
 template <typename TIn, bool WITHV>
 __device__ __forceinline__ void fetch_chunk(const ChunkArgs& args, ChunkRegs<TIn>& rg, int r, int h, int g, int row0,
-                                            int c0, int n) {
+                                            int c0, int n, int tid) {
   const int T = args.n_pos;
-  const int tid = threadIdx.x;
   const TIn* qg = static_cast<const TIn*>(args.q);
   const TIn* kg = static_cast<const TIn*>(args.k);
   const TIn* vg = static_cast<const TIn*>(args.v);
@@ -372,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep_kernel(const ChunkArg
 
   {
     ChunkRegs<TIn> rg;
-    fetch_chunk<TIn, false>(args, rg, r, h, h / args.group, 0, c0, n);
+    fetch_chunk<TIn, false>(args, rg, r, h, h / args.group, 0, c0, n, threadIdx.x);
     stage_chunk<TIn, LOGG>(lds, rg, n, Av, Bv);
   }
   __syncthreads();
@@ -548,12 +554,35 @@ __device__ __forceinline__ void fetch_rec(const float* rec, RecRegs& rr) {
   if (tid < 2 * kC / 4) rr.g = *reinterpret_cast<const f32x4*>(rec + kRecG + 4 * tid);
 }
 
-// Sequential staging of a fetched chunk: k and q (bf16 as loaded, or f32),
-// the block's v rows and a_t, b_t as f32.
+// The producer/consumer form's copy of a chunk's pre-pass record into LDS:
+// loaded by the 256 producer threads (ptid) into registers, written to the
+// input buffer unchanged.
+constexpr int kRecVec = kRecFloats / 4;                          // float4 per record
+constexpr int kRecVecPerThread = (kRecVec + kThreads - 1) / kThreads;
+static_assert(kRecFloats % 4 == 0, "whole float4 records");
+
+__device__ __forceinline__ void fetch_rec_pc(const float* rec, f32x4 (&rr)[kRecVecPerThread], int ptid) {
+#pragma unroll
+  for (int k = 0; k < kRecVecPerThread; ++k) {
+    const int i = ptid + k * kThreads;
+    if (i < kRecVec) rr[k] = reinterpret_cast<const f32x4*>(rec)[i];
+  }
+}
+
+__device__ __forceinline__ void stage_rec_pc(float* recl, const f32x4 (&rr)[kRecVecPerThread], int ptid) {
+#pragma unroll
+  for (int k = 0; k < kRecVecPerThread; ++k) {
+    const int i = ptid + k * kThreads;
+    if (i < kRecVec) reinterpret_cast<f32x4*>(recl)[i] = rr[k];
+  }
+}
+
+// Sequential staging of a fetched chunk into an input buffer: k and q (bf16
+// as loaded, or f32), the block's v rows and a_t, b_t as f32 (tid: the
+// staging thread, 0 .. kThreads - 1).
 template <typename TIn, bool LOGG>
-__device__ __forceinline__ void stage_seq(char* lds, const ChunkRegs<TIn>& rg, int n) {
+__device__ __forceinline__ void stage_seq(char* lds, const ChunkRegs<TIn>& rg, int n, int tid) {
   using L = SeqLds<sizeof(TIn) == 2>;
-  const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < kKQItems; ++i) {
     const int e = tid + i * kThreads;
@@ -624,12 +653,18 @@ __device__ __forceinline__ f32x4 k4_at(const char* lds, int t, int c) {
 // Sequential pass over the segment's chunks. init: the state the segment
 // starts from, request r's rows at init + r * init_rstride (the state
 // buffer, or with capture the checkpoint before the segment). LOGG: `a`
-// holds log decays; OUTBF: outputs are written as bf16.
-template <typename TIn, bool CAPTURE, bool LOGG, bool OUTBF>
-__global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs args, const float* ws, int chunk0,
-                                                               int n_seg, const float* init, size_t init_rstride) {
+// holds log decays; OUTBF: outputs are written as bf16. PC: 4 further
+// producer waves load chunk c + 2 and stage chunk c + 1 into the other of two
+// input buffers while the 4 compute waves process chunk c (the staging then
+// leaves the compute waves' path; every barrier is shared by both roles).
+template <typename TIn, bool CAPTURE, bool LOGG, bool OUTBF, bool PC>
+__global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kernel(const ChunkArgs args,
+                                                                                  const float* ws, int chunk0,
+                                                                                  int n_seg, const float* init,
+                                                                                  size_t init_rstride) {
   constexpr bool BF = sizeof(TIn) == 2;
-  using L = SeqLds<BF>;
+  static_assert(!PC || BF, "two f32 input buffers do not fit in LDS");
+  using L = SeqLds<BF, PC>;
   extern __shared__ float lds_f[];
   char* const lds = reinterpret_cast<char*>(lds_f);
   const int T = args.n_pos;
@@ -660,14 +695,13 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
   const int row_blk = wave * (64 / kLPR) + lane / kLPR;   // 0..15
   const size_t head_elems = static_cast<size_t>(kDK) * kDK;
   const size_t pos_stride = static_cast<size_t>(Hv) * head_elems;
-  const float* const Vl = reinterpret_cast<const float*>(lds + L::V);
+  const bool compute = !PC || tid < kThreads;   // wave-uniform
+  const int ptid = tid - kThreads;              // producer index (PC)
   float* const S0 = reinterpret_cast<float*>(lds + L::S0);
   float* const Yt = reinterpret_cast<float*>(lds + L::Y);
   float* const Wt = reinterpret_cast<float*>(lds + L::W);
-  float* const Gv = reinterpret_cast<float*>(lds + L::G);
-  float* const GC = reinterpret_cast<float*>(lds + L::GC);
-  const float* const Av = reinterpret_cast<const float*>(lds + L::AV);
-  const float* const Bv = reinterpret_cast<const float*>(lds + L::BV);
+  float* const GvC = reinterpret_cast<float*>(lds + L::G);   // without PC: g_t and G[n-1][t] of the chunk
+  float* const GCC = reinterpret_cast<float*>(lds + L::GC);
   const float* const rec0 = ws + (static_cast<size_t>(r) * Hv + h) * n_seg * kRecFloats;
 
   const size_t row_off = static_cast<size_t>(h) * head_elems + static_cast<size_t>(row0 + row_blk) * kDK;
@@ -677,8 +711,10 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
   const size_t out_h = (static_cast<size_t>(r) * T * Hv + h) * kDK + row0;   // element offset
 
   f32x4 s[kNCH];
+  if (compute) {
 #pragma unroll
-  for (int m = 0; m < kNCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(init_row + 4 * (li + kLPR * m));
+    for (int m = 0; m < kNCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(init_row + 4 * (li + kLPR * m));
+  }
 
   // A chunk's outputs wait in registers until the next chunk is staged:
   // stored right away they would sit in the memory counter in front of the
@@ -700,278 +736,354 @@ __global__ __launch_bounds__(kThreads) void gdn_chunked_kernel(const ChunkArgs a
   };
 
   ChunkRegs<TIn> rg;
-  RecRegs cur, nxt;
-  fetch_chunk<TIn, true>(args, rg, r, h, g, row0, chunk0 * kC, min(kC, T - chunk0 * kC));
-  fetch_rec(rec0, nxt);
+  RecRegs cur, nxt;                       // without PC: this chunk's and the next chunk's record
+  f32x4 rr[kRecVecPerThread];             // PC producers: the record being prefetched
+  if constexpr (PC) {
+    // The producers stage the first chunk and its record, and fetch the second.
+    if (!compute) {
+      fetch_chunk<TIn, true>(args, rg, r, h, g, row0, chunk0 * kC, min(kC, T - chunk0 * kC), ptid);
+      fetch_rec_pc(rec0, rr, ptid);
+      stage_seq<TIn, LOGG>(lds, rg, min(kC, T - chunk0 * kC), ptid);
+      stage_rec_pc(reinterpret_cast<float*>(lds + L::REC), rr, ptid);
+      if (n_seg > 1) {
+        fetch_chunk<TIn, true>(args, rg, r, h, g, row0, (chunk0 + 1) * kC, min(kC, T - (chunk0 + 1) * kC), ptid);
+        fetch_rec_pc(rec0 + kRecFloats, rr, ptid);
+      }
+    }
+  } else {
+    fetch_chunk<TIn, true>(args, rg, r, h, g, row0, chunk0 * kC, min(kC, T - chunk0 * kC), tid);
+    fetch_rec(rec0, nxt);
+  }
   for (int cl = 0; cl < n_seg; ++cl) {
     const int c0 = (chunk0 + cl) * kC;
     const int n = min(kC, T - c0);
-    __syncthreads();   // the previous chunk's LDS reads are done
-    // 1. Stage the fetched chunk, its decays and the current state rows (as
-    //    f32 and, for the bf16 products, as three bf16 parts), take over
-    //    the record's T and P T rows, then fetch the next chunk: its loads
-    //    complete while this one is processed.
-    stage_seq<TIn, LOGG>(lds, rg, n);
-    cur = nxt;
-    if (tid < 2 * kC / 4) *reinterpret_cast<f32x4*>(Gv + 4 * tid) = cur.g;
+    // This chunk's input buffer.
+    char* const inb = lds + (PC ? (cl & 1) * L::IN : 0);
+    const float* const Vl = reinterpret_cast<const float*>(inb + L::V);
+    const float* const Av = reinterpret_cast<const float*>(inb + L::AV);
+    const float* const Bv = reinterpret_cast<const float*>(inb + L::BV);
+    const float* const recl = reinterpret_cast<const float*>(inb + L::REC);   // PC: the chunk's record
+    const float* const Gv = PC ? recl + kRecG : GvC;
+    const float* const GC = PC ? recl + kRecGC : GCC;
+    __syncthreads();   // the previous chunk's LDS reads are done (PC: this chunk is staged)
+    // 1. Stage the fetched chunk (PC: staged already), its decays and the
+    //    current state rows (as f32 and, for the bf16 products, as three
+    //    bf16 parts), take over the record's T and P T rows, then fetch the
+    //    next chunk: its loads complete while this one is processed.
+    if constexpr (!PC) stage_seq<TIn, LOGG>(lds, rg, n, tid);
+    if (compute) {
+      if constexpr (!PC) {
+        cur = nxt;
+        if (tid < 2 * kC / 4) *reinterpret_cast<f32x4*>(GvC + 4 * tid) = cur.g;
+      }
 #pragma unroll
-    for (int m = 0; m < kNCH; ++m) {
-      *reinterpret_cast<f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m)) = s[m];
-      if constexpr (BF) {
-        uint32_t hp[4], mp[4], lp[4];
+      for (int m = 0; m < kNCH; ++m) {
+        *reinterpret_cast<f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m)) = s[m];
+        if constexpr (BF) {
+          uint32_t hp[4], mp[4], lp[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) split3(s[m][e], hp[e], mp[e], lp[e]);
-        char* const sp = lds + L::SPL + row_blk * L::kSplRow + 2 * 4 * (li + kLPR * m);
-        *reinterpret_cast<u32x2*>(sp) = u32x2{hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16)};
-        *reinterpret_cast<u32x2*>(sp + kRows * L::kSplRow) = u32x2{mp[0] | (mp[1] << 16), mp[2] | (mp[3] << 16)};
-        *reinterpret_cast<u32x2*>(sp + 2 * kRows * L::kSplRow) = u32x2{lp[0] | (lp[1] << 16), lp[2] | (lp[3] << 16)};
+          for (int e = 0; e < 4; ++e) split3(s[m][e], hp[e], mp[e], lp[e]);
+          char* const sp = lds + L::SPL + row_blk * L::kSplRow + 2 * 4 * (li + kLPR * m);
+          *reinterpret_cast<u32x2*>(sp) = u32x2{hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16)};
+          *reinterpret_cast<u32x2*>(sp + kRows * L::kSplRow) = u32x2{mp[0] | (mp[1] << 16), mp[2] | (mp[3] << 16)};
+          *reinterpret_cast<u32x2*>(sp + 2 * kRows * L::kSplRow) = u32x2{lp[0] | (lp[1] << 16), lp[2] | (lp[3] << 16)};
+        }
+      }
+      if constexpr (!PC) {
+        if (cl + 1 < n_seg) {
+          fetch_chunk<TIn, true>(args, rg, r, h, g, row0, c0 + kC, min(kC, T - c0 - kC), tid);
+          fetch_rec(rec0 + static_cast<size_t>(cl + 1) * kRecFloats, nxt);
+        }
       }
     }
-    if (cl + 1 < n_seg) {
-      fetch_chunk<TIn, true>(args, rg, r, h, g, row0, c0 + kC, min(kC, T - c0 - kC));
-      fetch_rec(rec0 + static_cast<size_t>(cl + 1) * kRecFloats, nxt);
-    }
     __syncthreads();
-    store_pending();
-    // 2. X = K S_0^T and QS = Q S_0^T: wave w takes positions [16 w,
-    //    16 w + 16) for all 16 state rows. bf16 inputs: three bf16 products
-    //    per operand pair (16x16x32 MFMA: k and q are bf16, S_0 = hi + mid +
-    //    lo exactly, each product exact, f32 accumulation); f32 inputs: f32
-    //    products (16x16x4 MFMA), lane group kq supplying columns [c + 4 kq,
-    //    c + 4 kq + 4) of each 16, so a lane reads its operands as 16-byte
-    //    LDS loads. Then Y = b (V - g X), stored transposed, and q_scale g QS
-    //    kept in the lanes that hold it.
     const int tb = 16 * wave + 4 * kq;   // this lane's 4 positions of the wave's tile
     f32x4 qsg;
-    {
-      const int row = 16 * wave + srow;
-      f32x4 xk, xq;
-      if constexpr (BF) {
-        f32x4 xh = {}, xm = {}, xl = {}, qh = {}, qm = {}, ql = {};
+    if (compute) {
+      store_pending();
+      // 2. X = K S_0^T and QS = Q S_0^T: wave w takes positions [16 w,
+      //    16 w + 16) for all 16 state rows. bf16 inputs: three bf16 products
+      //    per operand pair (16x16x32 MFMA: k and q are bf16, S_0 = hi + mid +
+      //    lo exactly, each product exact, f32 accumulation); f32 inputs: f32
+      //    products (16x16x4 MFMA), lane group kq supplying columns [c + 4 kq,
+      //    c + 4 kq + 4) of each 16, so a lane reads its operands as 16-byte
+      //    LDS loads. Then Y = b (V - g X), stored transposed, and q_scale g QS
+      //    kept in the lanes that hold it.
+      {
+        const int row = 16 * wave + srow;
+        f32x4 xk, xq;
+        if constexpr (BF) {
+          f32x4 xh = {}, xm = {}, xl = {}, qh = {}, qm = {}, ql = {};
 #pragma unroll
-        for (int c = 0; c < kDK; c += 32) {
-          const int col = 2 * (c + 8 * kq);
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lds + L::K + row * L::kKRow + col);
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(lds + L::Q + row * L::kKRow + col);
-          const char* const sp = lds + L::SPL + srow * L::kSplRow + col;
-          const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sp);
-          const bf16x8 sm = *reinterpret_cast<const bf16x8*>(sp + kRows * L::kSplRow);
-          const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sp + 2 * kRows * L::kSplRow);
-          xh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sh, xh, 0, 0, 0);
-          qh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, sh, qh, 0, 0, 0);
-          xm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sm, xm, 0, 0, 0);
-          qm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, sm, qm, 0, 0, 0);
-          xl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sl, xl, 0, 0, 0);
-          ql = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, sl, ql, 0, 0, 0);
+          for (int c = 0; c < kDK; c += 32) {
+            const int col = 2 * (c + 8 * kq);
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(inb + L::K + row * L::kKRow + col);
+            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(inb + L::Q + row * L::kKRow + col);
+            const char* const sp = lds + L::SPL + srow * L::kSplRow + col;
+            const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sp);
+            const bf16x8 sm = *reinterpret_cast<const bf16x8*>(sp + kRows * L::kSplRow);
+            const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sp + 2 * kRows * L::kSplRow);
+            xh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sh, xh, 0, 0, 0);
+            qh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, sh, qh, 0, 0, 0);
+            xm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sm, xm, 0, 0, 0);
+            qm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, sm, qm, 0, 0, 0);
+            xl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, sl, xl, 0, 0, 0);
+            ql = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, sl, ql, 0, 0, 0);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            xk[u] = (xl[u] + xm[u]) + xh[u];
+            xq[u] = (ql[u] + qm[u]) + qh[u];
+          }
+        } else {
+          xk = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          xq = xk;
+#pragma unroll 2
+          for (int c = 0; c < kDK; c += 16) {
+            const f32x4 kv = *reinterpret_cast<const f32x4*>(inb + L::K + row * L::kKRow + 4 * (c + 4 * kq));
+            const f32x4 qv = *reinterpret_cast<const f32x4*>(inb + L::Q + row * L::kKRow + 4 * (c + 4 * kq));
+            const f32x4 sv = *reinterpret_cast<const f32x4*>(S0 + srow * kSS + c + 4 * kq);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              xk = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[u], sv[u], xk, 0, 0, 0);
+              xq = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[u], sv[u], xq, 0, 0, 0);
+            }
+          }
         }
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(Gv + tb);
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(Bv + tb);
+        f32x4 y;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          xk[u] = (xl[u] + xm[u]) + xh[u];
-          xq[u] = (ql[u] + qm[u]) + qh[u];
+          y[u] = b4[u] * __builtin_fmaf(-g4[u], xk[u], Vl[(tb + u) * kRows + srow]);
+          qsg[u] = (g4[u] * args.q_scale) * xq[u];
         }
-      } else {
-        xk = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        xq = xk;
-#pragma unroll 2
-        for (int c = 0; c < kDK; c += 16) {
-          const f32x4 kv = *reinterpret_cast<const f32x4*>(lds + L::K + row * L::kKRow + 4 * (c + 4 * kq));
-          const f32x4 qv = *reinterpret_cast<const f32x4*>(lds + L::Q + row * L::kKRow + 4 * (c + 4 * kq));
-          const f32x4 sv = *reinterpret_cast<const f32x4*>(S0 + srow * kSS + c + 4 * kq);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            xk = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[u], sv[u], xk, 0, 0, 0);
-            xq = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[u], sv[u], xq, 0, 0, 0);
-          }
-        }
+        *reinterpret_cast<f32x4*>(Yt + srow * kTS + tb) = y;
       }
-      const f32x4 g4 = *reinterpret_cast<const f32x4*>(Gv + tb);
-      const f32x4 b4 = *reinterpret_cast<const f32x4*>(Bv + tb);
-      f32x4 y;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        y[u] = b4[u] * __builtin_fmaf(-g4[u], xk[u], Vl[(tb + u) * kRows + srow]);
-        qsg[u] = (g4[u] * args.q_scale) * xq[u];
-      }
-      *reinterpret_cast<f32x4*>(Yt + srow * kTS + tb) = y;
     }
     __syncthreads();
-    // 3. W = T Y and P T Y in one pass over Y (16x16x4 f32 MFMA; wave w
-    //    takes positions [16 w, 16 w + 16) with its T and P T rows in
-    //    registers; both are lower triangular, so the column blocks past w
-    //    are skipped); outputs o = q_scale g QS + P T Y, stored after the
-    //    next chunk is staged.
-    {
-      f32x4 wacc = {}, oacc = {};
+    if (compute) {
+      // 3. W = T Y and P T Y in one pass over Y (16x16x4 f32 MFMA; wave w
+      //    takes positions [16 w, 16 w + 16) with its T and P T rows in
+      //    registers, PC: read from the staged record; both are lower
+      //    triangular, so the column blocks past w are skipped); outputs
+      //    o = q_scale g QS + P T Y, stored after the next chunk is staged.
+      {
+        f32x4 wacc = {}, oacc = {};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (c <= wave) {
-          const f32x4 yv = *reinterpret_cast<const f32x4*>(Yt + srow * kTS + 16 * c + 4 * kq);
+        for (int c = 0; c < 4; ++c) {
+          if (c <= wave) {
+            const f32x4 yv = *reinterpret_cast<const f32x4*>(Yt + srow * kTS + 16 * c + 4 * kq);
+            f32x4 tc, pc;
+            if constexpr (PC) {
+              tc = *reinterpret_cast<const f32x4*>(recl + kRecT + tile_index(wave, c) * 256 + 4 * lane);
+              pc = *reinterpret_cast<const f32x4*>(recl + kRecPT + tile_index(wave, c) * 256 + 4 * lane);
+            } else {
+              tc = cur.t[c];
+              pc = cur.pt[c];
+            }
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            wacc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.t[c][u], yv[u], wacc, 0, 0, 0);
-            oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.pt[c][u], yv[u], oacc, 0, 0, 0);
+            for (int u = 0; u < 4; ++u) {
+              wacc = __builtin_amdgcn_mfma_f32_16x16x4f32(tc[u], yv[u], wacc, 0, 0, 0);
+              oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(pc[u], yv[u], oacc, 0, 0, 0);
+            }
           }
         }
-      }
-      *reinterpret_cast<f32x4*>(Wt + srow * kTS + tb) = wacc;
+        *reinterpret_cast<f32x4*>(Wt + srow * kTS + tb) = wacc;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) o_pend[u] = qsg[u] + oacc[u];
-      o_elem = out_h + static_cast<size_t>(c0 + tb) * Hv * kDK + srow;
-      o_cnt = min(4, max(0, n - tb));
+        for (int u = 0; u < 4; ++u) o_pend[u] = qsg[u] + oacc[u];
+        o_elem = out_h + static_cast<size_t>(c0 + tb) * Hv * kDK + srow;
+        o_cnt = min(4, max(0, n - tb));
+      }
+    } else if constexpr (PC) {
+      // Producers: stage the next chunk into the other buffer (its reads
+      // ended at the previous chunk's last barrier), then fetch the one
+      // after it.
+      if (cl + 1 < n_seg) {
+        char* const nb = lds + ((cl + 1) & 1) * L::IN;
+        stage_seq<TIn, LOGG>(nb, rg, min(kC, T - c0 - kC), ptid);
+        stage_rec_pc(reinterpret_cast<float*>(nb + L::REC), rr, ptid);
+        if (cl + 2 < n_seg) {
+          fetch_chunk<TIn, true>(args, rg, r, h, g, row0, c0 + 2 * kC, min(kC, T - c0 - 2 * kC), ptid);
+          fetch_rec_pc(rec0 + static_cast<size_t>(cl + 2) * kRecFloats, rr, ptid);
+        }
+      }
     }
     __syncthreads();
     if constexpr (CAPTURE) {
-      // 4. States: S_t = a_t S_{t-1} + w_t k_t^T, each checkpointed; 8
-      //    positions at a time so their LDS reads are issued together.
-      for (int t0 = 0; t0 < n; t0 += 8) {
-        float at[8], wt[8];
-        f32x4 kk[8][kNCH];
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(Wt + row_blk * kTS + t0);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(Wt + row_blk * kTS + t0 + 4);
+      if (compute) {
+        // 4. States: S_t = a_t S_{t-1} + w_t k_t^T, each checkpointed; 8
+        //    positions at a time so their LDS reads are issued together.
+        for (int t0 = 0; t0 < n; t0 += 8) {
+          float at[8], wt[8];
+          f32x4 kk[8][kNCH];
+          const f32x4 w0 = *reinterpret_cast<const f32x4*>(Wt + row_blk * kTS + t0);
+          const f32x4 w1 = *reinterpret_cast<const f32x4*>(Wt + row_blk * kTS + t0 + 4);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          wt[u] = w0[u];
-          wt[u + 4] = w1[u];
-        }
+          for (int u = 0; u < 4; ++u) {
+            wt[u] = w0[u];
+            wt[u + 4] = w1[u];
+          }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          at[u] = Av[t0 + u];
+          for (int u = 0; u < 8; ++u) {
+            at[u] = Av[t0 + u];
 #pragma unroll
-          for (int m = 0; m < kNCH; ++m) kk[u][m] = k4_at<BF>(lds, t0 + u, 4 * (li + kLPR * m));
-        }
-        const int un = min(8, n - t0);
+            for (int m = 0; m < kNCH; ++m) kk[u][m] = k4_at<BF>(inb, t0 + u, 4 * (li + kLPR * m));
+          }
+          const int un = min(8, n - t0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (un == 8 || u < un) {
+          for (int u = 0; u < 8; ++u) {
+            if (un == 8 || u < un) {
 #pragma unroll
-            for (int m = 0; m < kNCH; ++m) {
-              s[m].x = __builtin_fmaf(wt[u], kk[u][m].x, at[u] * s[m].x);
-              s[m].y = __builtin_fmaf(wt[u], kk[u][m].y, at[u] * s[m].y);
-              s[m].z = __builtin_fmaf(wt[u], kk[u][m].z, at[u] * s[m].z);
-              s[m].w = __builtin_fmaf(wt[u], kk[u][m].w, at[u] * s[m].w);
+              for (int m = 0; m < kNCH; ++m) {
+                s[m].x = __builtin_fmaf(wt[u], kk[u][m].x, at[u] * s[m].x);
+                s[m].y = __builtin_fmaf(wt[u], kk[u][m].y, at[u] * s[m].y);
+                s[m].z = __builtin_fmaf(wt[u], kk[u][m].z, at[u] * s[m].z);
+                s[m].w = __builtin_fmaf(wt[u], kk[u][m].w, at[u] * s[m].w);
+              }
+              float* dst = ckpt_row0 + static_cast<size_t>(c0 + t0 + u) * pos_stride;
+#pragma unroll
+              for (int m = 0; m < kNCH; ++m)
+                __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(dst + 4 * (li + kLPR * m)));
             }
-            float* dst = ckpt_row0 + static_cast<size_t>(c0 + t0 + u) * pos_stride;
-#pragma unroll
-            for (int m = 0; m < kNCH; ++m)
-              __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(dst + 4 * (li + kLPR * m)));
           }
         }
       }
     } else {
-      // 4. State at the chunk end only: S_C = g_{n-1} S_0 + sum_t G[n-1][t]
-      //    w_t k_t^T on the matrix cores (wave w takes columns [32 w, 32 w +
-      //    32)), every operand read before the first product; written over
-      //    S_0 and read back into the lanes' registers. bf16 inputs: the f32
-      //    factors G[n-1][t] w_t as three bf16 parts against bf16 k (16x16x32
-      //    MFMA, exact products); f32 inputs: 16x16x4 f32 MFMA.
-      f32x4 d0 = {}, d1 = {};
-      if constexpr (BF) {
-        bf16x8 ah[2], am[2], al[2], b0[2], b1[2];
+      if (compute) {
+        // 4. State at the chunk end only: S_C = g_{n-1} S_0 + sum_t G[n-1][t]
+        //    w_t k_t^T on the matrix cores (wave w takes columns [32 w, 32 w +
+        //    32)), every operand read before the first product; written over
+        //    S_0 and read back into the lanes' registers. bf16 inputs: the f32
+        //    factors G[n-1][t] w_t as three bf16 parts against bf16 k (16x16x32
+        //    MFMA, exact products); f32 inputs: 16x16x4 f32 MFMA.
+        f32x4 d0 = {}, d1 = {};
+        if constexpr (BF) {
+          bf16x8 ah[2], am[2], al[2], b0[2], b1[2];
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const int t8 = 32 * c2 + 8 * kq;
-          const f32x4 g0 = *reinterpret_cast<const f32x4*>(GC + t8);
-          const f32x4 g1 = *reinterpret_cast<const f32x4*>(GC + t8 + 4);
-          const f32x4 w0 = *reinterpret_cast<const f32x4*>(Wt + srow * kTS + t8);
-          const f32x4 w1 = *reinterpret_cast<const f32x4*>(Wt + srow * kTS + t8 + 4);
-          uint32_t hp[8], mp[8], lp[8];
+          for (int c2 = 0; c2 < 2; ++c2) {
+            const int t8 = 32 * c2 + 8 * kq;
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(GC + t8);
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(GC + t8 + 4);
+            const f32x4 w0 = *reinterpret_cast<const f32x4*>(Wt + srow * kTS + t8);
+            const f32x4 w1 = *reinterpret_cast<const f32x4*>(Wt + srow * kTS + t8 + 4);
+            uint32_t hp[8], mp[8], lp[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            split3(g0[e] * w0[e], hp[e], mp[e], lp[e]);
-            split3(g1[e] * w1[e], hp[e + 4], mp[e + 4], lp[e + 4]);
+            for (int e = 0; e < 4; ++e) {
+              split3(g0[e] * w0[e], hp[e], mp[e], lp[e]);
+              split3(g1[e] * w1[e], hp[e + 4], mp[e + 4], lp[e + 4]);
+            }
+            u32x4 kb0, kb1;
+            uint32_t kv0[8], kv1[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const char* kr = inb + L::K + (t8 + e) * L::kKRow + 2 * (32 * wave + srow);
+              kv0[e] = *reinterpret_cast<const uint16_t*>(kr);
+              kv1[e] = *reinterpret_cast<const uint16_t*>(kr + 32);
+            }
+            u32x4 hh, mm, ll;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              hh[e] = hp[2 * e] | (hp[2 * e + 1] << 16);
+              mm[e] = mp[2 * e] | (mp[2 * e + 1] << 16);
+              ll[e] = lp[2 * e] | (lp[2 * e + 1] << 16);
+              kb0[e] = kv0[2 * e] | (kv0[2 * e + 1] << 16);
+              kb1[e] = kv1[2 * e] | (kv1[2 * e + 1] << 16);
+            }
+            ah[c2] = __builtin_bit_cast(bf16x8, hh);
+            am[c2] = __builtin_bit_cast(bf16x8, mm);
+            al[c2] = __builtin_bit_cast(bf16x8, ll);
+            b0[c2] = __builtin_bit_cast(bf16x8, kb0);
+            b1[c2] = __builtin_bit_cast(bf16x8, kb1);
           }
-          u32x4 kb0, kb1;
-          uint32_t kv0[8], kv1[8];
+          f32x4 d0m = {}, d0l = {}, d1m = {}, d1l = {};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const char* kr = lds + L::K + (t8 + e) * L::kKRow + 2 * (32 * wave + srow);
-            kv0[e] = *reinterpret_cast<const uint16_t*>(kr);
-            kv1[e] = *reinterpret_cast<const uint16_t*>(kr + 32);
+          for (int c2 = 0; c2 < 2; ++c2) {
+            d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[c2], b0[c2], d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[c2], b1[c2], d1, 0, 0, 0);
+            d0m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[c2], b0[c2], d0m, 0, 0, 0);
+            d1m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[c2], b1[c2], d1m, 0, 0, 0);
+            d0l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[c2], b0[c2], d0l, 0, 0, 0);
+            d1l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[c2], b1[c2], d1l, 0, 0, 0);
           }
-          u32x4 hh, mm, ll;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            hh[e] = hp[2 * e] | (hp[2 * e + 1] << 16);
-            mm[e] = mp[2 * e] | (mp[2 * e + 1] << 16);
-            ll[e] = lp[2 * e] | (lp[2 * e + 1] << 16);
-            kb0[e] = kv0[2 * e] | (kv0[2 * e + 1] << 16);
-            kb1[e] = kv1[2 * e] | (kv1[2 * e + 1] << 16);
+          for (int u = 0; u < 4; ++u) {
+            d0[u] = (d0l[u] + d0m[u]) + d0[u];
+            d1[u] = (d1l[u] + d1m[u]) + d1[u];
           }
-          ah[c2] = __builtin_bit_cast(bf16x8, hh);
-          am[c2] = __builtin_bit_cast(bf16x8, mm);
-          al[c2] = __builtin_bit_cast(bf16x8, ll);
-          b0[c2] = __builtin_bit_cast(bf16x8, kb0);
-          b1[c2] = __builtin_bit_cast(bf16x8, kb1);
+        } else {
+          f32x4 wv[4];
+          float k0[4][4], k1[4][4];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int tq = 16 * q4 + 4 * kq;
+            const f32x4 gc = *reinterpret_cast<const f32x4*>(GC + tq);
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(Wt + srow * kTS + tq);
+            wv[q4] = f32x4{gc.x * w4.x, gc.y * w4.y, gc.z * w4.z, gc.w * w4.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              k0[q4][u] = k_at<BF>(inb, tq + u, 32 * wave + srow);
+              k1[q4][u] = k_at<BF>(inb, tq + u, 32 * wave + srow + 16);
+            }
+          }
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[q4][u], k0[q4][u], d0, 0, 0, 0);
+              d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[q4][u], k1[q4][u], d1, 0, 0, 0);
+            }
+          }
         }
-        f32x4 d0m = {}, d0l = {}, d1m = {}, d1l = {};
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[c2], b0[c2], d0, 0, 0, 0);
-          d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[c2], b1[c2], d1, 0, 0, 0);
-          d0m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[c2], b0[c2], d0m, 0, 0, 0);
-          d1m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[c2], b1[c2], d1m, 0, 0, 0);
-          d0l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[c2], b0[c2], d0l, 0, 0, 0);
-          d1l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[c2], b1[c2], d1l, 0, 0, 0);
-        }
+        const float gn = Gv[n - 1];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          d0[u] = (d0l[u] + d0m[u]) + d0[u];
-          d1[u] = (d1l[u] + d1m[u]) + d1[u];
+          float* e0 = S0 + (4 * kq + u) * kSS + 32 * wave + srow;
+          e0[0] = __builtin_fmaf(gn, e0[0], d0[u]);
+          e0[16] = __builtin_fmaf(gn, e0[16], d1[u]);
         }
-      } else {
-        f32x4 wv[4];
-        float k0[4][4], k1[4][4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int tq = 16 * q4 + 4 * kq;
-          const f32x4 gc = *reinterpret_cast<const f32x4*>(GC + tq);
-          const f32x4 w4 = *reinterpret_cast<const f32x4*>(Wt + srow * kTS + tq);
-          wv[q4] = f32x4{gc.x * w4.x, gc.y * w4.y, gc.z * w4.z, gc.w * w4.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            k0[q4][u] = k_at<BF>(lds, tq + u, 32 * wave + srow);
-            k1[q4][u] = k_at<BF>(lds, tq + u, 32 * wave + srow + 16);
-          }
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[q4][u], k0[q4][u], d0, 0, 0, 0);
-            d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[q4][u], k1[q4][u], d1, 0, 0, 0);
-          }
-        }
-      }
-      const float gn = Gv[n - 1];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float* e0 = S0 + (4 * kq + u) * kSS + 32 * wave + srow;
-        e0[0] = __builtin_fmaf(gn, e0[0], d0[u]);
-        e0[16] = __builtin_fmaf(gn, e0[16], d1[u]);
       }
       __syncthreads();
+      if (compute) {
 #pragma unroll
-      for (int m = 0; m < kNCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m));
+        for (int m = 0; m < kNCH; ++m)
+          s[m] = *reinterpret_cast<const f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m));
+      }
     }
   }
-  store_pending();
-  if (!CAPTURE) {
+  if (compute) {
+    store_pending();
+    if (!CAPTURE) {
 #pragma unroll
-    for (int m = 0; m < kNCH; ++m) *reinterpret_cast<f32x4*>(state_row + 4 * (li + kLPR * m)) = s[m];
+      for (int m = 0; m < kNCH; ++m) *reinterpret_cast<f32x4*>(state_row + 4 * (li + kLPR * m)) = s[m];
+    }
   }
 }
 
+template <typename TIn, bool CAPTURE, bool LOGG, bool OUTBF, bool PC>
+void launch_seq_kernel(const ChunkArgs& args, const float* ws, int chunk0, int n_seg, const float* init,
+                       size_t init_rstride, hipStream_t s) {
+  const int blocks = args.n_req * args.n_vheads * kRowBlocks;
+  constexpr size_t lds = SeqLds<sizeof(TIn) == 2, PC>::BYTES;
+  hipLaunchKernelGGL((gdn_chunked_kernel<TIn, CAPTURE, LOGG, OUTBF, PC>), dim3(blocks),
+                     dim3(PC ? 2 * kThreads : kThreads), lds, s, args, ws, chunk0, n_seg, init, init_rstride);
+}
+
+// Segments of several chunks with bf16 inputs take the producer/consumer
+// form; a single chunk has nothing to stage ahead (and the smaller form fits
+// two blocks per CU), and two f32 input buffers would not fit in LDS.
 template <typename TIn, bool CAPTURE, bool LOGG>
 hipError_t launch_seq(const ChunkArgs& args, const float* ws, int chunk0, int n_seg, const float* init,
                       size_t init_rstride, bool out_bf16, hipStream_t s) {
-  const int blocks = args.n_req * args.n_vheads * kRowBlocks;
-  constexpr size_t lds = SeqLds<sizeof(TIn) == 2>::BYTES;
-  if (out_bf16)
-    hipLaunchKernelGGL((gdn_chunked_kernel<TIn, CAPTURE, LOGG, true>), dim3(blocks), dim3(kThreads), lds, s, args,
-                       ws, chunk0, n_seg, init, init_rstride);
-  else
-    hipLaunchKernelGGL((gdn_chunked_kernel<TIn, CAPTURE, LOGG, false>), dim3(blocks), dim3(kThreads), lds, s, args,
-                       ws, chunk0, n_seg, init, init_rstride);
+  constexpr bool BF = sizeof(TIn) == 2;
+  const bool pc = BF && n_seg > 1;
+  if (out_bf16) {
+    if (pc) launch_seq_kernel<TIn, CAPTURE, LOGG, true, BF>(args, ws, chunk0, n_seg, init, init_rstride, s);
+    else launch_seq_kernel<TIn, CAPTURE, LOGG, true, false>(args, ws, chunk0, n_seg, init, init_rstride, s);
+  } else {
+    if (pc) launch_seq_kernel<TIn, CAPTURE, LOGG, false, BF>(args, ws, chunk0, n_seg, init, init_rstride, s);
+    else launch_seq_kernel<TIn, CAPTURE, LOGG, false, false>(args, ws, chunk0, n_seg, init, init_rstride, s);
+  }
   return launch_error();
 }
 
