@@ -38,7 +38,11 @@
 //    or G[C-1][t] w_t) is split into three bf16 parts whose sum is exactly the
 //    f32 value, so every product is exact and the sums are f32; f32 inputs
 //    use 16x16x4 f32 MFMA. The next chunk's inputs and pre-pass record are
-//    loaded into registers while a chunk is processed. Blocks are ordered so
+//    loaded while a chunk is processed: for a segment of several bf16 chunks
+//    by 4 producer waves, which stage them into the other of two LDS
+//    buffers; otherwise by the 4 compute waves into their registers (a
+//    single chunk keeps the smaller LDS footprint, two blocks per CU, and two
+//    f32 input buffers would not fit in LDS). Blocks are ordered so
 //    that the 8 row blocks of one head fall on one XCD (workgroups go to XCDs
 //    round robin), where they share the head's k, q and record through that
 //    XCD's L2.
