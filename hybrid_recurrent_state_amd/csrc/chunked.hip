@@ -864,6 +864,11 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
         }
         *reinterpret_cast<f32x4*>(Yt + srow * kTS + tb) = y;
       }
+    } else if constexpr (PC) {
+      // Producers, spread over three barrier intervals so that none of them
+      // outlasts the compute waves' step in it: the next chunk's inputs into
+      // the other buffer (its reads ended at this chunk's first barrier)...
+      if (cl + 1 < n_seg) stage_seq<TIn, LOGG>(lds + ((cl + 1) & 1) * L::IN, rg, min(kC, T - c0 - kC), ptid);
     }
     __syncthreads();
     if (compute) {
@@ -900,20 +905,17 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
         o_cnt = min(4, max(0, n - tb));
       }
     } else if constexpr (PC) {
-      // Producers: stage the next chunk into the other buffer (its reads
-      // ended at the previous chunk's last barrier), then fetch the one
-      // after it.
-      if (cl + 1 < n_seg) {
-        char* const nb = lds + ((cl + 1) & 1) * L::IN;
-        stage_seq<TIn, LOGG>(nb, rg, min(kC, T - c0 - kC), ptid);
-        stage_rec_pc(reinterpret_cast<float*>(nb + L::REC), rr, ptid);
-        if (cl + 2 < n_seg) {
-          fetch_chunk<TIn, true>(args, rg, r, h, g, row0, c0 + 2 * kC, min(kC, T - c0 - 2 * kC), ptid);
-          fetch_rec_pc(rec0 + static_cast<size_t>(cl + 2) * kRecFloats, rr, ptid);
-        }
-      }
+      // ... its record, and the loads of the inputs of the chunk after it ...
+      if (cl + 1 < n_seg)
+        stage_rec_pc(reinterpret_cast<float*>(lds + ((cl + 1) & 1) * L::IN + L::REC), rr, ptid);
+      if (cl + 2 < n_seg)
+        fetch_chunk<TIn, true>(args, rg, r, h, g, row0, c0 + 2 * kC, min(kC, T - c0 - 2 * kC), ptid);
     }
     __syncthreads();
+    if constexpr (PC) {
+      // ... and the loads of its record.
+      if (!compute && cl + 2 < n_seg) fetch_rec_pc(rec0 + static_cast<size_t>(cl + 2) * kRecFloats, rr, ptid);
+    }
     if constexpr (CAPTURE) {
       if (compute) {
         // 4. States: S_t = a_t S_{t-1} + w_t k_t^T, each checkpointed; 8
