@@ -654,6 +654,17 @@ __device__ __forceinline__ f32x4 k4_at(const char* lds, int t, int c) {
   }
 }
 
+// Four 16-bit values by the gfx950 transposing LDS read (ds_read_b64_tr_b16):
+// within each group of 16 lanes, lane i receives, as its j-th value, element
+// i % 4 of the four consecutive 16-bit values that lane 4 j + i / 4 of the
+// group addresses (p: 8-byte aligned, in LDS).
+__device__ __forceinline__ u32x2 ds_read_tr16(const char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(const_cast<char*>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Sequential pass over the segment's chunks. init: the state the segment
 // starts from, request r's rows at init + r * init_rstride (the state
 // buffer, or with capture the checkpoint before the segment). LOGG: `a`
@@ -979,28 +990,29 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
               split3(g0[e] * w0[e], hp[e], mp[e], lp[e]);
               split3(g1[e] * w1[e], hp[e + 4], mp[e + 4], lp[e + 4]);
             }
-            u32x4 kb0, kb1;
-            uint32_t kv0[8], kv1[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const char* kr = inb + L::K + (t8 + e) * L::kKRow + 2 * (32 * wave + srow);
-              kv0[e] = *reinterpret_cast<const uint16_t*>(kr);
-              kv1[e] = *reinterpret_cast<const uint16_t*>(kr + 32);
-            }
+            // k down its columns (positions t8 .. t8 + 7 of columns 32 w + i
+            // and 32 w + 16 + i for lane i of the group) by the transposing
+            // LDS read: in each group of 16 lanes, lane i of the result takes
+            // element i % 4 of the 4 that lane 4 j + i / 4 addressed, as its
+            // j-th value; lane s therefore addresses row t8 + s / 4 (+ 4),
+            // columns from 32 w + 4 (s % 4) (+ 16).
+            const char* const kc = inb + L::K + (t8 + (srow >> 2)) * L::kKRow + 2 * (32 * wave + 4 * (srow & 3));
+            const u32x2 k0lo = ds_read_tr16(kc);
+            const u32x2 k0hi = ds_read_tr16(kc + 4 * L::kKRow);
+            const u32x2 k1lo = ds_read_tr16(kc + 32);
+            const u32x2 k1hi = ds_read_tr16(kc + 4 * L::kKRow + 32);
             u32x4 hh, mm, ll;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               hh[e] = hp[2 * e] | (hp[2 * e + 1] << 16);
               mm[e] = mp[2 * e] | (mp[2 * e + 1] << 16);
               ll[e] = lp[2 * e] | (lp[2 * e + 1] << 16);
-              kb0[e] = kv0[2 * e] | (kv0[2 * e + 1] << 16);
-              kb1[e] = kv1[2 * e] | (kv1[2 * e + 1] << 16);
             }
             ah[c2] = __builtin_bit_cast(bf16x8, hh);
             am[c2] = __builtin_bit_cast(bf16x8, mm);
             al[c2] = __builtin_bit_cast(bf16x8, ll);
-            b0[c2] = __builtin_bit_cast(bf16x8, kb0);
-            b1[c2] = __builtin_bit_cast(bf16x8, kb1);
+            b0[c2] = __builtin_bit_cast(bf16x8, u32x4{k0lo.x, k0lo.y, k0hi.x, k0hi.y});
+            b1[c2] = __builtin_bit_cast(bf16x8, u32x4{k1lo.x, k1lo.y, k1hi.x, k1hi.y});
           }
           f32x4 d0m = {}, d0l = {}, d1m = {}, d1l = {};
 #pragma unroll
