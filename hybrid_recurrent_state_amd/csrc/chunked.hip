@@ -1087,14 +1087,31 @@ void launch_seq_kernel(const ChunkArgs& args, const float* ws, int chunk0, int n
                      dim3(PC ? 2 * kThreads : kThreads), lds, s, args, ws, chunk0, n_seg, init, init_rstride);
 }
 
+// LDS bytes a block may use on the current device, queried once per device
+// and thread (0 when the query fails).
+int max_lds_per_block() {
+  thread_local int cached_dev = -1;
+  thread_local int cached = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev != cached_dev) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) v = 0;
+    cached = v;
+    cached_dev = dev;
+  }
+  return cached;
+}
+
 // Segments of several chunks with bf16 inputs take the producer/consumer
-// form; a single chunk has nothing to stage ahead (and the smaller form fits
-// two blocks per CU), and two f32 input buffers would not fit in LDS.
+// form where its LDS fits (151,552 bytes; gfx950 blocks may use 160 KiB); a
+// single chunk has nothing to stage ahead (and the smaller form fits two
+// blocks per CU), and two f32 input buffers would not fit in LDS.
 template <typename TIn, bool CAPTURE, bool LOGG>
 hipError_t launch_seq(const ChunkArgs& args, const float* ws, int chunk0, int n_seg, const float* init,
                       size_t init_rstride, bool out_bf16, hipStream_t s) {
   constexpr bool BF = sizeof(TIn) == 2;
-  const bool pc = BF && n_seg > 1;
+  const bool pc = BF && n_seg > 1 && max_lds_per_block() >= static_cast<int>(SeqLds<true, true>::BYTES);
   if (out_bf16) {
     if (pc) launch_seq_kernel<TIn, CAPTURE, LOGG, true, BF>(args, ws, chunk0, n_seg, init, init_rstride, s);
     else launch_seq_kernel<TIn, CAPTURE, LOGG, true, false>(args, ws, chunk0, n_seg, init, init_rstride, s);
