@@ -791,17 +791,24 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
         cur = nxt;
         if (tid < 2 * kC / 4) *reinterpret_cast<f32x4*>(GvC + 4 * tid) = cur.g;
       }
+      // The starting state: from the lanes' registers with capture (the
+      // rank-1 recurrence keeps it there) and at the segment's first chunk;
+      // otherwise the previous chunk's end left it, and its parts, in LDS.
+      if (CAPTURE || cl == 0) {
 #pragma unroll
-      for (int m = 0; m < kNCH; ++m) {
-        *reinterpret_cast<f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m)) = s[m];
-        if constexpr (BF) {
-          uint32_t hp[4], mp[4], lp[4];
+        for (int m = 0; m < kNCH; ++m) {
+          *reinterpret_cast<f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m)) = s[m];
+          if constexpr (BF) {
+            uint32_t hp[4], mp[4], lp[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) split3(s[m][e], hp[e], mp[e], lp[e]);
-          char* const sp = lds + L::SPL + row_blk * L::kSplRow + 2 * 4 * (li + kLPR * m);
-          *reinterpret_cast<u32x2*>(sp) = u32x2{hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16)};
-          *reinterpret_cast<u32x2*>(sp + kRows * L::kSplRow) = u32x2{mp[0] | (mp[1] << 16), mp[2] | (mp[3] << 16)};
-          *reinterpret_cast<u32x2*>(sp + 2 * kRows * L::kSplRow) = u32x2{lp[0] | (lp[1] << 16), lp[2] | (lp[3] << 16)};
+            for (int e = 0; e < 4; ++e) split3(s[m][e], hp[e], mp[e], lp[e]);
+            char* const sp = lds + L::SPL + row_blk * L::kSplRow + 2 * 4 * (li + kLPR * m);
+            *reinterpret_cast<u32x2*>(sp) = u32x2{hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16)};
+            *reinterpret_cast<u32x2*>(sp + kRows * L::kSplRow) =
+                u32x2{mp[0] | (mp[1] << 16), mp[2] | (mp[3] << 16)};
+            *reinterpret_cast<u32x2*>(sp + 2 * kRows * L::kSplRow) =
+                u32x2{lp[0] | (lp[1] << 16), lp[2] | (lp[3] << 16)};
+          }
         }
       }
       if constexpr (!PC) {
@@ -1017,12 +1024,12 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
           f32x4 d0m = {}, d0l = {}, d1m = {}, d1l = {};
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
-            d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[c2], b0[c2], d0, 0, 0, 0);
-            d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[c2], b1[c2], d1, 0, 0, 0);
-            d0m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[c2], b0[c2], d0m, 0, 0, 0);
-            d1m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[c2], b1[c2], d1m, 0, 0, 0);
-            d0l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[c2], b0[c2], d0l, 0, 0, 0);
-            d1l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[c2], b1[c2], d1l, 0, 0, 0);
+            d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[c2], ah[c2], d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[c2], ah[c2], d1, 0, 0, 0);
+            d0m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[c2], am[c2], d0m, 0, 0, 0);
+            d1m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[c2], am[c2], d1m, 0, 0, 0);
+            d0l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[c2], al[c2], d0l, 0, 0, 0);
+            d1l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[c2], al[c2], d1l, 0, 0, 0);
           }
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
@@ -1048,25 +1055,48 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
           for (int q4 = 0; q4 < 4; ++q4) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-              d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[q4][u], k0[q4][u], d0, 0, 0, 0);
-              d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[q4][u], k1[q4][u], d1, 0, 0, 0);
+              d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(k0[q4][u], wv[q4][u], d0, 0, 0, 0);
+              d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(k1[q4][u], wv[q4][u], d1, 0, 0, 0);
             }
           }
         }
+        // The products are taken with k as the first operand, so each lane
+        // holds four consecutive columns of one row of the result (row srow,
+        // columns 32 w + 4 kq .. + 3 and 16 further on): the new state goes
+        // over S_0 in place and, for the bf16 products of the next chunk,
+        // as its three bf16 parts, written here; the next chunk starts from
+        // them without a trip through the lanes' registers.
         const float gn = Gv[n - 1];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          float* e0 = S0 + (4 * kq + u) * kSS + 32 * wave + srow;
-          e0[0] = __builtin_fmaf(gn, e0[0], d0[u]);
-          e0[16] = __builtin_fmaf(gn, e0[16], d1[u]);
+        for (int hf = 0; hf < 2; ++hf) {
+          const f32x4& d = hf ? d1 : d0;
+          const int col = 32 * wave + 16 * hf + 4 * kq;
+          float* const e = S0 + srow * kSS + col;
+          const f32x4 old = *reinterpret_cast<const f32x4*>(e);
+          f32x4 nv;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) nv[u] = __builtin_fmaf(gn, old[u], d[u]);
+          *reinterpret_cast<f32x4*>(e) = nv;
+          if constexpr (BF) {
+            uint32_t hp[4], mp[4], lp[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) split3(nv[u], hp[u], mp[u], lp[u]);
+            char* const sp = lds + L::SPL + srow * L::kSplRow + 2 * col;
+            *reinterpret_cast<u32x2*>(sp) = u32x2{hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16)};
+            *reinterpret_cast<u32x2*>(sp + kRows * L::kSplRow) = u32x2{mp[0] | (mp[1] << 16), mp[2] | (mp[3] << 16)};
+            *reinterpret_cast<u32x2*>(sp + 2 * kRows * L::kSplRow) =
+                u32x2{lp[0] | (lp[1] << 16), lp[2] | (lp[3] << 16)};
+          }
         }
       }
-      __syncthreads();
-      if (compute) {
+    }
+  }
+  if constexpr (!CAPTURE) {
+    // The state after the segment, from S_0 into the lanes that own its rows.
+    __syncthreads();
+    if (compute) {
 #pragma unroll
-        for (int m = 0; m < kNCH; ++m)
-          s[m] = *reinterpret_cast<const f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m));
-      }
+      for (int m = 0; m < kNCH; ++m) s[m] = *reinterpret_cast<const f32x4*>(S0 + row_blk * kSS + 4 * (li + kLPR * m));
     }
   }
   if (compute) {
