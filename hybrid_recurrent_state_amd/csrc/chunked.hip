@@ -112,9 +112,11 @@ struct SeqLds {
   static constexpr int W = Y + kRows * kTS * 4;                // f32 [16][kTS] W^T
   static constexpr int G = W + kRows * kTS * 4;                // f32 [C] g_t
   static constexpr int GC = G + kC * 4;                        // f32 [C] G[n-1][t] (follows g_t, as in the record)
-  static constexpr int BYTES = GC + kC * 4;
+  static constexpr int kWpRow = (kC + 8) * 2;                  // bytes per row of one part of G[n-1][t] w_t
+  static constexpr int WP = GC + kC * 4;                       // BF: bf16 [3][16] parts of G[n-1][t] w_t
+  static constexpr int BYTES = WP + (BF ? 3 * kRows * kWpRow : 0);
   static_assert(Q % 16 == 0 && V % 16 == 0 && REC % 16 == 0 && IN % 16 == 0 && S0 % 16 == 0 && SPL % 16 == 0 &&
-                    Y % 16 == 0 && W % 16 == 0, "16-byte LDS rows");
+                    Y % 16 == 0 && W % 16 == 0 && WP % 16 == 0 && kWpRow % 16 == 0, "16-byte LDS rows");
 };
 
 // Pre-pass LDS layout: k and q staged first; A, P, T and T^T take their
@@ -917,6 +919,17 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
           }
         }
         *reinterpret_cast<f32x4*>(Wt + srow * kTS + tb) = wacc;
+        if constexpr (BF && !CAPTURE) {
+          // The chunk-end state's factors G[n-1][t] w_t as three bf16 parts,
+          // once per value (the products read them as operands).
+          uint32_t hp[4], mp[4], lp[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) split3(GC[tb + u] * wacc[u], hp[u], mp[u], lp[u]);
+          char* const wp = lds + L::WP + srow * L::kWpRow + 2 * tb;
+          *reinterpret_cast<u32x2*>(wp) = u32x2{hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16)};
+          *reinterpret_cast<u32x2*>(wp + kRows * L::kWpRow) = u32x2{mp[0] | (mp[1] << 16), mp[2] | (mp[3] << 16)};
+          *reinterpret_cast<u32x2*>(wp + 2 * kRows * L::kWpRow) = u32x2{lp[0] | (lp[1] << 16), lp[2] | (lp[3] << 16)};
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) o_pend[u] = qsg[u] + oacc[u];
         o_elem = out_h + static_cast<size_t>(c0 + tb) * Hv * kDK + srow;
@@ -977,26 +990,20 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
       if (compute) {
         // 4. State at the chunk end only: S_C = g_{n-1} S_0 + sum_t G[n-1][t]
         //    w_t k_t^T on the matrix cores (wave w takes columns [32 w, 32 w +
-        //    32)), every operand read before the first product; written over
-        //    S_0 and read back into the lanes' registers. bf16 inputs: the f32
-        //    factors G[n-1][t] w_t as three bf16 parts against bf16 k (16x16x32
-        //    MFMA, exact products); f32 inputs: 16x16x4 f32 MFMA.
+        //    32)), every operand read before the first product. bf16 inputs:
+        //    the f32 factors G[n-1][t] w_t as the three bf16 parts step 3
+        //    wrote, against bf16 k (16x16x32 MFMA, exact products); f32
+        //    inputs: 16x16x4 f32 MFMA.
         f32x4 d0 = {}, d1 = {};
         if constexpr (BF) {
           bf16x8 ah[2], am[2], al[2], b0[2], b1[2];
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
             const int t8 = 32 * c2 + 8 * kq;
-            const f32x4 g0 = *reinterpret_cast<const f32x4*>(GC + t8);
-            const f32x4 g1 = *reinterpret_cast<const f32x4*>(GC + t8 + 4);
-            const f32x4 w0 = *reinterpret_cast<const f32x4*>(Wt + srow * kTS + t8);
-            const f32x4 w1 = *reinterpret_cast<const f32x4*>(Wt + srow * kTS + t8 + 4);
-            uint32_t hp[8], mp[8], lp[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              split3(g0[e] * w0[e], hp[e], mp[e], lp[e]);
-              split3(g1[e] * w1[e], hp[e + 4], mp[e + 4], lp[e + 4]);
-            }
+            const char* const wp = lds + L::WP + srow * L::kWpRow + 2 * t8;
+            ah[c2] = *reinterpret_cast<const bf16x8*>(wp);
+            am[c2] = *reinterpret_cast<const bf16x8*>(wp + kRows * L::kWpRow);
+            al[c2] = *reinterpret_cast<const bf16x8*>(wp + 2 * kRows * L::kWpRow);
             // k down its columns (positions t8 .. t8 + 7 of columns 32 w + i
             // and 32 w + 16 + i for lane i of the group) by the transposing
             // LDS read: in each group of 16 lanes, lane i of the result takes
@@ -1008,16 +1015,6 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
             const u32x2 k0hi = ds_read_tr16(kc + 4 * L::kKRow);
             const u32x2 k1lo = ds_read_tr16(kc + 32);
             const u32x2 k1hi = ds_read_tr16(kc + 4 * L::kKRow + 32);
-            u32x4 hh, mm, ll;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              hh[e] = hp[2 * e] | (hp[2 * e + 1] << 16);
-              mm[e] = mp[2 * e] | (mp[2 * e + 1] << 16);
-              ll[e] = lp[2 * e] | (lp[2 * e + 1] << 16);
-            }
-            ah[c2] = __builtin_bit_cast(bf16x8, hh);
-            am[c2] = __builtin_bit_cast(bf16x8, mm);
-            al[c2] = __builtin_bit_cast(bf16x8, ll);
             b0[c2] = __builtin_bit_cast(bf16x8, u32x4{k0lo.x, k0lo.y, k0hi.x, k0hi.y});
             b1[c2] = __builtin_bit_cast(bf16x8, u32x4{k1lo.x, k1lo.y, k1hi.x, k1hi.y});
           }
