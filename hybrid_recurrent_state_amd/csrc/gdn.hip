@@ -463,6 +463,10 @@ constexpr uint32_t kDroppedOffset = 0x80000000u;
 // resource, where the hardware drops the write, so no lane mask is needed;
 // in the 16-request chain loop, all 16 lanes of a row storing its value
 // measured 6% slower).
+typedef __attribute__((address_space(1))) char* GlobalBytes;
+typedef __attribute__((address_space(1))) f32x4* GlobalF32x4;
+typedef __attribute__((address_space(1))) float* GlobalFloat;
+
 template <int DK, int BITS>
 struct WaveStores {
   static constexpr int LPR = kLanesPerRow;
@@ -502,6 +506,24 @@ struct WaveStores {
   __device__ __forceinline__ void store_out(float o) {
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(out, 0, RPW * 4, 0x00020000);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), rsrc, out_off, 0, 0);
+    out += out_step;
+  }
+  // The same stores from the same bases as global streaming stores (the
+  // global address space named, so that no flat store also counts against
+  // the LDS wait counter), and the output from the first lane of each row
+  // only, under a lane mask (the buffer form sends all 64 lanes and drops
+  // 60). Used by tree blocks of 32 rows (many requests), where two
+  // row-owning waves share each SIMD: 146 vs 157 us per 16-request launch.
+  // With one row-owning wave per SIMD (one request) the buffer form's
+  // shorter instruction stream is what counts (16% faster there).
+  __device__ __forceinline__ void store_ckpt_plain(const f32x4 (&s)[NCH]) {
+    GlobalBytes p = (GlobalBytes)(ckpt) + ckpt_off;
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) __builtin_nontemporal_store(s[m], reinterpret_cast<GlobalF32x4>(p + m * LPR * 16));
+    ckpt += ckpt_step;
+  }
+  __device__ __forceinline__ void store_out_masked(float o, int lane) {
+    if (lane % LPR == 0) ((GlobalFloat)(out))[lane / LPR] = o;
     out += out_step;
   }
 };
@@ -556,7 +578,9 @@ __device__ __forceinline__ void run_positions(const float* buf, f32x4* stash, f3
     // request) this loop was bound by its instruction stream (~8 cycles per
     // instruction, ~111 instructions and 0.37 us per position); without the
     // copies and with scalar store addresses, ~85 instructions: 48-layer
-    // span-only stacks 11.6 -> 10.6 us per launch.
+    // span-only stacks 11.6 -> 10.6 us per launch. Blocks of 32 rows (many
+    // requests, two row-owning waves per SIMD) keep the copies and take
+    // per-lane global stores instead (see WaveStores).
     struct In {
       f32x4 k[NCH], q[NCH];
       float a, b, v;
@@ -593,24 +617,44 @@ __device__ __forceinline__ void run_positions(const float* buf, f32x4* stash, f3
       }
       const float u = row_dot<NCH>(s, c.k);
       update_row<NCH>(s, c.k, c.a, c.b * __builtin_fmaf(-c.a, u, c.v));
-      if (CAPTURE) st.store_ckpt(s);
+      if constexpr (CAPTURE) {
+        if constexpr (NW == 4)
+          st.store_ckpt(s);
+        else
+          st.store_ckpt_plain(s);
+      }
       const int sv = static_cast<int8_t>((c.code >> 16) & 0xFF);
       if (sv >= 0) {
 #pragma unroll
         for (int m = 0; m < NCH; ++m) stash[(sv * NCH + m) * NTHREADS + tid] = s[m];
       }
-      st.store_out(row_dot<NCH>(s, c.q));
+      const float o = row_dot<NCH>(s, c.q);
+      if constexpr (NW == 4)
+        st.store_out(o);
+      else
+        st.store_out_masked(o, lane);
     };
     In A, B;
     if (tn > 0) fetch(0, A);
-    int tt = 0;
-    for (; tt + 1 < tn; tt += 2) {
-      fetch(tt + 1, B);
-      step(A);
-      fetch(min(tt + 2, tn - 1), A);   // the last pair re-reads its own last position
-      step(B);
+    if constexpr (NW == 4) {
+      int tt = 0;
+      for (; tt + 1 < tn; tt += 2) {
+        fetch(tt + 1, B);
+        step(A);
+        fetch(min(tt + 2, tn - 1), A);   // the last pair re-reads its own last position
+        step(B);
+      }
+      if (tt < tn) step(A);
+    } else {
+      // 32-row blocks: one register set copied per position. With these
+      // stores it measured 146 vs 155 us per 16-request launch against the
+      // two sets (the two sets with flat stores: 147).
+      for (int tt = 0; tt < tn; ++tt) {
+        B = A;
+        if (tt + 1 < tn) fetch(tt + 1, A);
+        step(B);
+      }
     }
-    if (tt < tn) step(A);
   } else if constexpr (NW == 4) {
     // Blocks of one 16-row unit (launches too small to give every CU more
     // than one unit): each SIMD runs one row-owning wave, so the position
