@@ -539,9 +539,11 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep_kernel(const ChunkArg
 
 // The pre-pass record of one chunk in registers, in the layout of the
 // matrix-core operands that read it: wave w's lane (i, kq) = (lane % 16,
-// lane / 16) holds T[16 w + i][16 c + 4 kq + u] and the same of P T for the
-// column blocks c <= w (one coalesced 16-byte load per lane and tile); the
-// first 32 threads also hold g and G[n-1][.] (4 values each).
+// lane / 16) holds T[16 w + i][16 c + 4 kq + u] for the column blocks c <= w
+// and P T[16 (3 - w) + i][16 c + 4 kq + u] for c <= 3 - w (wave w computes
+// W for its own positions and the outputs for the mirrored block, w + 1 and
+// 4 - w tiles: five per wave); one coalesced 16-byte load per lane and tile.
+// The first 32 threads also hold g and G[n-1][.] (4 values each).
 struct RecRegs {
   f32x4 t[4], pt[4], g;
 };
@@ -552,10 +554,9 @@ __device__ __forceinline__ void fetch_rec(const float* rec, RecRegs& rr) {
   const int lane = tid & 63;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    if (c <= wave) {
-      rr.t[c] = *reinterpret_cast<const f32x4*>(rec + kRecT + tile_index(wave, c) * 256 + 4 * lane);
-      rr.pt[c] = *reinterpret_cast<const f32x4*>(rec + kRecPT + tile_index(wave, c) * 256 + 4 * lane);
-    }
+    if (c <= wave) rr.t[c] = *reinterpret_cast<const f32x4*>(rec + kRecT + tile_index(wave, c) * 256 + 4 * lane);
+    if (c <= 3 - wave)
+      rr.pt[c] = *reinterpret_cast<const f32x4*>(rec + kRecPT + tile_index(3 - wave, c) * 256 + 4 * lane);
   }
   if (tid < 2 * kC / 4) rr.g = *reinterpret_cast<const f32x4*>(rec + kRecG + 4 * tid);
 }
@@ -821,7 +822,8 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
       }
     }
     __syncthreads();
-    const int tb = 16 * wave + 4 * kq;   // this lane's 4 positions of the wave's tile
+    const int tb = 16 * wave + 4 * kq;         // this lane's 4 positions of the wave's W tile
+    const int tq = 16 * (3 - wave) + 4 * kq;   // and of its output tile (the mirrored block)
     f32x4 qsg;
     if (compute) {
       store_pending();
@@ -835,6 +837,7 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
       //    kept in the lanes that hold it.
       {
         const int row = 16 * wave + srow;
+        const int qrow = 16 * (3 - wave) + srow;
         f32x4 xk, xq;
         if constexpr (BF) {
           f32x4 xh = {}, xm = {}, xl = {}, qh = {}, qm = {}, ql = {};
@@ -842,7 +845,7 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
           for (int c = 0; c < kDK; c += 32) {
             const int col = 2 * (c + 8 * kq);
             const bf16x8 ka = *reinterpret_cast<const bf16x8*>(inb + L::K + row * L::kKRow + col);
-            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(inb + L::Q + row * L::kKRow + col);
+            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(inb + L::Q + qrow * L::kKRow + col);
             const char* const sp = lds + L::SPL + srow * L::kSplRow + col;
             const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sp);
             const bf16x8 sm = *reinterpret_cast<const bf16x8*>(sp + kRows * L::kSplRow);
@@ -865,7 +868,7 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
 #pragma unroll 2
           for (int c = 0; c < kDK; c += 16) {
             const f32x4 kv = *reinterpret_cast<const f32x4*>(inb + L::K + row * L::kKRow + 4 * (c + 4 * kq));
-            const f32x4 qv = *reinterpret_cast<const f32x4*>(inb + L::Q + row * L::kKRow + 4 * (c + 4 * kq));
+            const f32x4 qv = *reinterpret_cast<const f32x4*>(inb + L::Q + qrow * L::kKRow + 4 * (c + 4 * kq));
             const f32x4 sv = *reinterpret_cast<const f32x4*>(S0 + srow * kSS + c + 4 * kq);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -876,11 +879,12 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
         }
         const f32x4 g4 = *reinterpret_cast<const f32x4*>(Gv + tb);
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(Bv + tb);
+        const f32x4 gq = *reinterpret_cast<const f32x4*>(Gv + tq);
         f32x4 y;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           y[u] = b4[u] * __builtin_fmaf(-g4[u], xk[u], Vl[(tb + u) * kRows + srow]);
-          qsg[u] = (g4[u] * args.q_scale) * xq[u];
+          qsg[u] = (gq[u] * args.q_scale) * xq[u];
         }
         *reinterpret_cast<f32x4*>(Yt + srow * kTS + tb) = y;
       }
@@ -892,29 +896,32 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
     }
     __syncthreads();
     if (compute) {
-      // 3. W = T Y and P T Y in one pass over Y (16x16x4 f32 MFMA; wave w
-      //    takes positions [16 w, 16 w + 16) with its T and P T rows in
-      //    registers, PC: read from the staged record; both are lower
-      //    triangular, so the column blocks past w are skipped); outputs
-      //    o = q_scale g QS + P T Y, stored after the next chunk is staged.
+      // 3. W = T Y and P T Y in one pass over Y (16x16x4 f32 MFMA), T and
+      //    P T lower triangular in 16-position blocks: wave w takes W for its
+      //    positions [16 w, 16 w + 16) (column blocks c <= w) and P T Y for
+      //    the mirrored block 3 - w (c <= 3 - w), five tiles per wave (the
+      //    same block for both took 2, 4, 6 and 8); its T and P T rows are in
+      //    registers, PC: read from the staged record. Outputs o = q_scale g
+      //    QS + P T Y, stored after the next chunk is staged.
       {
         f32x4 wacc = {}, oacc = {};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          if (c <= wave) {
+          const bool wt = c <= wave, ot = c <= 3 - wave;   // wave-uniform
+          if (wt || ot) {
             const f32x4 yv = *reinterpret_cast<const f32x4*>(Yt + srow * kTS + 16 * c + 4 * kq);
-            f32x4 tc, pc;
-            if constexpr (PC) {
-              tc = *reinterpret_cast<const f32x4*>(recl + kRecT + tile_index(wave, c) * 256 + 4 * lane);
-              pc = *reinterpret_cast<const f32x4*>(recl + kRecPT + tile_index(wave, c) * 256 + 4 * lane);
-            } else {
-              tc = cur.t[c];
-              pc = cur.pt[c];
-            }
+            if (wt) {
+              const f32x4 tc = PC ? *reinterpret_cast<const f32x4*>(recl + kRecT + tile_index(wave, c) * 256 + 4 * lane)
+                                  : cur.t[c];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              wacc = __builtin_amdgcn_mfma_f32_16x16x4f32(tc[u], yv[u], wacc, 0, 0, 0);
-              oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(pc[u], yv[u], oacc, 0, 0, 0);
+              for (int u = 0; u < 4; ++u) wacc = __builtin_amdgcn_mfma_f32_16x16x4f32(tc[u], yv[u], wacc, 0, 0, 0);
+            }
+            if (ot) {
+              const f32x4 pc = PC ? *reinterpret_cast<const f32x4*>(recl + kRecPT + tile_index(3 - wave, c) * 256 +
+                                                                    4 * lane)
+                                  : cur.pt[c];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(pc[u], yv[u], oacc, 0, 0, 0);
             }
           }
         }
@@ -932,8 +939,8 @@ __global__ __launch_bounds__(PC ? 2 * kThreads : kThreads) void gdn_chunked_kern
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) o_pend[u] = qsg[u] + oacc[u];
-        o_elem = out_h + static_cast<size_t>(c0 + tb) * Hv * kDK + srow;
-        o_cnt = min(4, max(0, n - tb));
+        o_elem = out_h + static_cast<size_t>(c0 + tq) * Hv * kDK + srow;
+        o_cnt = min(4, max(0, n - tq));
       }
     } else if constexpr (PC) {
       // ... its record, and the loads of the inputs of the chunk after it ...
