@@ -453,6 +453,12 @@ __device__ __forceinline__ uintptr_t wave_uniform(uintptr_t v) {
 // A raw-buffer offset past every resource here: an access there is dropped.
 constexpr uint32_t kDroppedOffset = 0x80000000u;
 
+// Pointers into global memory, for stores the compiler would otherwise emit
+// as flat stores (which also count against the LDS wait counter).
+typedef __attribute__((address_space(1))) char* GlobalBytes;
+typedef __attribute__((address_space(1))) f32x4* GlobalF32x4;
+typedef __attribute__((address_space(1))) float* GlobalFloat;
+
 // The per-position stores of a wave, through raw buffer resources whose
 // base is wave-uniform and advances by a scalar add per position (the lane
 // offsets are loop invariant): the checkpoint rows of one position, with the
@@ -463,10 +469,6 @@ constexpr uint32_t kDroppedOffset = 0x80000000u;
 // resource, where the hardware drops the write, so no lane mask is needed;
 // in the 16-request chain loop, all 16 lanes of a row storing its value
 // measured 6% slower).
-typedef __attribute__((address_space(1))) char* GlobalBytes;
-typedef __attribute__((address_space(1))) f32x4* GlobalF32x4;
-typedef __attribute__((address_space(1))) float* GlobalFloat;
-
 template <int DK, int BITS>
 struct WaveStores {
   static constexpr int LPR = kLanesPerRow;
@@ -508,14 +510,13 @@ struct WaveStores {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), rsrc, out_off, 0, 0);
     out += out_step;
   }
-  // The same stores from the same bases as global streaming stores (the
-  // global address space named, so that no flat store also counts against
-  // the LDS wait counter), and the output from the first lane of each row
-  // only, under a lane mask (the buffer form sends all 64 lanes and drops
-  // 60). Used by tree blocks of 32 rows (many requests), where two
-  // row-owning waves share each SIMD: 146 vs 157 us per 16-request launch.
-  // With one row-owning wave per SIMD (one request) the buffer form's
-  // shorter instruction stream is what counts (16% faster there).
+  // The same stores from the same bases as global streaming stores with
+  // per-lane addresses, and the output from the first lane of each row only,
+  // under a lane mask (the buffer form sends all 64 lanes and drops 60).
+  // Used by tree blocks of 32 rows (many requests), where two row-owning
+  // waves share each SIMD: 146 vs 157 us per 16-request launch. With one
+  // row-owning wave per SIMD (one request) the buffer form's shorter
+  // instruction stream is what counts (this form measured 16% slower there).
   __device__ __forceinline__ void store_ckpt_plain(const f32x4 (&s)[NCH]) {
     GlobalBytes p = (GlobalBytes)(ckpt) + ckpt_off;
 #pragma unroll
