@@ -84,8 +84,6 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ float f(int i) const { return i < 4 ? v0[i] : v1[i - 4]; }
 };
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
-
 // Weights of 8 channels: w[c][m], c in [c0, c0+8), m in [0, W).
 template <typename T>
 __device__ __forceinline__ void load_weights(const T* w, int c0, float (&wt)[8][kWidth]) {
@@ -107,7 +105,11 @@ __device__ __forceinline__ void conv_out(const float (&wt)[8][kWidth], const Raw
     float acc = wt[c][0] * win[0].f(c);
 #pragma unroll
     for (int m = 1; m < kWidth; ++m) acc = __builtin_fmaf(wt[c][m], win[m].f(c), acc);
-    o[c] = silu_on ? silu(acc) : acc;
+    o[c] = acc;
+  }
+  if (silu_on) {   // one uniform branch for the 8 channels
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = silu_fast(o[c]);
   }
   *reinterpret_cast<f32x4*>(y) = f32x4{o[0], o[1], o[2], o[3]};
   *reinterpret_cast<f32x4*>(y + 4) = f32x4{o[4], o[5], o[6], o[7]};

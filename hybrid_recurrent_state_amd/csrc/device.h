@@ -63,6 +63,16 @@ template <> __device__ __forceinline__ void load8<float>(const float* p, float* 
   o[4] = y.x; o[5] = y.y; o[6] = y.z; o[7] = y.w;
 }
 
+// SiLU z / (1 + e^-z) from the hardware base-2 exponential and reciprocal:
+// e^-z = 2^(-z log2 e); a few ulp from the correctly rounded value (large
+// negative z gives -0 through 1 / inf, large positive z gives z). The conv
+// kernels and the fused layer's staging share it, so every launch shape and
+// path gives a request the same values.
+__device__ __forceinline__ float silu_fast(float z) {
+  const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // Cross-lane move inside a 16-lane DPP row. CTRL is a DPP control code:
 // 0xB1 quad_perm[1,0,3,2], 0x4E quad_perm[2,3,0,1], 0x141 row_half_mirror,
 // 0x140 row_mirror. Every lane has a valid source for these patterns.

@@ -267,16 +267,6 @@ template <> struct Raw16<float> {
   __device__ __forceinline__ float at(int c) const { return v[c >> 2][c & 3]; }
 };
 
-// SiLU z / (1 + e^-z) from the hardware base-2 exponential and reciprocal:
-// e^-z = 2^(-z log2 e); a few ulp from the correctly rounded value (large
-// negative z gives -0 through 1 / inf, large positive z gives z). Both
-// fused launch shapes use it, so a request's results do not depend on how
-// many requests share its launch.
-__device__ __forceinline__ float silu_fast(float z) {
-  const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
-  return z * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
 // Staging, fused layer: for every staged position, the conv (and SiLU) of
 // the unit's channels, written where the plain staging puts q, k and v: q
 // and k of key head g scaled to unit L2 norm (q also by q_scale), and the

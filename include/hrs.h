@@ -310,7 +310,8 @@ typedef struct {
   int32_t channels;  /* C, multiple of 8                                   */
   int32_t width;     /* W, conv width; 4 is built                          */
   hrs_dtype dtype;   /* dtype of x, w and the conv state                   */
-  int32_t silu;      /* nonzero: y = z / (1 + exp(-z)) after the conv      */
+  int32_t silu;      /* nonzero: y = z / (1 + exp(-z)) after the conv (to  */
+                     /* a few ulp: hardware exp2 and reciprocal)           */
   hrs_topology topo;
   const int32_t* parent; /* host [n_req][n_pos] when topo == HRS_TREE      */
 } hrs_conv_desc;
