@@ -468,11 +468,8 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep_kernel(const ChunkArg
 #pragma unroll
     for (int m = 0; m < 4; ++m) Tl[(d0 + 4 * sub + m) * kTS + d0 + col] = xs[m];
     *reinterpret_cast<f32x4*>(Tt + (d0 + col) * kTS + d0 + 4 * sub) = f32x4{xs[0], xs[1], xs[2], xs[3]};
-    // Blocks above the diagonal are 0 (never read; written so the record is defined).
-    for (int e = tid; e < kC * kC; e += kThreads) {
-      const int rr = e >> 6, cc = e & 63;
-      if ((cc >> 4) > (rr >> 4)) Tl[rr * kTS + cc] = 0.0f;
-    }
+    // The blocks above the diagonal are never read (the record holds the
+    // lower tiles only), so they are left unwritten.
   }
   __syncthreads();
   {
