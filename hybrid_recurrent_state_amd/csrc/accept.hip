@@ -8,8 +8,8 @@
 //
 // MI355X design: the argmax rows are long (151,936 entries) and few (T per
 // request), so pass 1 splits every row into 8192-entry chunks, one block
-// each, streaming 16-byte loads (each thread issues its four loads before its
-// first compare). A chunk is reduced in two passes over the registers: the
+// each, streaming 16-byte nontemporal loads (each thread issues its four
+// loads before its first compare). A chunk is reduced in two passes over the registers: the
 // largest value by a chain of IEEE maximum operations over quieted values
 // (NaN never wins; three operands fold into one instruction), then the
 // lowest index holding that value (float equality, so -0 and +0 tie and the
@@ -109,6 +109,23 @@ __device__ __forceinline__ uint64_t thread_key(float (&v)[kIter][8], const int (
   return n_valid > 0 ? make_key(__builtin_nanf(""), static_cast<uint32_t>(e[0])) : 0;
 }
 
+// The logits are read once: nontemporal loads (16 requests x 17 rows x
+// 151,936 bf16 logits: 18.2 vs 19.7 us per call with plain loads).
+template <typename T> __device__ __forceinline__ void load8_nt(const T* p, float* o);
+template <> __device__ __forceinline__ void load8_nt<uint16_t>(const uint16_t* p, float* o) {
+  const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  o[0] = bf16_lo(w.x); o[1] = bf16_hi(w.x);
+  o[2] = bf16_lo(w.y); o[3] = bf16_hi(w.y);
+  o[4] = bf16_lo(w.z); o[5] = bf16_hi(w.z);
+  o[6] = bf16_lo(w.w); o[7] = bf16_hi(w.w);
+}
+template <> __device__ __forceinline__ void load8_nt<float>(const float* p, float* o) {
+  const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  const f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+  o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+  o[4] = y.x; o[5] = y.y; o[6] = y.z; o[7] = y.w;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const T* logits, uint64_t* keys, int32_t vocab,
                                                                   int32_t n_chunks) {
@@ -126,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const T* logit
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
     e[it] = begin + (it * kThreads + threadIdx.x) * 8;
-    load8<T>(base + min(e[it], end - 8), v[it]);
+    load8_nt<T>(base + min(e[it], end - 8), v[it]);
   }
   int n_valid = 0;
 #pragma unroll
