@@ -415,7 +415,7 @@ size_t accept_greedy_workspace_bytes(const hrs_accept_desc* desc);
  * path [R][T], bonus [R]. workspace: device scratch of at least
  * accept_greedy_workspace_bytes(desc) bytes, 16-byte aligned, contents
  * ignored on entry. Size limits: n_req * n_pos <= 65535 * 64 and
- * n_req * n_pos * ceil(V / 8192) <= 2^24 (else HRS_EINVAL). Errors:
+ * n_req * n_pos * ceil(V / 16384) <= 2^24 (else HRS_EINVAL). Errors:
  * HRS_EINVAL, HRS_EALIGN, HRS_EGEOMETRY, HRS_EDEVICE.
  */
 int accept_greedy(const hrs_accept_desc* desc, const void* logits, const int32_t* tokens,
@@ -424,8 +424,8 @@ int accept_greedy(const hrs_accept_desc* desc, const void* logits, const int32_t
                   size_t workspace_bytes, void* stream);
 
 /* Largest workspace accept_greedy_noalloc can use: 1 MiB, the pass-1 keys of
- * up to 131,072 (row, 8192-logit chunk) pairs (e.g. 272 rows of 151,936
- * logits need 41,344 bytes). */
+ * up to 131,072 (row, 16384-logit chunk) pairs (e.g. 272 rows of 151,936
+ * logits need 21,760 bytes). */
 #define HRS_ACCEPT_NOALLOC_MAX_BYTES (1u << 20)
 
 /*

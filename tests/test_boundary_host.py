@@ -205,9 +205,9 @@ def accept_call(ws_bytes=None, **kw):
 def test_accept_rejections_and_workspace_size():
     E = hrs
     st, need = accept_call()
-    assert need == 2 * 5 * 1 * 8          # one 8192-entry chunk per row, 8-byte keys
+    assert need == 2 * 5 * 1 * 8          # one 16384-entry chunk per row, 8-byte keys
     assert st == E.HRS_EDEVICE
-    assert accept_call(vocab=151936)[1] == 2 * 5 * 19 * 8
+    assert accept_call(vocab=151936)[1] == 2 * 5 * 10 * 8
     assert accept_call(vocab=1001)[0] == E.HRS_EINVAL
     assert accept_call(ws_bytes=need - 1)[0] == E.HRS_EINVAL
     assert accept_call(tokens=None)[0] == E.HRS_EINVAL
@@ -216,12 +216,12 @@ def test_accept_rejections_and_workspace_size():
     assert accept_call(topo=E.HRS_TREE, parent=[-1, 0, 0, 1, 1, -1, 0, 1, 1, 2])[0] == E.HRS_EDEVICE
     assert accept_call(path=MIS)[0] == E.HRS_EALIGN
     assert accept_call(vocab=0)[1] == 0
-    # pass-1 blocks (rows x 8192-logit chunks) are bounded by 2^24: the largest
-    # vocabulary (2^31 - 8, 2^18 chunks) fits 64 rows, not 128
+    # pass-1 blocks (rows x 16384-logit chunks) are bounded by 2^24: the
+    # largest vocabulary (2^31 - 8, 2^17 chunks) fits 128 rows, not 192
     vmax = (1 << 31) - 8
-    d64 = hrs.AcceptDesc(1, 64, vmax, E.HRS_BF16, E.HRS_CHAIN, None)
-    assert hrs.lib.accept_greedy_workspace_bytes(ctypes.byref(d64)) == 64 * (1 << 18) * 8
-    assert accept_call(n_req=2, n_pos=64, vocab=vmax) == (E.HRS_EINVAL, 0)
+    d64 = hrs.AcceptDesc(2, 64, vmax, E.HRS_BF16, E.HRS_CHAIN, None)
+    assert hrs.lib.accept_greedy_workspace_bytes(ctypes.byref(d64)) == 128 * (1 << 17) * 8
+    assert accept_call(n_req=3, n_pos=64, vocab=vmax) == (E.HRS_EINVAL, 0)
 
 
 def test_accept_noalloc_rejections():
@@ -244,11 +244,11 @@ def test_accept_noalloc_rejections():
     assert call(path=MIS) == E.HRS_EALIGN
     assert call(n_pos=0) == E.HRS_EGEOMETRY
     assert call(parent=[-1, 0, 0, 1, 7, -1, 0, 1, 1, 2]) == E.HRS_EGEOMETRY
-    # 128 x 64 rows x 19 chunks x 8 B of keys exceed the 1 MiB array; 64 x 64 rows fit
-    assert call(n_req=128, n_pos=64, vocab=151936) == E.HRS_EINVAL
+    # 256 x 64 rows x 10 chunks x 8 B of keys exceed the 1 MiB array; 128 x 64 rows fit
+    assert call(n_req=256, n_pos=64, vocab=151936) == E.HRS_EINVAL
     assert hrs.ACCEPT_NOALLOC_MAX_BYTES == 1 << 20
     # a well-formed call gets past every check; with no GPU visible the launch fails
-    assert call(n_req=64, n_pos=64, vocab=151936) == E.HRS_EDEVICE
+    assert call(n_req=128, n_pos=64, vocab=151936) == E.HRS_EDEVICE
     assert call() == E.HRS_EDEVICE
 
 

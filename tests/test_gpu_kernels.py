@@ -489,13 +489,13 @@ def test_accept_random_matches_brute_force(hrs):
 
 @pytest.mark.parametrize("dtype", [F32, BF16])
 def test_accept_special_values(hrs, dtype):
-    V = 16384 + 64
+    V = 2 * 16384 + 64   # two whole 16384-logit chunks and a ragged one
     rows = np.full((8, V), -5.0, dtype=np.float32)
     rows[0, 3] = np.nan; rows[0, 10] = 1.0                 # NaN never wins
     rows[1, :] = np.nan                                      # all NaN -> 0
     rows[2, :] = -np.inf; rows[2, 7] = np.nan               # -inf row with a NaN -> first -inf (0)
-    rows[3, 9000] = 2.0; rows[3, 100] = 2.0                  # tie across chunks -> lowest
-    rows[4, 8191] = 3.0; rows[4, 8192] = 3.0                 # tie at a chunk boundary
+    rows[3, 20000] = 2.0; rows[3, 100] = 2.0                 # tie across chunks -> lowest
+    rows[4, 16383] = 3.0; rows[4, 16384] = 3.0               # tie at a chunk boundary
     rows[5, :] = 0.0; rows[5, :5] = -0.0                    # -0 == +0 -> index 0
     rows[6, V - 1] = np.inf; rows[6, V - 2] = np.inf         # inf ties -> lowest
     rows[7, V - 1] = 7.0                                     # max in the ragged last chunk
@@ -506,7 +506,7 @@ def test_accept_special_values(hrs, dtype):
         logits[0, 3] = nanbits; logits[1, :] = nanbits; logits[2, 7] = nanbits
     tok = np.zeros((1, 8), dtype=np.int32)
     got = gpu_accept(hrs, logits[None], tok)
-    expect = [10, 0, 0, 100, 8191, 0, V - 2, V - 1]
+    expect = [10, 0, 0, 100, 16383, 0, V - 2, V - 1]
     assert list(got[0][0]) == expect
     assert list(oacc.argmax_rows(logits)) == expect
 
@@ -516,7 +516,7 @@ def test_accept_signalling_nan_patterns(hrs, dtype):
     """NaN bit patterns whose quiet bit is clear (a bf16 NaN widens to such a
     float32) never win either, before or after the true maximum, in the same
     or another chunk; a row of them alone gives 0."""
-    V = 8192 + 1024
+    V = 16384 + 1024
     if dtype == F32:
         pats = np.array([0x7F800001, 0xFF800001, 0x7FBFFFFF, 0x7FC00000], dtype=np.uint32)
         rows = np.full((5, V), -3.0, dtype=np.float32)
@@ -526,9 +526,9 @@ def test_accept_signalling_nan_patterns(hrs, dtype):
         rows = bf16_bits(np.full((5, V), -3.0, dtype=np.float32))
         bits = rows
     bits[0, 5] = pats[0]; rows_max = {0: 4000}
-    bits[1, 8200] = pats[1]; rows_max[1] = 17
+    bits[1, 16400] = pats[1]; rows_max[1] = 17
     bits[2, :] = pats[2]                                # every entry NaN -> 0
-    bits[3, 0] = pats[0]; bits[3, 1] = pats[2]; rows_max[3] = 8191
+    bits[3, 0] = pats[0]; bits[3, 1] = pats[2]; rows_max[3] = 16383
     bits[4, ::3] = pats[3]; rows_max[4] = V - 1
     for r, i in rows_max.items():
         if dtype == F32:
@@ -537,7 +537,7 @@ def test_accept_signalling_nan_patterns(hrs, dtype):
             rows[r, i] = bf16_bits(np.float32(1.5))
     tok = np.zeros((1, 5), dtype=np.int32)
     got = gpu_accept(hrs, rows[None], tok)
-    expect = [4000, 17, 0, 8191, V - 1]
+    expect = [4000, 17, 0, 16383, V - 1]
     assert list(oacc.argmax_rows(rows)) == expect
     assert list(got[0][0]) == expect
 

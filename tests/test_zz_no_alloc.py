@@ -58,7 +58,7 @@ def test_noalloc_equals_workspace_call_twice_second_smaller(hrs):
 
 def test_noalloc_rejects_sizes_beyond_the_array(hrs):
     import torch
-    R, T, V = 128, 64, 151936        # 8,192 rows x 19 chunks x 8 B = 1.19 MiB of keys
+    R, T, V = 256, 64, 151936        # 16,384 rows x 10 chunks x 8 B = 1.25 MiB of keys
     d, _keep = hrs.accept_desc(R, T, V, hrs.HRS_BF16)
     assert hrs.lib.accept_greedy_workspace_bytes(ctypes.byref(d)) > hrs.ACCEPT_NOALLOC_MAX_BYTES
     small = torch.zeros(64, dtype=torch.int32, device="cuda")   # never read: rejected before any launch
