@@ -232,7 +232,7 @@ def chunked_prefill_row(reps: int = 10, T: int = 1024, R: int = 1):
                                       "speedup": res["recurrent_r16"] / res["chunked_r16"]}}
 
 
-def row_rates(step, shape, h, L: int, reps: int = 5):
+def row_rates(step, shape, h, L: int, reps: int = 15):
     """Achieved HBM rate of the step's other rows, each timed alone after the
     timed regions: the L conv spans back to back (per layer), acceptance,
     rollback of every layer, ring set + get. Event pairs around each piece,
