@@ -123,6 +123,12 @@ struct SeqLds {
 // place once the Gram products are in registers.
 constexpr int kPOffK = 0;
 constexpr int kPOffQ = kC * kKS;
+// bf16 inputs stage k and q as their bf16 bits instead: rows of kPKRowB bytes
+// (16-byte rows, a 4-bank shift per row), q after k.
+constexpr int kPOffKB = 0;
+constexpr int kPKRowB = (kDK + 8) * 2;
+constexpr int kPQOffB = kC * kPKRowB;
+static_assert(2 * kPQOffB <= kC * kKS * 2 * 4, "bf16 k and q fit where the f32 rows would");
 constexpr int kPOffA = 0;
 constexpr int kPOffP = kC * kTS;
 constexpr int kPOffT = 2 * kC * kTS;
@@ -154,24 +160,12 @@ struct ChunkArgs {
   float q_scale;
 };
 
-// Eight staged f32 values that are bf16-exact, packed back into bf16 pairs
-// (the upper halves of their bit patterns).
-__device__ __forceinline__ bf16x8 pack_bf16(const float* p) {
-  const u32x4 x = *reinterpret_cast<const u32x4*>(p);
-  const u32x4 y = *reinterpret_cast<const u32x4*>(p + 4);
-  u32x4 r;
-  r.x = (x.x >> 16) | (x.y & 0xFFFF0000u);
-  r.y = (x.z >> 16) | (x.w & 0xFFFF0000u);
-  r.z = (y.x >> 16) | (y.y & 0xFFFF0000u);
-  r.w = (y.z >> 16) | (y.w & 0xFFFF0000u);
-  return __builtin_bit_cast(bf16x8, r);
-}
-
 // K K^T and Q K^T of the staged chunk (q unscaled), computed into registers
 // and then written over the staging area as A and P (64 x 64 each, row
 // stride kTS); the block barrier between the two keeps every read of k and
 // q ahead of the writes. bf16 inputs: 32 x 32 tiles on the matrix cores,
-// operands packed back to bf16 from the staged rows (exact), f32
+// operands read straight from the staged bf16 rows (staged as f32 and packed
+// back at each read, the pre-pass took 1.5-2% longer per prefill), f32
 // accumulation, one tile of each per wave. f32 inputs: vector FMA, 2 x 8
 // outputs of each per thread.
 template <typename TIn>
@@ -188,12 +182,16 @@ __device__ __forceinline__ void gram(float* lds) {
     const int ra = 32 * ti + (lane & 31);
     const int rb = 32 * tj + (lane & 31);
     const int ko = 8 * (lane >> 5);
+    const char* const Kb = reinterpret_cast<const char*>(lds) + kPOffKB;
+    auto op = [&](int q, int row, int kk) {   // 8 bf16 of k (q = 0) or q (q = 1)
+      return *reinterpret_cast<const bf16x8*>(Kb + q * kPQOffB + row * kPKRowB + 2 * (kk + ko));
+    };
     f32x16 acc_k = {}, acc_q = {};
 #pragma unroll
     for (int kk = 0; kk < kDK; kk += 16) {
-      const bf16x8 b8 = pack_bf16(K + rb * kKS + kk + ko);
-      acc_k = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack_bf16(K + ra * kKS + kk + ko), b8, acc_k, 0, 0, 0);
-      acc_q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack_bf16(Q + ra * kKS + kk + ko), b8, acc_q, 0, 0, 0);
+      const bf16x8 b8 = op(0, rb, kk);
+      acc_k = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(0, ra, kk), b8, acc_k, 0, 0, 0);
+      acc_q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(1, ra, kk), b8, acc_q, 0, 0, 0);
     }
     __syncthreads();
 #pragma unroll
@@ -323,20 +321,28 @@ __device__ __forceinline__ void fetch_chunk(const ChunkArgs& args, ChunkRegs<TIn
 template <typename TIn, bool LOGG>
 __device__ __forceinline__ void stage_chunk(float* lds, const ChunkRegs<TIn>& rg, int n, float* av, float* bv) {
   const int tid = threadIdx.x;
-  float* const Kl = lds + kPOffK;
-  float* const Ql = lds + kPOffQ;
 #pragma unroll
   for (int i = 0; i < kKQItems; ++i) {
     const int e = tid + i * kThreads;
     const int t = e / (kDK / 8);
     const int j = (e % (kDK / 8)) * 8;
-    float x[8];
-    rg.k[i].widen(x);
-    *reinterpret_cast<f32x4*>(Kl + t * kKS + j) = f32x4{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<f32x4*>(Kl + t * kKS + j + 4) = f32x4{x[4], x[5], x[6], x[7]};
-    rg.q[i].widen(x);
-    *reinterpret_cast<f32x4*>(Ql + t * kKS + j) = f32x4{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<f32x4*>(Ql + t * kKS + j + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    if constexpr (sizeof(TIn) == 2) {
+      // bf16: the loaded bits, in rows of kPKRowB bytes (the Gram products
+      // read them as their operands).
+      char* const Kb = reinterpret_cast<char*>(lds) + kPOffKB;
+      *reinterpret_cast<u32x4*>(Kb + t * kPKRowB + 2 * j) = rg.k[i].v;
+      *reinterpret_cast<u32x4*>(Kb + kPQOffB + t * kPKRowB + 2 * j) = rg.q[i].v;
+    } else {
+      float* const Kl = lds + kPOffK;
+      float* const Ql = lds + kPOffQ;
+      float x[8];
+      rg.k[i].widen(x);
+      *reinterpret_cast<f32x4*>(Kl + t * kKS + j) = f32x4{x[0], x[1], x[2], x[3]};
+      *reinterpret_cast<f32x4*>(Kl + t * kKS + j + 4) = f32x4{x[4], x[5], x[6], x[7]};
+      rg.q[i].widen(x);
+      *reinterpret_cast<f32x4*>(Ql + t * kKS + j) = f32x4{x[0], x[1], x[2], x[3]};
+      *reinterpret_cast<f32x4*>(Ql + t * kKS + j + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    }
   }
   if (tid < kC) {
     // Log-space gates: a_t = exp(g_t) (positions past the span end keep a = 1).
