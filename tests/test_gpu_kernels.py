@@ -542,6 +542,26 @@ def test_accept_signalling_nan_patterns(hrs, dtype):
     assert list(got[0][0]) == expect
 
 
+
+@pytest.mark.parametrize("V", [8, 16384, 32768, 16384 + 8])
+def test_accept_vocab_at_chunk_boundaries(hrs, V):
+    """Vocabularies that end exactly at a pass-1 chunk boundary (one or two
+    whole 16384-logit chunks), a single 8-logit slice, and one slice past a
+    boundary: every row's argmax equals the oracle's, with the maximum in the
+    first slot, the last slot, a tie across the last boundary, and random."""
+    rng = np.random.default_rng(V)
+    rows = rng.standard_normal((5, V)).astype(np.float32)
+    rows[0, 0] = 9.0
+    rows[1, V - 1] = 9.0
+    rows[2, V - 1] = 9.0; rows[2, max(0, V - 16385)] = 9.0   # tie: the lower index wins
+    logits = bf16_bits(rows)
+    tok = np.zeros((1, 5), dtype=np.int32)
+    say(f"accept vocab {V}")
+    got = gpu_accept(hrs, logits[None], tok)
+    expect = list(oacc.argmax_rows(logits))
+    assert expect[0] == 0 and expect[1] == V - 1 and expect[2] == max(0, V - 16385)
+    assert list(got[0][0]) == expect
+
 def test_accept_workspace_reused_across_calls(hrs):
     """Workspace contents are ignored on entry: one buffer serves consecutive
     calls of different sizes, with garbage written into it between them, and
